@@ -1,0 +1,322 @@
+/*
+ * fp4moe_oracle.c -- plain, slow CPU oracle for the FP8-activation x block-scaled FP4 expert GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the benchmark's CPU-baseline
+ * leg may load this library.  The product path (the HIP library) never calls it, shares no code,
+ * header, table or helper with it, and must fail loudly instead of falling back to it.
+ *
+ * Sources (the pages this oracle is written from; cited by page title and item):
+ *   [GATE]   memra-engine 0.98.0, src/bin/dsv4_native_gemm_gate.rs -- `quant_rows` (act-quant),
+ *            `ExpertRaw` (weight layout), `f64_ref` (f64 reference of the quantized GEMM),
+ *            comparison 2 in the module doc and in `main` (the f32 error model).
+ *   [CHECK]  memra-engine 0.71.0, src/bin/kernel_check.rs -- F8-E4M3 matvec section, the CPU e4m3
+ *            decode closure (sign, 4-bit exponent with bias 7, 3-bit mantissa, subnormals, NaN);
+ *            f16g grouped GEMM section (CSR row offsets per expert).
+ *   [QWEN]   memra-engine 0.125.0, src/bin/qwen4exp_gpu_gate.rs -- NVFP4 synthetic checkpoint rows.
+ *
+ * Readings where the pages are silent (each is listed with its reason in the design notes):
+ *   - E2M1 values: the pages import a table without printing it; the OCP MX E2M1 grid
+ *     {0, 0.5, 1, 1.5, 2, 3, 4, 6} with a sign bit is used (8 magnitudes, maximum 6).
+ *   - E8M0: 2^(c-127) for c in 0..254, c = 255 is NaN.
+ *   - f32 -> E4M3 encode: round to nearest, ties to even mantissa, subnormal spacing 2^-9 down
+ *     to zero, sign kept on zero, saturating at 448.
+ *   - pow2_ceil(p): the smallest power of two >= p (an exact power of two maps to itself).
+ *
+ * Precision: the act-quant follows the page in f32 arithmetic; the GEMM accumulates in f64 in
+ * ascending k, every product being exact in f64.  Build with -O2 -ffp-contract=off and no
+ * fast-math, so that each f32 operation is one IEEE operation.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------------------------------------
+ * Element decoders
+ * ------------------------------------------------------------------------------------------- */
+
+/* E2M1 (FP4) value of a 4-bit code [GATE: the imported E2M1 table, indexed by nibble].
+ * Closed form of the OCP grid: exponent field e = bits 2..1, mantissa m = bit 0;
+ * e == 0 is the subnormal 0.5*m, otherwise (1 + m/2) * 2^(e-1); bit 3 is the sign. */
+double or_e2m1_value(unsigned code) {
+    unsigned e = (code >> 1) & 3u, m = code & 1u;
+    double mag = (e == 0) ? 0.5 * (double)m : (1.0 + 0.5 * (double)m) * ldexp(1.0, (int)e - 1);
+    return (code & 8u) ? -mag : mag;
+}
+
+/* E4M3 (FP8) value of a byte [CHECK: CPU e4m3 decode]: sign bit 7, exponent bits 6..3 with
+ * bias 7, mantissa bits 2..0; exponent 0 is subnormal m * 2^-9; exponent 15 with mantissa 7 is
+ * NaN; everything else is (1 + m/8) * 2^(e-7). */
+double or_e4m3_value(unsigned byte) {
+    unsigned s = (byte >> 7) & 1u, e = (byte >> 3) & 15u, m = byte & 7u;
+    double v;
+    if (e == 0)
+        v = (double)m * ldexp(1.0, -9);
+    else if (e == 15 && m == 7)
+        return NAN;
+    else
+        v = (1.0 + (double)m / 8.0) * ldexp(1.0, (int)e - 7);
+    return s ? -v : v;
+}
+
+/* E8M0 value of a byte [GATE: the imported e8m0_to_f32]: a pure biased exponent, 2^(c-127);
+ * c = 255 is NaN. */
+double or_e8m0_value(unsigned byte) {
+    if (byte == 255u) return NAN;
+    return ldexp(1.0, (int)byte - 127);
+}
+
+/* f32 -> E4M3 byte [GATE: the imported f32_to_fp8_e4m3, applied to values already clamped to
+ * +-448].  Round to nearest, ties to the even code (code LSB == mantissa LSB), magnitudes above
+ * 448 saturate to 448, and the sign bit of x is kept even when the magnitude rounds to zero.
+ * Found by a binary search over the 127 finite non-negative codes, which increase with the code,
+ * then one exact comparison with the midpoint of the two neighbours. */
+unsigned or_e4m3_encode(float x) {
+    uint32_t bits;
+    memcpy(&bits, &x, sizeof bits);
+    unsigned sign = (bits >> 31) & 1u;
+    double a = fabs((double)x);
+    unsigned r;
+    if (a >= 448.0) {
+        r = 0x7Eu;
+    } else {
+        unsigned lo = 0, hi = 0x7Eu; /* invariant: value(lo) <= a < value(hi) */
+        while (hi - lo > 1) {
+            unsigned mid = (lo + hi) / 2;
+            if (or_e4m3_value(mid) <= a) lo = mid; else hi = mid;
+        }
+        double mid = 0.5 * (or_e4m3_value(lo) + or_e4m3_value(hi)); /* exact in f64 */
+        if (a < mid) r = lo;
+        else if (a > mid) r = hi;
+        else r = (lo & 1u) ? hi : lo;
+    }
+    return (sign << 7) | r;
+}
+
+void or_e4m3_encode_many(const float* x, int64_t n, uint8_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)or_e4m3_encode(x[i]);
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * Activation quantization [GATE: quant_rows]
+ * ------------------------------------------------------------------------------------------- */
+
+/* Smallest power of two >= p, for finite p > 0 (reading of the imported pow2_ceil). */
+float or_pow2_ceil(float p) {
+    int e;
+    float f = frexpf(p, &e); /* p = f * 2^e, f in [0.5, 1) */
+    if (f == 0.5f) return p;
+    return ldexpf(1.0f, e);
+}
+
+/* Per row, per 128-column group: amax of |x| floored at 1e-4, times 1/448 rounded once to f32,
+ * rounded up to a power of two -> scale s; code = E4M3(clamp(x / s, -448, 448)).
+ * x: f32 [rows, k] row-major; codes: u8 [rows, k]; scales: f32 [rows, k/128].  k % 128 == 0. */
+void or_act_quant(const float* x, int64_t rows, int64_t k, uint8_t* codes, float* scales) {
+    const int64_t kq = k / 128;
+    const float inv = (float)(1.0 / 448.0);
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t q = 0; q < kq; ++q) {
+            const float* grp = x + r * k + q * 128;
+            float amax = 0.0f;
+            for (int i = 0; i < 128; ++i) amax = fmaxf(amax, fabsf(grp[i]));
+            amax = fmaxf(amax, 1e-4f);
+            float s = or_pow2_ceil(amax * inv);
+            scales[r * kq + q] = s;
+            for (int i = 0; i < 128; ++i) {
+                float v = grp[i] / s;
+                if (v < -448.0f) v = -448.0f;
+                if (v > 448.0f) v = 448.0f;
+                codes[r * k + q * 128 + i] = (uint8_t)or_e4m3_encode(v);
+            }
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * Quantized GEMM, f64 route [GATE: ExpertRaw, f64_ref]
+ * ------------------------------------------------------------------------------------------- */
+
+enum { OR_NVFP4 = 0, OR_MXFP4 = 1 };
+
+/* Weight scale of column c, group j: NVFP4 = f32(E4M3(S) * scale2) rounded once to f32,
+ * MXFP4 = E8M0(S) [GATE: the ws match in f64_ref]. */
+static double weight_scale(int kind, uint8_t sbyte, float scale2) {
+    if (kind == OR_NVFP4) {
+        float ws = (float)or_e4m3_value(sbyte) * scale2;
+        return (double)ws;
+    }
+    return (double)(float)or_e8m0_value(sbyte);
+}
+
+/* One output (row r, column c) of one expert: ref = sum over k of
+ *   E4M3(A[r,k]) * E2M1(W[c,k]) * (ws[c, k/gs] * as[r, k/128])
+ * in ascending k, and absp = the same sum of magnitudes.  W is nibble-packed [n, k/2] with even k
+ * in the low nibble; S is [n, k/gs] (gs = 16 NVFP4, 32 MXFP4); as is [g, k/128]. */
+static void gemm_one(const uint8_t* a_codes, const float* a_scales, const uint8_t* w,
+                     const uint8_t* s, float scale2, int kind, int64_t k, int64_t r, int64_t c,
+                     double* ref, double* absp) {
+    const int64_t gs = (kind == OR_NVFP4) ? 16 : 32;
+    const int64_t ngroups = k / gs, kq = k / 128;
+    const uint8_t* arow = a_codes + r * k;
+    const float* asrow = a_scales + r * kq;
+    const uint8_t* wrow = w + c * (k / 2);
+    const uint8_t* srow = s + c * ngroups;
+    double acc = 0.0, aabs = 0.0;
+    for (int64_t j = 0; j < ngroups; ++j) {
+        double sc = weight_scale(kind, srow[j], scale2) * (double)asrow[j * gs / 128];
+        for (int64_t i = 0; i < gs; ++i) {
+            int64_t kk = j * gs + i;
+            uint8_t byte = wrow[kk >> 1];
+            unsigned code = (kk & 1) ? (byte >> 4) : (byte & 0x0Fu);
+            double p = or_e4m3_value(arow[kk]) * or_e2m1_value(code) * sc;
+            acc += p;
+            aabs += fabs(p);
+        }
+    }
+    *ref = acc;
+    *absp = aabs;
+}
+
+typedef struct {
+    const uint8_t* a_codes; const float* a_scales; const uint8_t* w; const uint8_t* s;
+    float scale2; int kind; int64_t g, n, k; double* out; double* absp;
+    int64_t r0, r1;
+} gemm_job;
+
+static void* gemm_rows(void* p) {
+    gemm_job* j = (gemm_job*)p;
+    for (int64_t r = j->r0; r < j->r1; ++r)
+        for (int64_t c = 0; c < j->n; ++c)
+            gemm_one(j->a_codes, j->a_scales, j->w, j->s, j->scale2, j->kind, j->k, r, c,
+                     &j->out[r * j->n + c], &j->absp[r * j->n + c]);
+    return NULL;
+}
+
+/* Full single-expert GEMM: out, absp f64 [g, n].  Rows are split over nthreads threads; each
+ * output is computed by exactly one thread with the same ascending-k sum. */
+void or_expert_gemm(const uint8_t* a_codes, const float* a_scales, const uint8_t* w,
+                    const uint8_t* s, float scale2, int kind, int64_t g, int64_t n, int64_t k,
+                    double* out, double* absp, int nthreads) {
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nthreads > g) nthreads = (int)(g > 0 ? g : 1);
+    pthread_t th[256];
+    gemm_job jobs[256];
+    for (int t = 0; t < nthreads; ++t) {
+        gemm_job jb = {a_codes, a_scales, w, s, scale2, kind, g, n, k, out, absp,
+                       g * t / nthreads, g * (t + 1) / nthreads};
+        jobs[t] = jb;
+    }
+    if (nthreads == 1) { gemm_rows(&jobs[0]); return; }
+    for (int t = 0; t < nthreads; ++t) pthread_create(&th[t], NULL, gemm_rows, &jobs[t]);
+    for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+}
+
+/* Selected outputs of a single expert: for each i, (rows[i], cols[i]) -> out[i], absp[i]. */
+void or_expert_gemm_points(const uint8_t* a_codes, const float* a_scales, const uint8_t* w,
+                           const uint8_t* s, float scale2, int kind, int64_t k,
+                           const int64_t* rows, const int64_t* cols, int64_t count,
+                           double* out, double* absp) {
+    for (int64_t i = 0; i < count; ++i)
+        gemm_one(a_codes, a_scales, w, s, scale2, kind, k, rows[i], cols[i], &out[i], &absp[i]);
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * Grouped GEMM: rows packed per expert [CHECK: f16g grouped GEMM, CSR offsets; GATE: f64_ref per
+ * expert].  Expert e owns rows offsets[e] .. offsets[e+1]-1 of A and of out, and multiplies them
+ * by its own planes w_ptrs[e], s_ptrs[e] (host addresses) in format kinds[e] with scale2[e].
+ * ------------------------------------------------------------------------------------------- */
+
+typedef struct {
+    const uint8_t* a_codes; const float* a_scales; const int32_t* offsets; int32_t num_experts;
+    const uint8_t* const* w_ptrs; const uint8_t* const* s_ptrs; const int32_t* kinds;
+    const float* scale2; int64_t n, k; double* out; double* absp;
+    int64_t row0, r0, r1;
+} grouped_job;
+
+static int32_t expert_of_row(const int32_t* offsets, int32_t num_experts, int64_t row) {
+    for (int32_t e = 0; e < num_experts; ++e)
+        if (row >= offsets[e] && row < offsets[e + 1]) return e;
+    return -1;
+}
+
+static void* grouped_rows(void* p) {
+    grouped_job* j = (grouped_job*)p;
+    const int64_t kq = j->k / 128;
+    for (int64_t r = j->r0; r < j->r1; ++r) {
+        int32_t e = expert_of_row(j->offsets, j->num_experts, r);
+        if (e < 0) continue;
+        for (int64_t c = 0; c < j->n; ++c) {
+            /* gemm_one indexes A and as by row within the segment; pass the row's own base. */
+            gemm_one(j->a_codes + r * j->k, j->a_scales + r * kq, j->w_ptrs[e], j->s_ptrs[e],
+                     j->scale2[e], j->kinds[e], j->k, 0, c, &j->out[(r - j->row0) * j->n + c],
+                     &j->absp[(r - j->row0) * j->n + c]);
+        }
+    }
+    return NULL;
+}
+
+/* Grouped GEMM over the rows [row0, row1) of the packed activation matrix: out, absp f64
+ * [row1-row0, n] (row-major, first row = row0).  Rows outside every segment are left untouched. */
+void or_grouped_gemm(const uint8_t* a_codes, const float* a_scales, const int32_t* offsets,
+                     int32_t num_experts, const uint8_t* const* w_ptrs,
+                     const uint8_t* const* s_ptrs, const int32_t* kinds, const float* scale2,
+                     int64_t n, int64_t k, int64_t row0, int64_t row1, double* out, double* absp,
+                     int nthreads) {
+    const int64_t rows = row1 - row0;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nthreads > rows) nthreads = (int)(rows > 0 ? rows : 1);
+    pthread_t th[256];
+    grouped_job jobs[256];
+    for (int t = 0; t < nthreads; ++t) {
+        grouped_job jb = {a_codes, a_scales, offsets, num_experts, w_ptrs, s_ptrs, kinds, scale2,
+                          n, k, out, absp, row0,
+                          row0 + rows * t / nthreads, row0 + rows * (t + 1) / nthreads};
+        jobs[t] = jb;
+    }
+    if (nthreads == 1) { grouped_rows(&jobs[0]); return; }
+    for (int t = 0; t < nthreads; ++t) pthread_create(&th[t], NULL, grouped_rows, &jobs[t]);
+    for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+}
+
+/* Selected outputs of the grouped GEMM: (rows[i] in the packed order, cols[i]).  A row outside
+ * every segment yields NaN. */
+void or_grouped_gemm_points(const uint8_t* a_codes, const float* a_scales, const int32_t* offsets,
+                            int32_t num_experts, const uint8_t* const* w_ptrs,
+                            const uint8_t* const* s_ptrs, const int32_t* kinds,
+                            const float* scale2, int64_t k, const int64_t* rows,
+                            const int64_t* cols, int64_t count, double* out, double* absp) {
+    const int64_t kq = k / 128;
+    for (int64_t i = 0; i < count; ++i) {
+        int32_t e = expert_of_row(offsets, num_experts, rows[i]);
+        if (e < 0) { out[i] = NAN; absp[i] = NAN; continue; }
+        gemm_one(a_codes + rows[i] * k, a_scales + rows[i] * kq, w_ptrs[e], s_ptrs[e], scale2[e],
+                 kinds[e], k, 0, cols[i], &out[i], &absp[i]);
+    }
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * Dequantize-then-dense route [GATE: comparison 3, the bf16-dequant rung, computed here in f64]
+ * ------------------------------------------------------------------------------------------- */
+
+/* Wd[c,k] = E2M1(W[c,k]) * ws[c, k/gs], f64 [n, k]. */
+void or_dequant_weights(const uint8_t* w, const uint8_t* s, float scale2, int kind, int64_t n,
+                        int64_t k, double* wd) {
+    const int64_t gs = (kind == OR_NVFP4) ? 16 : 32;
+    for (int64_t c = 0; c < n; ++c)
+        for (int64_t kk = 0; kk < k; ++kk) {
+            uint8_t byte = w[c * (k / 2) + (kk >> 1)];
+            unsigned code = (kk & 1) ? (byte >> 4) : (byte & 0x0Fu);
+            wd[c * k + kk] = or_e2m1_value(code) * weight_scale(kind, s[c * (k / gs) + kk / gs], scale2);
+        }
+}
+
+/* Ad[r,k] = E4M3(A[r,k]) * as[r, k/128], f64 [g, k]. */
+void or_dequant_acts(const uint8_t* a_codes, const float* a_scales, int64_t g, int64_t k,
+                     double* ad) {
+    for (int64_t r = 0; r < g; ++r)
+        for (int64_t kk = 0; kk < k; ++kk)
+            ad[r * k + kk] = or_e4m3_value(a_codes[r * k + kk]) * (double)a_scales[r * (k / 128) + kk / 128];
+}

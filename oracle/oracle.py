@@ -1,0 +1,279 @@
+"""numpy driver for the plain C oracle (fp4moe_oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may
+import this module.  It shares no code with the HIP library and never imports it.
+
+Every arithmetic step lives in fp4moe_oracle.c (see that file's header for the passages of the
+pages each function follows).  This module builds the C file with gcc, marshals numpy arrays, and
+adds one independent route: the dequantize-then-dense product, whose dense step is numpy's f64
+matmul (a library primitive standing in for the pages' bf16-dequant rung, computed in f64 here).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+NVFP4 = 0
+MXFP4 = 1
+GROUP_SIZE = {NVFP4: 16, MXFP4: 32}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fp4moe_oracle.c")
+_LIB = os.path.join(_HERE, "libfp4moe_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle (host-only C, no FMA contraction, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-fPIC", "-shared",
+               "-pthread", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB)
+            P = ctypes.c_void_p
+            I64 = ctypes.c_int64
+            lib.or_e2m1_value.restype = ctypes.c_double
+            lib.or_e2m1_value.argtypes = [ctypes.c_uint]
+            lib.or_e4m3_value.restype = ctypes.c_double
+            lib.or_e4m3_value.argtypes = [ctypes.c_uint]
+            lib.or_e8m0_value.restype = ctypes.c_double
+            lib.or_e8m0_value.argtypes = [ctypes.c_uint]
+            lib.or_e4m3_encode.restype = ctypes.c_uint
+            lib.or_e4m3_encode.argtypes = [ctypes.c_float]
+            lib.or_e4m3_encode_many.restype = None
+            lib.or_e4m3_encode_many.argtypes = [P, I64, P]
+            lib.or_pow2_ceil.restype = ctypes.c_float
+            lib.or_pow2_ceil.argtypes = [ctypes.c_float]
+            lib.or_act_quant.restype = None
+            lib.or_act_quant.argtypes = [P, I64, I64, P, P]
+            lib.or_expert_gemm.restype = None
+            lib.or_expert_gemm.argtypes = [P, P, P, P, ctypes.c_float, ctypes.c_int, I64, I64, I64,
+                                           P, P, ctypes.c_int]
+            lib.or_expert_gemm_points.restype = None
+            lib.or_expert_gemm_points.argtypes = [P, P, P, P, ctypes.c_float, ctypes.c_int, I64,
+                                                  P, P, I64, P, P]
+            lib.or_grouped_gemm.restype = None
+            lib.or_grouped_gemm.argtypes = [P, P, P, ctypes.c_int32, P, P, P, P, I64, I64, I64,
+                                            I64, P, P, ctypes.c_int]
+            lib.or_grouped_gemm_points.restype = None
+            lib.or_grouped_gemm_points.argtypes = [P, P, P, ctypes.c_int32, P, P, P, P, I64, P, P,
+                                                   I64, P, P]
+            lib.or_dequant_weights.restype = None
+            lib.or_dequant_weights.argtypes = [P, P, ctypes.c_float, ctypes.c_int, I64, I64, P]
+            lib.or_dequant_acts.restype = None
+            lib.or_dequant_acts.argtypes = [P, P, I64, I64, P]
+            _lib = lib
+    return _lib
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+# --------------------------------------------------------------------------- element decoders
+def e2m1_value(codes) -> np.ndarray:
+    lib = _load()
+    codes = np.asarray(codes)
+    return np.array([lib.or_e2m1_value(int(c)) for c in codes.ravel()]).reshape(codes.shape)
+
+
+def e4m3_value(codes) -> np.ndarray:
+    lib = _load()
+    codes = np.asarray(codes)
+    return np.array([lib.or_e4m3_value(int(c)) for c in codes.ravel()]).reshape(codes.shape)
+
+
+def e8m0_value(codes) -> np.ndarray:
+    lib = _load()
+    codes = np.asarray(codes)
+    return np.array([lib.or_e8m0_value(int(c)) for c in codes.ravel()]).reshape(codes.shape)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """f32 -> E4M3 byte (RNE, sign-preserving zero, saturating) for an array of any shape."""
+    lib = _load()
+    x, px = _c(x, np.float32)
+    out = np.empty(x.shape, dtype=np.uint8)
+    lib.or_e4m3_encode_many(px, x.size, out.ctypes.data)
+    return out
+
+
+def pow2_ceil(p: float) -> np.float32:
+    return np.float32(_load().or_pow2_ceil(float(np.float32(p))))
+
+
+# --------------------------------------------------------------------------- act-quant
+def act_quant(x) -> tuple[np.ndarray, np.ndarray]:
+    """x f32 [rows, k] (k % 128 == 0) -> (codes u8 [rows, k], scales f32 [rows, k/128])."""
+    lib = _load()
+    x, px = _c(x, np.float32)
+    rows, k = x.shape
+    if k % 128:
+        raise ValueError("k must be a multiple of 128")
+    codes = np.empty((rows, k), dtype=np.uint8)
+    scales = np.empty((rows, k // 128), dtype=np.float32)
+    lib.or_act_quant(px, rows, k, codes.ctypes.data, scales.ctypes.data)
+    return codes, scales
+
+
+# --------------------------------------------------------------------------- GEMM (f64 route)
+def _check_expert(w, s, kind, n, k):
+    gs = GROUP_SIZE[kind]
+    if w.shape != (n, k // 2) or s.shape != (n, k // gs):
+        raise ValueError(f"weight planes {w.shape}/{s.shape} do not match n={n} k={k} kind={kind}")
+
+
+def expert_gemm(a_codes, a_scales, w, s, scale2, kind, threads=None):
+    """Single expert, f64 quantized route: returns (ref f64 [g, n], absp f64 [g, n])."""
+    lib = _load()
+    a_codes, pa = _c(a_codes, np.uint8)
+    a_scales, ps = _c(a_scales, np.float32)
+    w, pw = _c(w, np.uint8)
+    s, pss = _c(s, np.uint8)
+    g, k = a_codes.shape
+    n = w.shape[0]
+    _check_expert(w, s, kind, n, k)
+    out = np.empty((g, n), dtype=np.float64)
+    absp = np.empty((g, n), dtype=np.float64)
+    lib.or_expert_gemm(pa, ps, pw, pss, float(np.float32(scale2)), int(kind), g, n, k,
+                       out.ctypes.data, absp.ctypes.data, int(threads or default_threads()))
+    return out, absp
+
+
+def expert_gemm_points(a_codes, a_scales, w, s, scale2, kind, rows, cols):
+    lib = _load()
+    a_codes, pa = _c(a_codes, np.uint8)
+    a_scales, ps = _c(a_scales, np.float32)
+    w, pw = _c(w, np.uint8)
+    s, pss = _c(s, np.uint8)
+    rows, pr = _c(rows, np.int64)
+    cols, pc = _c(cols, np.int64)
+    k = a_codes.shape[1]
+    _check_expert(w, s, kind, w.shape[0], k)
+    out = np.empty(rows.shape, dtype=np.float64)
+    absp = np.empty(rows.shape, dtype=np.float64)
+    lib.or_expert_gemm_points(pa, ps, pw, pss, float(np.float32(scale2)), int(kind), k, pr, pc,
+                              rows.size, out.ctypes.data, absp.ctypes.data)
+    return out, absp
+
+
+def _expert_tables(weights, scales, kinds, scale2, n, k):
+    E = len(weights)
+    keep = []
+    wp = np.empty(E, dtype=np.uint64)
+    sp = np.empty(E, dtype=np.uint64)
+    for e in range(E):
+        w, pw = _c(weights[e], np.uint8)
+        s, ps = _c(scales[e], np.uint8)
+        _check_expert(w, s, int(kinds[e]), n, k)
+        keep += [w, s]
+        wp[e] = pw
+        sp[e] = ps
+    kinds_a, _ = _c(kinds, np.int32)
+    s2, _ = _c(scale2, np.float32)
+    return keep, wp, sp, kinds_a, s2
+
+
+def grouped_gemm(a_codes, a_scales, offsets, weights, scales, kinds, scale2, n,
+                 row0=0, row1=None, threads=None):
+    """Grouped f64 route over packed rows [row0, row1): (ref, absp) f64 [row1-row0, n].
+
+    weights[e]: u8 [n, k/2]; scales[e]: u8 [n, k/gs(kind[e])]; kinds, scale2: per expert."""
+    lib = _load()
+    a_codes, pa = _c(a_codes, np.uint8)
+    a_scales, ps = _c(a_scales, np.float32)
+    offsets, po = _c(offsets, np.int32)
+    R, k = a_codes.shape
+    row1 = R if row1 is None else row1
+    keep, wp, sp, kinds_a, s2 = _expert_tables(weights, scales, kinds, scale2, n, k)
+    out = np.full((row1 - row0, n), np.nan, dtype=np.float64)
+    absp = np.full((row1 - row0, n), np.nan, dtype=np.float64)
+    lib.or_grouped_gemm(pa, ps, po, len(weights), wp.ctypes.data, sp.ctypes.data,
+                        kinds_a.ctypes.data, s2.ctypes.data, n, k, row0, row1,
+                        out.ctypes.data, absp.ctypes.data, int(threads or default_threads()))
+    del keep
+    return out, absp
+
+
+def grouped_gemm_points(a_codes, a_scales, offsets, weights, scales, kinds, scale2, n, rows, cols):
+    lib = _load()
+    a_codes, pa = _c(a_codes, np.uint8)
+    a_scales, ps = _c(a_scales, np.float32)
+    offsets, po = _c(offsets, np.int32)
+    rows, pr = _c(rows, np.int64)
+    cols, pc = _c(cols, np.int64)
+    k = a_codes.shape[1]
+    keep, wp, sp, kinds_a, s2 = _expert_tables(weights, scales, kinds, scale2, n, k)
+    out = np.empty(rows.shape, dtype=np.float64)
+    absp = np.empty(rows.shape, dtype=np.float64)
+    lib.or_grouped_gemm_points(pa, ps, po, len(weights), wp.ctypes.data, sp.ctypes.data,
+                               kinds_a.ctypes.data, s2.ctypes.data, k, pr, pc, rows.size,
+                               out.ctypes.data, absp.ctypes.data)
+    del keep
+    return out, absp
+
+
+# --------------------------------------------------------------------------- dequant route
+def dequant_weights(w, s, scale2, kind) -> np.ndarray:
+    lib = _load()
+    w, pw = _c(w, np.uint8)
+    s, ps = _c(s, np.uint8)
+    n, k = w.shape[0], w.shape[1] * 2
+    _check_expert(w, s, kind, n, k)
+    wd = np.empty((n, k), dtype=np.float64)
+    lib.or_dequant_weights(pw, ps, float(np.float32(scale2)), int(kind), n, k, wd.ctypes.data)
+    return wd
+
+
+def dequant_acts(a_codes, a_scales) -> np.ndarray:
+    lib = _load()
+    a_codes, pa = _c(a_codes, np.uint8)
+    a_scales, ps = _c(a_scales, np.float32)
+    g, k = a_codes.shape
+    ad = np.empty((g, k), dtype=np.float64)
+    lib.or_dequant_acts(pa, ps, g, k, ad.ctypes.data)
+    return ad
+
+
+def dense_route(a_codes, a_scales, w, s, scale2, kind) -> np.ndarray:
+    """Dequantize both operands in f64 and multiply with numpy's f64 matmul."""
+    return dequant_acts(a_codes, a_scales) @ dequant_weights(w, s, scale2, kind).T
+
+
+# --------------------------------------------------------------------------- acceptance rule
+U32 = 2.0 ** -24
+
+
+def gemm_bound(absp, k) -> np.ndarray:
+    """f32-accumulation error bound with the operation count taken as k: k * 2^-24 * sum|p|."""
+    return float(k) * U32 * np.asarray(absp, dtype=np.float64)
+
+
+def pages_op_count(kind, k) -> float:
+    """The pages' own op count for their 128-thread kernel: (gs-1) + ceil(groups/128) + 7
+    (reported as a diagnostic only)."""
+    gs = GROUP_SIZE[kind]
+    return (gs - 1) + np.ceil((k / gs) / 128.0) + 7

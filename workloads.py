@@ -1,0 +1,261 @@
+"""Seeded synthetic inputs for the FP8-activation x block-scaled FP4 expert GEMM.
+
+This module holds no step of the method: it draws random activations, random weight nibbles and
+random scale codes, and builds routing tables.  Scale codes are drawn from stated byte ranges; what
+those bytes decode to is checked by the oracle's tests, never computed here.  Both the HIP path (via
+the tests and the benchmark) and the CPU oracle consume exactly these arrays.
+
+Workloads (sizes from the pages' expert shapes; distributions stated per function):
+  config0  single NVFP4 expert, g=4, k=512, n=256
+  config1  single MXFP4 expert, g in {1,2,4,8}, k=7168, n=2048 (decode-shaped)
+  config2  single NVFP4 down-projection expert, g=16, k=2048, n=7168, 1% outliers x40
+  config3  grouped NVFP4 decode step: 512 tokens, 256 experts, top-8, k=7168, n=2048
+  config4  grouped prefill: 8192 tokens, 256 experts (255 NVFP4 + 1 MXFP4), Zipf(1.1) top-8,
+           k=7168, n=4096, Student-t(3) activations
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+NVFP4 = 0
+MXFP4 = 1
+GROUP_SIZE = {NVFP4: 16, MXFP4: 32}
+
+SEED_BASE = 20261202
+
+# E4M3 scale bytes drawn for NVFP4 weights: every positive code from 0x20 to 0x48 inclusive
+# (41 codes; the oracle tests check they are exactly the E4M3 values in [2^-3, 2^2]).
+NVFP4_SCALE_CODE_RANGE = (0x20, 0x48)
+# E8M0 biased exponents drawn for MXFP4 weights.
+MXFP4_SCALE_CODE_RANGE = (117, 124)
+# Per-expert NVFP4 scale2 choices for the grouped workloads: the powers of two 2^-8 .. 2^-5.
+GROUPED_SCALE2_CHOICES = (2.0 ** -8, 2.0 ** -7, 2.0 ** -6, 2.0 ** -5)
+
+# Exact-by-construction inputs.  E4M3 bytes of the integers 0..16 (the oracle tests check that each
+# decodes to its integer), used with both signs; weight scale bytes for NVFP4 (E4M3 1, 2, 4) and
+# MXFP4 (E8M0 0.5, 1, 2).  With activation scale 1 and scale2 1 every product is a multiple of 1/4
+# and every partial sum of k <= 7168 terms stays below 2^22, so any f32 summation order is exact.
+EXACT_INT_E4M3_CODES = (0x00, 0x38, 0x40, 0x44, 0x48, 0x4A, 0x4C, 0x4E, 0x50, 0x51, 0x52, 0x53,
+                        0x54, 0x55, 0x56, 0x57, 0x58)
+EXACT_NVFP4_SCALE_CODES = (0x38, 0x40, 0x48)
+EXACT_MXFP4_SCALE_CODES = (126, 127, 128)
+
+
+def rng_for(config: int, variant: int = 0) -> np.random.Generator:
+    return np.random.default_rng([SEED_BASE, config, variant])
+
+
+def random_nibbles(rng, n: int, k: int) -> np.ndarray:
+    """Uniform 4-bit codes packed two per byte, [n, k/2] (uniform bytes are exactly that)."""
+    return np.frombuffer(rng.bytes(n * (k // 2)), dtype=np.uint8).reshape(n, k // 2).copy()
+
+
+def random_scale_codes(rng, kind: int, n: int, k: int) -> np.ndarray:
+    lo, hi = NVFP4_SCALE_CODE_RANGE if kind == NVFP4 else MXFP4_SCALE_CODE_RANGE
+    return rng.integers(lo, hi + 1, size=(n, k // GROUP_SIZE[kind]), dtype=np.uint8)
+
+
+@dataclass
+class Expert:
+    kind: int
+    w: np.ndarray        # u8 [n, k/2], even k in the low nibble
+    s: np.ndarray        # u8 [n, k/gs]
+    scale2: float        # NVFP4 per-tensor f32 scale (ignored for MXFP4)
+
+
+@dataclass
+class SingleWorkload:
+    name: str
+    x: np.ndarray        # f32 [g, k]
+    expert: Expert
+
+    @property
+    def g(self): return self.x.shape[0]
+
+    @property
+    def k(self): return self.x.shape[1]
+
+    @property
+    def n(self): return self.expert.w.shape[0]
+
+
+@dataclass
+class GroupedWorkload:
+    name: str
+    x: np.ndarray              # f32 [T, k] token activations
+    row_ids: np.ndarray        # int32 [R]: token of each packed row
+    offsets: np.ndarray        # int32 [E+1]: expert e owns packed rows offsets[e]..offsets[e+1]-1
+    kinds: np.ndarray          # int32 [E]
+    scale2: np.ndarray         # f32 [E]
+    w_bank: np.ndarray         # u8, all experts' nibble planes back to back
+    s_bank: np.ndarray         # u8, all experts' scale planes back to back
+    w_off: np.ndarray          # int64 [E] byte offset of expert e's nibble plane in w_bank
+    s_off: np.ndarray          # int64 [E] byte offset of expert e's scale plane in s_bank
+    n: int
+    k: int
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def E(self): return len(self.kinds)
+
+    @property
+    def R(self): return int(self.offsets[-1])
+
+    def w_of(self, e: int) -> np.ndarray:
+        o = int(self.w_off[e])
+        return self.w_bank[o:o + self.n * self.k // 2].reshape(self.n, self.k // 2)
+
+    def s_of(self, e: int) -> np.ndarray:
+        gs = GROUP_SIZE[int(self.kinds[e])]
+        o = int(self.s_off[e])
+        return self.s_bank[o:o + self.n * self.k // gs].reshape(self.n, self.k // gs)
+
+    def weight_stream_bytes(self) -> int:
+        """Nibble + scale-plane + scale2 bytes of every expert that owns at least one row."""
+        total = 0
+        for e in range(self.E):
+            if self.offsets[e + 1] > self.offsets[e]:
+                total += self.n * self.k // 2 + self.n * self.k // GROUP_SIZE[int(self.kinds[e])]
+                total += 4 if int(self.kinds[e]) == NVFP4 else 0
+        return total
+
+
+# --------------------------------------------------------------------------- single experts
+def config0() -> SingleWorkload:
+    rng = rng_for(0)
+    x = rng.standard_normal((4, 512), dtype=np.float32)
+    ex = Expert(NVFP4, random_nibbles(rng, 256, 512), random_scale_codes(rng, NVFP4, 256, 512),
+                2.0 ** -6)
+    return SingleWorkload("config0: single NVFP4 expert g=4 k=512 n=256", x, ex)
+
+
+def config1(g: int) -> SingleWorkload:
+    rng = rng_for(1, g)
+    x = rng.standard_normal((g, 7168), dtype=np.float32)
+    ex = Expert(MXFP4, random_nibbles(rng, 2048, 7168), random_scale_codes(rng, MXFP4, 2048, 7168),
+                0.0)
+    return SingleWorkload(f"config1: single MXFP4 expert g={g} k=7168 n=2048", x, ex)
+
+
+def config2() -> SingleWorkload:
+    rng = rng_for(2)
+    g, k, n = 16, 2048, 7168
+    x = (0.5 * rng.standard_normal((g, k), dtype=np.float32)).astype(np.float32)
+    n_out = int(round(0.01 * g * k))
+    idx = rng.choice(g * k, size=n_out, replace=False)
+    x.reshape(-1)[idx] *= np.float32(40.0)
+    ex = Expert(NVFP4, random_nibbles(rng, n, k), random_scale_codes(rng, NVFP4, n, k), 2.0 ** -7)
+    return SingleWorkload("config2: single NVFP4 down-proj expert g=16 k=2048 n=7168 (1% x40)",
+                          x, ex)
+
+
+def single_random(seed: int, g: int, n: int, k: int, kind: int, scale2: float = 2.0 ** -6,
+                  x_scale: float = 1.0) -> SingleWorkload:
+    """A small random expert of any shape (parity cases: ragged n, odd g, several tiles)."""
+    rng = np.random.default_rng([SEED_BASE, 100, seed])
+    x = (x_scale * rng.standard_normal((g, k), dtype=np.float32)).astype(np.float32)
+    ex = Expert(kind, random_nibbles(rng, n, k), random_scale_codes(rng, kind, n, k),
+                scale2 if kind == NVFP4 else 0.0)
+    return SingleWorkload(f"random seed={seed} g={g} n={n} k={k} kind={kind}", x, ex)
+
+
+def exact_arm(seed: int, g: int, n: int, k: int, kind: int):
+    """Quantized GEMM inputs given directly as codes: (a_codes, a_scales=1, Expert(scale2=1))."""
+    rng = np.random.default_rng([SEED_BASE, 200, seed])
+    mags = np.array(EXACT_INT_E4M3_CODES, dtype=np.uint8)
+    a = mags[rng.integers(0, len(mags), size=(g, k))]
+    a |= (rng.integers(0, 2, size=(g, k), dtype=np.uint8) << 7)
+    a_scales = np.ones((g, k // 128), dtype=np.float32)
+    codes = EXACT_NVFP4_SCALE_CODES if kind == NVFP4 else EXACT_MXFP4_SCALE_CODES
+    s = np.array(codes, dtype=np.uint8)[rng.integers(0, 3, size=(n, k // GROUP_SIZE[kind]))]
+    ex = Expert(kind, random_nibbles(rng, n, k), s, 1.0 if kind == NVFP4 else 0.0)
+    return a.astype(np.uint8), a_scales, ex
+
+
+# --------------------------------------------------------------------------- routing
+def route_topk(logits: np.ndarray, top: int):
+    """Top-`top` experts per token by logit, ties to the lower expert id; rows packed per expert in
+    ascending token order.  Returns (row_ids int32 [T*top], offsets int32 [E+1])."""
+    T, E = logits.shape
+    order = np.argsort(-logits, axis=1, kind="stable")[:, :top]       # [T, top]
+    tok = np.repeat(np.arange(T, dtype=np.int64), top)
+    exp = order.reshape(-1)
+    perm = np.lexsort((tok, exp))                                      # by expert, then token
+    row_ids = tok[perm].astype(np.int32)
+    counts = np.bincount(exp, minlength=E)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    return row_ids, offsets
+
+
+def _bank(rng, kinds, n, k):
+    E = len(kinds)
+    w_off = np.arange(E, dtype=np.int64) * (n * k // 2)
+    w_bank = np.frombuffer(rng.bytes(E * n * k // 2), dtype=np.uint8).copy()
+    s_sizes = np.array([n * k // GROUP_SIZE[int(kd)] for kd in kinds], dtype=np.int64)
+    s_off = np.zeros(E, dtype=np.int64)
+    s_off[1:] = np.cumsum(s_sizes)[:-1]
+    s_bank = np.empty(int(s_sizes.sum()), dtype=np.uint8)
+    for kd in (NVFP4, MXFP4):
+        sel = [e for e in range(E) if int(kinds[e]) == kd]
+        if not sel:
+            continue
+        lo, hi = NVFP4_SCALE_CODE_RANGE if kd == NVFP4 else MXFP4_SCALE_CODE_RANGE
+        draws = rng.integers(lo, hi + 1, size=len(sel) * (n * k // GROUP_SIZE[kd]), dtype=np.uint8)
+        per = n * k // GROUP_SIZE[kd]
+        for i, e in enumerate(sel):
+            s_bank[s_off[e]:s_off[e] + per] = draws[i * per:(i + 1) * per]
+    return w_bank, s_bank, w_off, s_off
+
+
+def grouped_random(seed: int, T: int, E: int, top: int, n: int, k: int, kinds=None,
+                   empty_experts=(), zipf: float | None = None, x_dist: str = "normal"):
+    """A grouped workload of any size (parity cases).  `empty_experts` get no rows."""
+    rng = np.random.default_rng([SEED_BASE, 300, seed])
+    kinds = np.zeros(E, dtype=np.int32) if kinds is None else np.asarray(kinds, dtype=np.int32)
+    x = (rng.standard_t(3, size=(T, k)) if x_dist == "t3" else rng.standard_normal((T, k))).astype(np.float32)
+    if zipf is not None:
+        ranks = rng.permutation(E) + 1
+        logits = -zipf * np.log(ranks)[None, :] + rng.gumbel(size=(T, E))
+    else:
+        logits = rng.standard_normal((T, E))
+    for e in empty_experts:
+        logits[:, e] = -np.inf
+    row_ids, offsets = route_topk(logits, top)
+    scale2 = np.array(GROUPED_SCALE2_CHOICES, dtype=np.float32)[rng.integers(0, 4, size=E)]
+    scale2[kinds == MXFP4] = 0.0
+    w_bank, s_bank, w_off, s_off = _bank(rng, kinds, n, k)
+    return GroupedWorkload(f"grouped seed={seed} T={T} E={E} top={top} n={n} k={k}", x, row_ids,
+                           offsets, kinds, scale2, w_bank, s_bank, w_off, s_off, n, k)
+
+
+def config3() -> GroupedWorkload:
+    rng = rng_for(3)
+    T, E, top, n, k = 512, 256, 8, 2048, 7168
+    x = rng.standard_normal((T, k), dtype=np.float32)
+    logits = rng.standard_normal((T, E), dtype=np.float32)
+    row_ids, offsets = route_topk(logits, top)
+    kinds = np.zeros(E, dtype=np.int32)
+    scale2 = np.array(GROUPED_SCALE2_CHOICES, dtype=np.float32)[rng.integers(0, 4, size=E)]
+    w_bank, s_bank, w_off, s_off = _bank(rng, kinds, n, k)
+    return GroupedWorkload("config3: grouped NVFP4 decode, 512 tokens, E=256, top-8, k=7168, n=2048",
+                           x, row_ids, offsets, kinds, scale2, w_bank, s_bank, w_off, s_off, n, k)
+
+
+def config4() -> GroupedWorkload:
+    rng = rng_for(4)
+    T, E, top, n, k = 8192, 256, 8, 4096, 7168
+    x = rng.standard_t(3, size=(T, k)).astype(np.float32)
+    ranks = rng.permutation(E) + 1
+    logits = -1.1 * np.log(ranks)[None, :] + rng.gumbel(size=(T, E))
+    row_ids, offsets = route_topk(logits, top)
+    kinds = np.zeros(E, dtype=np.int32)
+    kinds[E - 1] = MXFP4
+    scale2 = np.array(GROUPED_SCALE2_CHOICES, dtype=np.float32)[rng.integers(0, 4, size=E)]
+    scale2[E - 1] = 0.0
+    w_bank, s_bank, w_off, s_off = _bank(rng, kinds, n, k)
+    return GroupedWorkload("config4: grouped prefill, 8192 tokens, E=256 (255 NVFP4 + 1 MXFP4), "
+                           "Zipf(1.1) top-8, k=7168, n=4096, Student-t(3)",
+                           x, row_ids, offsets, kinds, scale2, w_bank, s_bank, w_off, s_off, n, k)
