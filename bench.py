@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8-activation x block-scaled FP4 expert GEMM hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: act_quant_fp8 of the token rows, then
+fp4_grouped_gemm over the routed rows packed per expert.  Default workload: the grouped NVFP4
+decode step (512 tokens, 256 experts, top-8, k=7168, n=2048).  Inputs are resident in HBM before
+the timed region; the weights (2.1 GB) exceed the 256 MB Infinity Cache, so every step streams
+them from HBM.
+
+Prints ONE JSON line on stdout; human-readable detail goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402  (seeded input generators; no torch, no method arithmetic)
+
+METRIC = "FP4 expert GEMM weight-stream TB/s (decode) + TFLOP/s (grouped prefill)"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "fp8": 5000.0}
+GEMM_SOURCES = ["block_scaled_fp4_quant_amd/csrc/gemm_decode.hip",
+                "block_scaled_fp4_quant_amd/csrc/device_common.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def sources_sha() -> str:
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per GEMM launch measured with rocprofv3 counters for this exact kernel source, or
+    None when no measurement matches the current source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(workload)
+    if not ent or ent.get("gemm_sources_sha") != sources_sha():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def algorithmic_bytes(wl) -> dict:
+    """Bytes the grouped GEMM must move at minimum: every touched expert's nibble + scale planes
+    (+ scale2), the activation codes and scales of the token rows, the routing tables, the f32
+    output."""
+    T, k = wl.x.shape
+    weights = wl.weight_stream_bytes()
+    acts = T * k + T * (k // 128) * 4
+    tables = wl.R * 4 + (wl.E + 1) * 4 + wl.E * (8 + 8 + 4 + 4)
+    out = wl.R * wl.n * 4
+    return {"weights": weights, "acts": acts, "tables": tables, "out": out,
+            "total": weights + acts + tables + out}
+
+
+def cpu_baseline(wl, budget_s: float):
+    """Time the oracle (as it stands) on a bounded sample of the same workload: act-quant of every
+    token row, then the grouped GEMM of the first experts' packed rows, adding experts until about
+    budget_s of CPU work.  Returns the weight-stream rate of the sample in TB/s."""
+    import oracle
+    oracle.build()
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    codes, scales = oracle.act_quant(wl.x)
+    t_aq = time.perf_counter() - t0
+    pc, ps = codes[wl.row_ids], scales[wl.row_ids]
+    ws = [wl.w_of(e) for e in range(wl.E)]
+    ss = [wl.s_of(e) for e in range(wl.E)]
+    done_e, rows, t_gemm, nbytes = 0, 0, 0.0, 0
+    used_threads = 1
+    e = 0
+    while e < wl.E and t_gemm + t_aq < budget_s:
+        # grow the batch geometrically so that thread start-up is amortised
+        e_hi = min(wl.E, e + max(1, done_e))
+        r0, r1 = int(wl.offsets[e]), int(wl.offsets[e_hi])
+        if r1 > r0:
+            t1 = time.perf_counter()
+            oracle.grouped_gemm(pc, ps, wl.offsets, ws, ss, wl.kinds, wl.scale2, wl.n, row0=r0,
+                                row1=r1, threads=threads)
+            t_gemm += time.perf_counter() - t1
+            used_threads = max(used_threads, min(threads, r1 - r0))
+        for ee in range(e, e_hi):
+            if wl.offsets[ee + 1] > wl.offsets[ee]:
+                nbytes += wl.n * wl.k // 2 + wl.n * wl.k // workloads.GROUP_SIZE[int(wl.kinds[ee])] + 4
+        rows += r1 - r0
+        done_e = e_hi
+        e = e_hi
+    frac = done_e / wl.E
+    elapsed = t_gemm + t_aq * frac
+    return {"value": nbytes / elapsed / 1e12, "unit": "TB/s", "cores": used_threads,
+            "kind": "oracle",
+            "sample": (f"oracle act-quant of all {wl.x.shape[0]} token rows (time pro-rated to the "
+                       f"sampled share) + f64 grouped GEMM of experts 0..{done_e - 1} "
+                       f"({rows} packed rows, {nbytes} weight bytes) of the same workload; "
+                       f"{t_gemm:.1f} s GEMM + {t_aq:.1f} s act-quant")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="config3", choices=["config3", "config4"])
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the cpu_baseline leg (0 disables it)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_scaled_fp4_quant_amd as fp4
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    log(f"library: {fp4.version()}  device: {torch.cuda.get_device_name(dev)}")
+
+    t0 = time.perf_counter()
+    wl = workloads.config3() if args.workload == "config3" else workloads.config4()
+    log(f"workload: {wl.name}  (generated in {time.perf_counter() - t0:.1f} s)")
+
+    x = torch.from_numpy(wl.x).to(dev)
+    row_ids = torch.from_numpy(wl.row_ids).to(dev)
+    offsets = torch.from_numpy(wl.offsets).to(dev)
+    kinds = torch.from_numpy(wl.kinds).to(dev)
+    scale2 = torch.from_numpy(wl.scale2.astype(np.float32)).to(dev)
+    w_bank = torch.from_numpy(wl.w_bank).to(dev)
+    s_bank = torch.from_numpy(wl.s_bank).to(dev)
+    w_ptrs = torch.from_numpy((w_bank.data_ptr() + wl.w_off).astype(np.int64)).to(dev)
+    s_ptrs = torch.from_numpy((s_bank.data_ptr() + wl.s_off).astype(np.int64)).to(dev)
+    T, k = wl.x.shape
+    codes = torch.empty((T, k), dtype=torch.uint8, device=dev)
+    scales = torch.empty((T, k // 128), dtype=torch.float32, device=dev)
+    out = torch.empty((wl.R, wl.n), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        fp4.act_quant_fp8(x, codes, scales, stream=stream)
+        fp4.fp4_grouped_gemm(codes, scales, row_ids, offsets, w_ptrs, s_ptrs, kinds, scale2, wl.n,
+                             out=out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        fp4.act_quant_fp8(x, codes, scales, stream=stream)
+        ev[i][1].record(stream)
+        fp4.fp4_grouped_gemm(codes, scales, row_ids, offsets, w_ptrs, s_ptrs, kinds, scale2, wl.n,
+                             out=out, stream=stream)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = ev[0][0].elapsed_time(ev[K - 1][2]) / K
+    aq_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    gemm_ms_min = float(np.min([e[1].elapsed_time(e[2]) for e in ev]))
+    log(f"timed {K} steps: wall {wall * 1e3 / K:.3f} ms/step, events {step_ms:.3f} ms/step "
+        f"(act_quant {aq_ms * 1e3:.1f} us, grouped GEMM {gemm_ms * 1e3:.1f} us avg / "
+        f"{gemm_ms_min * 1e3:.1f} us min)")
+
+    alg = algorithmic_bytes(wl)
+    flops = 2.0 * wl.R * wl.k * wl.n
+    ws_bytes = alg["weights"]
+    gemm_s = gemm_ms * 1e-3
+    achieved_gbs = alg["total"] / gemm_s / 1e9
+    traffic = recorded_traffic(args.workload)
+    if args.workload == "config3":
+        value = ws_bytes / (step_ms * 1e-3) / 1e12
+        unit = "TB/s"
+        roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                    "traffic": traffic}
+    else:
+        value = flops / (step_ms * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        tf = flops / gemm_s / 1e12
+        roofline = {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_PEAK_TFLOPS["f16"],
+                    "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_TFLOPS["f16"], 4),
+                    "traffic": traffic}
+    log(f"weight stream {ws_bytes / 1e9:.3f} GB -> {ws_bytes / gemm_s / 1e12:.3f} TB/s in the GEMM "
+        f"kernel; algorithmic bytes {alg['total'] / 1e9:.3f} GB -> {achieved_gbs:.0f} GB/s "
+        f"({achieved_gbs / HBM_PEAK_GBS:.1%} of 8 TB/s); {flops / gemm_s / 1e12:.1f} TFLOP/s")
+
+    result = {
+        "metric": METRIC, "value": round(value, 4), "unit": unit, "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8xfp4->f32", "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": int(T), "experts": int(wl.E), "top_k": 8,
+                   "routed_rows": int(wl.R), "k": int(wl.k), "n": int(wl.n),
+                   "weight_stream_bytes": int(ws_bytes), "gemm_us": round(gemm_ms * 1e3, 2),
+                   "act_quant_us": round(aq_ms * 1e3, 2)},
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if args.cpu_budget > 0:
+        if args.workload == "config3":
+            log(f"cpu_baseline: timing the oracle for about {args.cpu_budget:.0f} s ...")
+            result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+            log(f"cpu_baseline: {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

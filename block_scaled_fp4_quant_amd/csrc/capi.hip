@@ -1,0 +1,133 @@
+// capi.hip -- the extern "C" entry points of libfp4moe (declared and documented in
+// include/fp4moe.h): host-side argument validation, kernel dispatch, per-thread error messages.
+#include <cstdarg>
+#include <cstdio>
+
+#include "fp4moe.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return FP4MOE_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(FP4MOE_ELAUNCH, "%s: HIP launch error: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int check_k(int32_t k, const char* what) {
+  if (k <= 0 || k % 128 != 0)
+    return fail(FP4MOE_EINVAL, "%s: k = %d must be a positive multiple of 128", what, (int)k);
+  return FP4MOE_OK;
+}
+
+// The GEMM kernels address every operand plane with 32-bit byte offsets: each plane must stay
+// below 2^31 bytes.
+constexpr int64_t kMaxPlaneBytes = (int64_t)1 << 31;
+
+int check_planes(int64_t a_rows, int32_t n, int32_t k, const char* what) {
+  if (a_rows * (int64_t)k >= kMaxPlaneBytes)
+    return fail(FP4MOE_EINVAL, "%s: activation plane of %lld x %d bytes exceeds 2^31", what,
+                (long long)a_rows, (int)k);
+  if ((int64_t)n * (k / 2) >= kMaxPlaneBytes)
+    return fail(FP4MOE_EINVAL, "%s: weight plane of %d x %d bytes exceeds 2^31", what, (int)n, (int)(k / 2));
+  return FP4MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int act_quant_fp8(const float* x, uint8_t* codes, float* scales, int32_t rows, int32_t k,
+                  hipStream_t stream) {
+  if (rows < 0) return fail(FP4MOE_EINVAL, "act_quant_fp8: rows = %d < 0", (int)rows);
+  if (int rc = check_k(k, "act_quant_fp8")) return rc;
+  if (rows == 0) return ok();
+  if (!x || !codes || !scales) return fail(FP4MOE_EINVAL, "act_quant_fp8: NULL buffer with rows > 0");
+  const int64_t ngroups = (int64_t)rows * (k / 128);
+  return launched(fp4moe::launch_act_quant(x, codes, scales, ngroups, stream), "act_quant_fp8");
+}
+
+int fp4_expert_gemm(const uint8_t* a_codes, const float* a_scales, const uint8_t* w_packed,
+                    const uint8_t* w_scales, float scale2, int32_t kind, float* out, int32_t g,
+                    int32_t n, int32_t k, hipStream_t stream) {
+  if (g < 0) return fail(FP4MOE_EINVAL, "fp4_expert_gemm: g = %d < 0", (int)g);
+  if (n <= 0) return fail(FP4MOE_EINVAL, "fp4_expert_gemm: n = %d must be positive", (int)n);
+  if (int rc = check_k(k, "fp4_expert_gemm")) return rc;
+  if (kind != FP4MOE_NVFP4 && kind != FP4MOE_MXFP4)
+    return fail(FP4MOE_EINVAL, "fp4_expert_gemm: kind = %d is neither 0 (NVFP4) nor 1 (MXFP4)", (int)kind);
+  if (g == 0) return ok();
+  if (!a_codes || !a_scales || !w_packed || !w_scales || !out)
+    return fail(FP4MOE_EINVAL, "fp4_expert_gemm: NULL buffer with g > 0");
+  if (int rc = check_planes(g, n, k, "fp4_expert_gemm")) return rc;
+  fp4moe::GemmArgs a{};
+  a.a_codes = a_codes;
+  a.a_scales = a_scales;
+  a.a_rows = g;
+  a.num_experts = 1;
+  a.total_rows = g;
+  a.w = w_packed;
+  a.s = w_scales;
+  a.scale2 = scale2;
+  a.kind = kind;
+  a.out = out;
+  a.n = n;
+  a.k = k;
+  return launched(fp4moe::launch_gemm_decode(a, stream), "fp4_expert_gemm");
+}
+
+int fp4_grouped_gemm(const uint8_t* a_codes, const float* a_scales, int32_t a_rows,
+                     const int32_t* row_ids, const int32_t* offsets, int32_t num_experts,
+                     int32_t total_rows, const uint64_t* w_ptrs, const uint64_t* s_ptrs,
+                     const int32_t* kinds, const float* scale2, float* out, int32_t n, int32_t k,
+                     hipStream_t stream) {
+  if (a_rows < 0 || total_rows < 0)
+    return fail(FP4MOE_EINVAL, "fp4_grouped_gemm: a_rows = %d, total_rows = %d must be >= 0",
+                (int)a_rows, (int)total_rows);
+  if (num_experts <= 0)
+    return fail(FP4MOE_EINVAL, "fp4_grouped_gemm: num_experts = %d must be positive", (int)num_experts);
+  if (n <= 0) return fail(FP4MOE_EINVAL, "fp4_grouped_gemm: n = %d must be positive", (int)n);
+  if (int rc = check_k(k, "fp4_grouped_gemm")) return rc;
+  if (!row_ids && a_rows < total_rows)
+    return fail(FP4MOE_EINVAL, "fp4_grouped_gemm: row_ids is NULL but a_rows = %d < total_rows = %d",
+                (int)a_rows, (int)total_rows);
+  if (total_rows == 0) return ok();
+  if (!a_codes || !a_scales || !offsets || !w_ptrs || !s_ptrs || !kinds || !scale2 || !out)
+    return fail(FP4MOE_EINVAL, "fp4_grouped_gemm: NULL buffer with total_rows > 0");
+  if (int rc = check_planes(a_rows, n, k, "fp4_grouped_gemm")) return rc;
+  fp4moe::GemmArgs a{};
+  a.a_codes = a_codes;
+  a.a_scales = a_scales;
+  a.row_ids = row_ids;
+  a.a_rows = a_rows;
+  a.offsets = offsets;
+  a.num_experts = num_experts;
+  a.total_rows = total_rows;
+  a.w_ptrs = w_ptrs;
+  a.s_ptrs = s_ptrs;
+  a.kinds = kinds;
+  a.scale2s = scale2;
+  a.out = out;
+  a.n = n;
+  a.k = k;
+  return launched(fp4moe::launch_gemm_decode(a, stream), "fp4_grouped_gemm");
+}
+
+const char* fp4moe_last_error(void) { return g_err; }
+
+const char* fp4moe_version(void) { return "libfp4moe 0.1.0 (gfx950)"; }
+
+}  // extern "C"

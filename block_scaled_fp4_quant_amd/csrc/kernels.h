@@ -1,0 +1,40 @@
+// kernels.h -- internal launch interface between the C ABI (capi.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4moe {
+
+// One GEMM problem in the layout of fp4moe.h.  Single expert: offsets == nullptr, the planes are
+// w/s/kind/scale2 and the rows are 0 .. total_rows-1 (row_ids == nullptr).  Grouped: the planes
+// come from the device tables w_ptrs/s_ptrs/kinds/scale2s indexed by expert.
+struct GemmArgs {
+  const uint8_t* a_codes;
+  const float* a_scales;
+  const int32_t* row_ids;     // nullable
+  int32_t a_rows;
+  const int32_t* offsets;     // [num_experts + 1] or nullptr
+  int32_t num_experts;
+  int32_t total_rows;
+  const uint64_t* w_ptrs;
+  const uint64_t* s_ptrs;
+  const int32_t* kinds;
+  const float* scale2s;
+  const uint8_t* w;
+  const uint8_t* s;
+  float scale2;
+  int32_t kind;
+  float* out;
+  int32_t n;
+  int32_t k;
+};
+
+hipError_t launch_act_quant(const float* x, uint8_t* codes, float* scales, int64_t ngroups,
+                            hipStream_t stream);
+
+// Row-streaming kernel for few rows per expert (decode): every expert's weights are read once per
+// pass of 32 rows.
+hipError_t launch_gemm_decode(const GemmArgs& a, hipStream_t stream);
+
+}  // namespace fp4moe

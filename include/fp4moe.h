@@ -1,0 +1,117 @@
+/*
+ * fp4moe.h -- C ABI of libfp4moe: FP8 E4M3 activation quantization and the block-scaled FP4
+ * (NVFP4 / MXFP4) expert GEMM, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources the operations are defined by (cited by page title and item):
+ *   [GATE]  memra-engine 0.98.0, src/bin/dsv4_native_gemm_gate.rs: `quant_rows` (act-quant), the
+ *           `ExpertRaw` layout, `f64_ref` (the quantized GEMM), comparison 2 (error model), and the
+ *           FFI calls of the act-quant and FP4 GEMM kernels in `main` (pointer/size/stream
+ *           convention, return code 0 = success, kind 0 = NVFP4 / 1 = MXFP4).
+ *   [CHECK] memra-engine 0.71.0, src/bin/kernel_check.rs: f16g grouped GEMM section (rows packed
+ *           per expert with a CSR offsets array) and the direct-from-quant section (a per-expert
+ *           table of weight addresses).
+ *
+ * Conventions for every call:
+ *   - All pointers are DEVICE pointers unless marked [host].  Buffers are row-major and densely
+ *     packed.  The caller allocates every buffer; the library never allocates, frees or
+ *     synchronizes.  Each call only enqueues kernels on `stream` (0 = the null stream) and returns.
+ *   - Sizes are int32.  Arguments are validated on the host before anything is enqueued.
+ *   - Return value: FP4MOE_OK (0) on success; FP4MOE_EINVAL for an invalid argument (nothing was
+ *     enqueued); FP4MOE_ELAUNCH when the HIP runtime reports a launch error.  fp4moe_last_error()
+ *     then holds a message (per thread).
+ *   - Calls that write the same output buffer, or whose inputs another call writes, race unless
+ *     the caller orders them (same stream or events).
+ */
+#ifndef FP4MOE_H
+#define FP4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define FP4MOE_API __attribute__((visibility("default")))
+#else
+#define FP4MOE_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { FP4MOE_NVFP4 = 0, FP4MOE_MXFP4 = 1 };
+enum { FP4MOE_OK = 0, FP4MOE_EINVAL = 1, FP4MOE_ELAUNCH = 2 };
+
+/*
+ * act_quant_fp8 -- [GATE: quant_rows].  For every row r and every group q of 128 columns:
+ *   amax = max over the group of |x|, floored at 1e-4;
+ *   s    = the smallest power of two >= f32(amax * f32(1/448));
+ *   codes[r, c] = E4M3(clamp(x[r, c] / s, -448, 448)), round to nearest even, sign kept on zero;
+ *   scales[r, q] = s.
+ * x:      f32 [rows, k], read only.
+ * codes:  u8  [rows, k], written (OCP E4M3FN bytes, bias 7, max 448).
+ * scales: f32 [rows, k/128], written.
+ * Errors: EINVAL if rows < 0, k <= 0, k % 128 != 0, or a pointer is NULL while rows > 0.
+ * rows == 0 is a no-op.  Inputs must be finite (NaN/Inf give unspecified codes).
+ */
+FP4MOE_API int act_quant_fp8(const float* x, uint8_t* codes, float* scales, int32_t rows, int32_t k,
+                  hipStream_t stream);
+
+/*
+ * fp4_expert_gemm -- [GATE: f64_ref, ExpertRaw].  One expert:
+ *   out[r, c] = sum over groups j of ( sum over the gs k in group j of
+ *                 E4M3(a_codes[r, k]) * E2M1(nibble(w_packed, c, k)) ) * ws[c, j] * a_scales[r, k/128]
+ * with gs = 16 and ws = E4M3(w_scales[c, j]) * scale2 for NVFP4 (kind 0), gs = 32 and
+ * ws = 2^(w_scales[c, j] - 127) for MXFP4 (kind 1; scale2 ignored), accumulated in f32.
+ * a_codes:  u8  [g, k] E4M3 bytes;  a_scales: f32 [g, k/128].
+ * w_packed: u8  [n, k/2]: element (c, k) is the low nibble of byte (c, k/2) for even k, the high
+ *           nibble for odd k.
+ * w_scales: u8  [n, k/16] E4M3 (NVFP4) or [n, k/32] E8M0 (MXFP4).
+ * scale2:   [host] f32 per-tensor NVFP4 scale.
+ * out:      f32 [g, n], overwritten.
+ * Accuracy: |out - exact| <= k * 2^-24 * sum over k of |term| per output (f32 accumulation),
+ * for inputs whose products stay in the f32 normal range.
+ * Errors: EINVAL if g < 0, n <= 0, k <= 0, k % 128 != 0, kind not 0/1, a pointer is NULL while
+ * g > 0, or g*k or n*k/2 is 2^31 or more (planes are addressed with 32-bit offsets).
+ * g == 0 is a no-op.
+ */
+FP4MOE_API int fp4_expert_gemm(const uint8_t* a_codes, const float* a_scales, const uint8_t* w_packed,
+                    const uint8_t* w_scales, float scale2, int32_t kind, float* out, int32_t g,
+                    int32_t n, int32_t k, hipStream_t stream);
+
+/*
+ * fp4_grouped_gemm -- [CHECK: f16g grouped GEMM, CSR offsets; GATE: f64_ref per expert].
+ * Routed rows packed per expert: packed row p belongs to expert e when
+ * offsets[e] <= p < offsets[e+1], and its activation is row row_ids[p] of a_codes/a_scales (row p
+ * itself when row_ids is NULL).  out[p, :] is fp4_expert_gemm of that activation row with expert
+ * e's planes, format and scale2.  Experts with no rows cost nothing; both formats may be mixed.
+ * a_codes:  u8  [a_rows, k];  a_scales: f32 [a_rows, k/128]  (e.g. one row per token).
+ * row_ids:  int32 [total_rows] indices into [0, a_rows), or NULL (then a_rows >= total_rows).
+ * offsets:  int32 [num_experts + 1], offsets[0] = 0, non-decreasing, offsets[E] = total_rows.
+ * w_ptrs, s_ptrs: u64 [num_experts] device addresses of expert e's w_packed [n, k/2] and
+ *           w_scales [n, k/gs] planes.
+ * kinds:    int32 [num_experts] (0 NVFP4, 1 MXFP4);  scale2: f32 [num_experts] (NVFP4 only).
+ * out:      f32 [total_rows, n], every row overwritten.
+ * All tables are read on the device only.  Out-of-range table entries never cause an
+ * out-of-bounds access: offsets are clamped to [0, total_rows]; a row whose row_ids entry is
+ * outside [0, a_rows), or whose expert has a kind other than 0/1, is written as NaN.
+ * Errors: EINVAL if a_rows < 0, total_rows < 0, num_experts <= 0, n <= 0, k <= 0, k % 128 != 0,
+ * row_ids is NULL while a_rows < total_rows, a pointer is NULL while total_rows > 0, or a_rows*k
+ * or n*k/2 is 2^31 or more.  total_rows == 0 is a no-op.
+ */
+FP4MOE_API int fp4_grouped_gemm(const uint8_t* a_codes, const float* a_scales, int32_t a_rows,
+                     const int32_t* row_ids, const int32_t* offsets, int32_t num_experts,
+                     int32_t total_rows, const uint64_t* w_ptrs, const uint64_t* s_ptrs,
+                     const int32_t* kinds, const float* scale2, float* out, int32_t n, int32_t k,
+                     hipStream_t stream);
+
+/* Message for the last nonzero return code of a call made by this thread ("" if none). */
+FP4MOE_API const char* fp4moe_last_error(void);
+
+/* Library version string. */
+FP4MOE_API const char* fp4moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP4MOE_H */

@@ -1,0 +1,222 @@
+"""GPU FP4 expert GEMM (single and grouped) vs the oracle: every output within
+k * 2^-24 * sum|p|, bit identity on exact-by-construction inputs, determinism, batch invariance,
+and the degenerate cases (empty experts, invalid table entries, ragged shapes)."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp4_quant_amd as fp4
+import workloads
+from gpu_util import GroupedDevice, check_bound, dev, require_gpu
+
+pytestmark = pytest.mark.gpu
+NV, MX = workloads.NVFP4, workloads.MXFP4
+
+
+def run_single(wl, orc, check_codes=True):
+    """act_quant + fp4_expert_gemm on the GPU; full oracle comparison."""
+    x = dev(wl.x)
+    codes, scales = fp4.act_quant_fp8(x)
+    ex = wl.expert
+    out = fp4.fp4_expert_gemm(codes, scales, dev(ex.w), dev(ex.s), ex.scale2, ex.kind)
+    torch.cuda.synchronize()
+    rc, rs = orc.act_quant(wl.x)
+    if check_codes:
+        assert np.array_equal(codes.cpu().numpy(), rc)
+    ref, absp = orc.expert_gemm(rc, rs, ex.w, ex.s, ex.scale2, ex.kind)
+    return out.cpu().numpy(), ref, absp
+
+
+def test_config0(orc):
+    wl = workloads.config0()
+    got, ref, absp = run_single(wl, orc)
+    worst = check_bound(got, ref, absp, wl.k, "config0")
+    print(f"config0 worst err / (2^-24 sum|p|) = {worst:.2f}; pages' op count "
+          f"{orc.pages_op_count(NV, wl.k):.0f}")
+
+
+@pytest.mark.parametrize("g", [1, 2, 4, 8])
+def test_config1(orc, g):
+    wl = workloads.config1(g)
+    got, ref, absp = run_single(wl, orc)
+    check_bound(got, ref, absp, wl.k, f"config1 g={g}")
+
+
+def test_config2(orc):
+    wl = workloads.config2()
+    got, ref, absp = run_single(wl, orc)
+    check_bound(got, ref, absp, wl.k, "config2")
+
+
+SHAPES = [(1, 16, 128), (5, 200, 256), (16, 64, 640), (17, 72, 384), (31, 130, 512),
+          (32, 256, 1024), (33, 96, 256), (50, 64, 2048), (100, 48, 384)]
+
+
+@pytest.mark.parametrize("kind", [NV, MX])
+@pytest.mark.parametrize("g,n,k", SHAPES)
+def test_random_shapes(orc, kind, g, n, k):
+    wl = workloads.single_random(1000 + g * 7 + n + k, g, n, k, kind, scale2=2.0 ** -5, x_scale=2.0)
+    got, ref, absp = run_single(wl, orc)
+    check_bound(got, ref, absp, k, f"g={g} n={n} k={k} kind={kind}")
+
+
+def test_non_pow2_scale2(orc):
+    wl = workloads.single_random(77, 9, 80, 512, NV, scale2=0.37)
+    got, ref, absp = run_single(wl, orc)
+    check_bound(got, ref, absp, 512, "scale2=0.37")
+
+
+@pytest.mark.parametrize("kind", [NV, MX])
+@pytest.mark.parametrize("g,n,k", [(3, 48, 512), (16, 64, 7168), (29, 130, 2048)])
+def test_exact_arm_bit_identity(orc, kind, g, n, k):
+    a_codes, a_scales, ex = workloads.exact_arm(g + n, g, n, k, kind)
+    out = fp4.fp4_expert_gemm(dev(a_codes), dev(a_scales), dev(ex.w), dev(ex.s), ex.scale2, kind)
+    ref, _ = orc.expert_gemm(a_codes, a_scales, ex.w, ex.s, ex.scale2, kind)
+    got = out.cpu().numpy()
+    assert np.array_equal(got.astype(np.float64), ref), \
+        f"{int(np.sum(got != ref))} outputs differ; max diff {np.max(np.abs(got - ref))}"
+
+
+def test_determinism_and_row_invariance(orc):
+    wl = workloads.single_random(5, 24, 256, 1024, NV)
+    codes, scales = fp4.act_quant_fp8(dev(wl.x))
+    w, s = dev(wl.expert.w), dev(wl.expert.s)
+    o1 = fp4.fp4_expert_gemm(codes, scales, w, s, wl.expert.scale2, NV)
+    o2 = fp4.fp4_expert_gemm(codes, scales, w, s, wl.expert.scale2, NV)
+    assert torch.equal(o1, o2)
+    # each row alone gives the same bits as in the batched launch
+    for r in (0, 7, 16, 23):
+        o_r = fp4.fp4_expert_gemm(codes[r:r + 1].contiguous(), scales[r:r + 1].contiguous(), w, s,
+                                  wl.expert.scale2, NV)
+        assert torch.equal(o_r[0], o1[r])
+
+
+def grouped_check(gd: GroupedDevice, orc, out, rows=None):
+    wl = gd.wl
+    codes, scales = orc.act_quant(wl.x)
+    pc, ps = codes[wl.row_ids], scales[wl.row_ids]
+    ws = [wl.w_of(e) for e in range(wl.E)]
+    ss = [wl.s_of(e) for e in range(wl.E)]
+    got = out.cpu().numpy()
+    if rows is None:
+        ref, absp = orc.grouped_gemm(pc, ps, wl.offsets, ws, ss, wl.kinds, wl.scale2, wl.n)
+        return check_bound(got, ref, absp, wl.k, wl.name)
+    r, c = rows
+    ref, absp = orc.grouped_gemm_points(pc, ps, wl.offsets, ws, ss, wl.kinds, wl.scale2, wl.n, r, c)
+    return check_bound(got[r, c], ref, absp, wl.k, wl.name + " (sampled)")
+
+
+@pytest.mark.parametrize("seed,T,E,top,n,k", [(1, 40, 8, 2, 96, 512), (2, 64, 16, 4, 200, 384),
+                                              (3, 300, 12, 3, 64, 1024)])
+def test_grouped_small_mixed(orc, seed, T, E, top, n, k):
+    kinds = [NV if e % 3 else MX for e in range(E)]
+    wl = workloads.grouped_random(seed, T, E, top, n, k, kinds=kinds, empty_experts=(1, E - 2))
+    gd = GroupedDevice(wl)
+    _, _, out = gd.step()
+    grouped_check(gd, orc, out)
+
+
+def test_grouped_matches_single_expert_bits(orc):
+    wl = workloads.grouped_random(4, 96, 8, 3, 128, 512, kinds=[NV, MX] * 4)
+    gd = GroupedDevice(wl)
+    codes, scales, out = gd.step()
+    for e in range(wl.E):
+        lo, hi = int(wl.offsets[e]), int(wl.offsets[e + 1])
+        if hi == lo:
+            continue
+        ids = gd.row_ids[lo:hi].long()
+        o = fp4.fp4_expert_gemm(codes[ids].contiguous(), scales[ids].contiguous(),
+                                dev(wl.w_of(e)), dev(wl.s_of(e)), float(wl.scale2[e]), int(wl.kinds[e]))
+        assert torch.equal(o, out[lo:hi]), f"expert {e}"
+
+
+def test_grouped_without_row_ids(orc):
+    wl = workloads.grouped_random(5, 32, 4, 2, 64, 256, kinds=[NV, MX, NV, MX])
+    gd = GroupedDevice(wl)
+    codes, scales = fp4.act_quant_fp8(gd.x)
+    pc, ps = codes[gd.row_ids.long()].contiguous(), scales[gd.row_ids.long()].contiguous()
+    out = fp4.fp4_grouped_gemm(pc, ps, None, gd.offsets, gd.w_ptrs, gd.s_ptrs, gd.kinds,
+                               gd.scale2, wl.n, out=torch.empty((wl.R, wl.n), device=pc.device))
+    _, _, ref_out = gd.step()
+    assert torch.equal(out, ref_out)
+
+
+def test_grouped_invalid_entries_give_nan(orc):
+    wl = workloads.grouped_random(6, 24, 4, 2, 64, 256)
+    gd = GroupedDevice(wl)
+    codes, scales, good = gd.step()
+    bad_ids = gd.row_ids.clone()
+    bad_ids[3] = 10 ** 6                       # outside [0, a_rows)
+    bad_ids[5] = -1
+    bad_kinds = gd.kinds.clone()
+    bad_kinds[2] = 7
+    out = fp4.fp4_grouped_gemm(codes, scales, bad_ids, gd.offsets, gd.w_ptrs, gd.s_ptrs, bad_kinds,
+                               gd.scale2, wl.n)
+    torch.cuda.synchronize()
+    nan_rows = {3, 5} | set(range(int(wl.offsets[2]), int(wl.offsets[3])))
+    for r in range(wl.R):
+        if r in nan_rows:
+            assert bool(torch.isnan(out[r]).all()), r
+        else:
+            assert torch.equal(out[r], good[r]), r
+
+
+def test_grouped_offsets_are_clamped(orc):
+    # offsets past total_rows are clamped: rows beyond R are never touched and every row is written
+    wl = workloads.grouped_random(7, 16, 4, 2, 32, 128)
+    gd = GroupedDevice(wl)
+    codes, scales, good = gd.step()
+    offs = gd.offsets.clone()
+    offs[2] = offs[2] + 10 ** 6                # expert 1 now claims rows past the end
+    sentinel = torch.full((wl.R + 8, wl.n), 123.0, device=codes.device)
+    out = sentinel[:wl.R]
+    fp4.fp4_grouped_gemm(codes, scales, gd.row_ids, offs, gd.w_ptrs, gd.s_ptrs, gd.kinds, gd.scale2,
+                         wl.n, out=out)
+    torch.cuda.synchronize()
+    assert bool((sentinel[wl.R:] == 123.0).all())
+    lo = int(wl.offsets[1])
+    assert torch.equal(out[:lo], good[:lo])
+
+
+def _sample(R, n, count, seed):
+    rng = np.random.default_rng(seed)
+    rows = np.concatenate([rng.integers(0, R, count - 2 * n // 16), np.zeros(n // 16, np.int64),
+                           np.full(n // 16, R - 1)])
+    cols = np.concatenate([rng.integers(0, n, count - 2 * n // 16), np.arange(0, n, 16),
+                           np.arange(0, n, 16)])
+    return rows.astype(np.int64), cols.astype(np.int64)
+
+
+@pytest.fixture(scope="module")
+def config3_dev():
+    return GroupedDevice(workloads.config3())
+
+
+@pytest.fixture(scope="module")
+def config4_dev():
+    return GroupedDevice(workloads.config4())
+
+
+def test_config3_sampled(orc, config3_dev):
+    gd = config3_dev
+    _, _, out = gd.step()
+    _, _, out2 = gd.step()
+    assert torch.equal(out, out2)                              # run-to-run bit identity
+    assert not bool(torch.isnan(out).any())
+    rows, cols = _sample(gd.R, gd.n, 16384, 3)
+    worst = grouped_check(gd, orc, out, (rows, cols))
+    print(f"config3 worst err / (2^-24 sum|p|) over {rows.size} samples = {worst:.2f}")
+
+
+def test_config4_sampled(orc, config4_dev):
+    gd = config4_dev
+    _, _, out = gd.step()
+    assert not bool(torch.isnan(out).any())
+    rows, cols = _sample(gd.R, gd.n, 16384, 4)
+    # include rows of the MXFP4 expert (the last one)
+    lo, hi = int(gd.wl.offsets[-2]), int(gd.wl.offsets[-1])
+    if hi > lo:
+        rows = np.concatenate([rows, np.arange(lo, hi)[:64]])
+        cols = np.concatenate([cols, (np.arange(lo, hi)[:64] * 37) % gd.n])
+    worst = grouped_check(gd, orc, out, (rows, cols))
+    print(f"config4 worst err / (2^-24 sum|p|) over {rows.size} samples = {worst:.2f}")

@@ -1,0 +1,97 @@
+"""The C-ABI library loads, exports every function include/*.h declares, and rejects invalid
+arguments on the host (these calls enqueue nothing, so no GPU is needed)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+LIB = os.path.join(ROOT, "block_scaled_fp4_quant_amd", "libfp4moe.so")
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"FP4MOE_API\s+[\w\s\*]+?\b(\w+)\s*\(", text))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} is not built (run __graft_entry__.build())")
+    import block_scaled_fp4_quant_amd as m
+    return m.lib()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for fn in ("act_quant_fp8", "fp4_expert_gemm", "fp4_grouped_gemm", "fp4moe_last_error",
+               "fp4moe_version"):
+        assert fn in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for fn in declared_functions():
+        assert hasattr(lib, fn), fn
+
+
+def test_version(lib):
+    import block_scaled_fp4_quant_amd as m
+    assert "gfx950" in m.version()
+
+
+NULL = None
+BAD = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("rows,k", [(-1, 128), (4, 0), (4, 100), (4, 129)])
+def test_act_quant_rejects(lib, rows, k):
+    assert lib.act_quant_fp8(BAD, BAD, BAD, rows, k, NULL) == 1
+    assert lib.fp4moe_last_error().decode().startswith("act_quant_fp8")
+
+
+def test_act_quant_null_and_noop(lib):
+    assert lib.act_quant_fp8(NULL, BAD, BAD, 4, 128, NULL) == 1
+    assert lib.act_quant_fp8(NULL, NULL, NULL, 0, 128, NULL) == 0      # rows == 0: no-op
+    assert lib.fp4moe_last_error().decode() == ""
+
+
+@pytest.mark.parametrize("g,n,k,kind", [(-1, 16, 128, 0), (4, 0, 128, 0), (4, 16, 96, 0),
+                                        (4, 16, 128, 2), (4, 16, 128, -1), (1 << 24, 16, 256, 0),
+                                        (4, 1 << 20, 8192, 1)])
+def test_expert_gemm_rejects(lib, g, n, k, kind):
+    assert lib.fp4_expert_gemm(BAD, BAD, BAD, BAD, 1.0, kind, BAD, g, n, k, NULL) == 1
+    assert "fp4_expert_gemm" in lib.fp4moe_last_error().decode()
+
+
+def test_expert_gemm_null_and_noop(lib):
+    assert lib.fp4_expert_gemm(BAD, BAD, NULL, BAD, 1.0, 0, BAD, 4, 16, 128, NULL) == 1
+    assert lib.fp4_expert_gemm(NULL, NULL, NULL, NULL, 1.0, 1, NULL, 0, 16, 128, NULL) == 0
+
+
+@pytest.mark.parametrize("a_rows,row_ids,E,R,n,k", [(-1, BAD, 4, 8, 16, 128), (8, BAD, 4, -1, 16, 128),
+                                                    (8, BAD, 0, 8, 16, 128), (8, BAD, 4, 8, 0, 128),
+                                                    (8, BAD, 4, 8, 16, 200), (4, NULL, 4, 8, 16, 128)])
+def test_grouped_gemm_rejects(lib, a_rows, row_ids, E, R, n, k):
+    assert lib.fp4_grouped_gemm(BAD, BAD, a_rows, row_ids, BAD, E, R, BAD, BAD, BAD, BAD, BAD,
+                                n, k, NULL) == 1
+    assert "fp4_grouped_gemm" in lib.fp4moe_last_error().decode()
+
+
+def test_grouped_gemm_null_and_noop(lib):
+    assert lib.fp4_grouped_gemm(BAD, BAD, 8, BAD, NULL, 4, 8, BAD, BAD, BAD, BAD, BAD, 16, 128, NULL) == 1
+    assert lib.fp4_grouped_gemm(NULL, NULL, 0, NULL, NULL, 4, 0, NULL, NULL, NULL, NULL, NULL,
+                                16, 128, NULL) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import block_scaled_fp4_quant_amd as m
+    monkeypatch.setattr(m, "_lib", None)
+    monkeypatch.setattr(m, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(m.Fp4MoeError):
+        m.lib()
