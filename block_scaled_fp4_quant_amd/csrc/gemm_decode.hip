@@ -76,21 +76,25 @@ struct PassOffsets {
   uint32_t w[kCT], s[kCT], a[MT], as[MT];
 };
 
+// Loads of block b.  Every load is issued even when b is past the last block: its offset is then
+// out of range and the load returns zeros without touching memory, so the number of outstanding
+// loads is the same on every path and the compiler's wait counts stay exact.
 template <int MT, int KIND>
 __device__ __forceinline__ void load_block(const PassRsrc& r, const PassOffsets<MT>& o, int b,
-                                           BlockData<MT>& d) {
+                                           bool valid, BlockData<MT>& d) {
+  const uint32_t ub = (uint32_t)b;
 #pragma unroll
   for (int ct = 0; ct < kCT; ++ct) {
-    d.wq[ct] = buf_load_x4(r.w, o.w[ct] + (uint32_t)b * 64u);
-    d.sc[ct] = (KIND == kNV) ? buf_load_u16(r.s, o.s[ct] + (uint32_t)b * 8u)
-                             : buf_load_u8(r.s, o.s[ct] + (uint32_t)b * 4u);
+    d.wq[ct] = buf_load_x4(r.w, valid ? o.w[ct] + ub * 64u : kOffNone);
+    d.sc[ct] = (KIND == kNV) ? buf_load_u16(r.s, valid ? o.s[ct] + ub * 8u : kOffNone)
+                             : buf_load_u8(r.s, valid ? o.s[ct] + ub * 4u : kOffNone);
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const uint32_t ab = o.a[mt] + (uint32_t)b * 128u;
+    const uint32_t ab = valid ? o.a[mt] + ub * 128u : kOffNone;
     d.aq[mt][0] = buf_load_x4(r.a, ab);
     d.aq[mt][1] = buf_load_x4(r.a, ab + (KIND == kNV ? 16u : 64u));
-    d.asa[mt] = u2f(buf_load_u32(r.as, o.as[mt] + (uint32_t)b * 4u));
+    d.asa[mt] = u2f(buf_load_u32(r.as, valid ? o.as[mt] + ub * 4u : kOffNone));
   }
 }
 
@@ -155,7 +159,8 @@ __device__ __forceinline__ void compute_block(const BlockData<MT>& d, f32x4 (&ac
 template <int MT, int KIND>
 __device__ void run_pass(const GemmArgs& p, const ExpertView& ex, int n0, int m0, int mend,
                          f32x4 (*red)[2][kCT][64]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
   const int c16 = lane & 15, g = lane >> 4;
   const int k = p.k, nblk = k >> 7;
   constexpr int GS = (KIND == kNV) ? 16 : 32;
@@ -187,19 +192,28 @@ __device__ void run_pass(const GemmArgs& p, const ExpertView& ex, int n0, int m0
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct) acc[mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Blocks wave, wave+4, ... in a two-buffer pipeline: the loads of the next block are in flight
-  // while the current one is computed.
-  BlockData<MT> d0, d1;
-  int b = wave;
-  if (b < nblk) load_block<MT, KIND>(r, o, b, d0);
-  while (b < nblk) {
-    if (b + kWaves < nblk) load_block<MT, KIND>(r, o, b + kWaves, d1);
-    compute_block<MT, KIND>(d0, acc);
-    b += kWaves;
-    if (b >= nblk) break;
-    if (b + kWaves < nblk) load_block<MT, KIND>(r, o, b + kWaves, d0);
-    compute_block<MT, KIND>(d1, acc);
-    b += kWaves;
+  // Blocks wave, wave+4, ... through a ring of D register buffers: the loads of the next D-1
+  // blocks are in flight while one block is computed (the stream is latency-bound otherwise).
+  constexpr int D = (MT == 1) ? 4 : 2;
+  BlockData<MT> buf[D];
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    const int bj = wave + kWaves * j;
+    load_block<MT, KIND>(r, o, bj, bj < nblk, buf[j]);
+    // Pin every group of loads where it is written: the machine scheduler would otherwise sink
+    // loads toward their first use (the loop latch) or reorder the prologue, and the wait counts
+    // at the loop head would then drain the whole ring.
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int b0 = wave; b0 < nblk; b0 += kWaves * D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int bb = b0 + kWaves * j;
+      if (bb < nblk) compute_block<MT, KIND>(buf[j], acc);
+      const int bn = bb + kWaves * D;
+      load_block<MT, KIND>(r, o, bn, bn < nblk, buf[j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // Fixed-order reduction of the 4 wavefronts' partial tiles.
