@@ -6,28 +6,34 @@
 // weights.  Grouped form: rows packed per expert with a CSR offsets array (kernel_check.rs page,
 // f16g grouped GEMM section).
 //
-// Work decomposition.  A workgroup of 4 wavefronts owns 64 output columns of one expert and streams
-// that expert's 64 weight rows (k/2 + k/gs bytes each) once per pass of up to 32 activation rows;
-// with decode-sized row counts that is one pass, so the weights are read from HBM exactly once.
-// The 4 wavefronts split k: wavefront w takes the 128-wide k blocks w, w+4, w+8, ...; each covers
-// all 64 columns (4 MFMA column tiles) and all rows of the pass (1 or 2 MFMA row tiles), and the
-// 4 partial tiles are added in a fixed order through LDS at the end (deterministic).
+// Work decomposition.  A workgroup of 4 wavefronts owns 256 output columns of one expert; each
+// wavefront owns 64 of them (4 MFMA column tiles) over the whole of k, for every row of a pass of up
+// to 32 activation rows.  With decode-sized row counts a pass covers all rows, so every weight byte
+// is read from HBM exactly once.
+//
+// Data movement (the path is HBM-bound; what costs is the number and geometry of load requests):
+//   weights: each lane streams 16 bytes per column tile per 128-wide k block straight into a ring of
+//     4 register slots (one per block of a 512-wide k chunk); a load instruction covers 16 column
+//     rows x 64 contiguous bytes.
+//   activation codes, activation scales and weight scales: staged per 512-wide k chunk through a
+//     two-stage LDS ring shared by the 4 wavefronts, loaded as contiguous row pieces (512 bytes of
+//     activation codes, 32 or 16 bytes of weight scales per column row).  One activation load serves
+//     256 columns.  NVFP4 weight scales are transposed on the way in so that a lane reads the scale
+//     pairs of its 4 blocks with one 8-byte LDS read.
 //
 // Inner step for one 128-wide k block, per lane (c16 = lane%16, g = lane/16):
-//   weights: one 16-byte load per column tile = 32 nibbles k0+32g .. +32 of column c16.
 //   NVFP4: f16 MFMA 16x16x32.  Nibbles -> f16 with the hardware FP4 conversion, times the E4M3
-//     scale in f16 (exact); activation bytes -> f16 (exact).  MFMA i of the block pairs lane
-//     group g with k = k0 + 32g + 8i .. +8, so the 128 k of a block are one activation-scale group:
-//     the block's four MFMAs accumulate a partial tile that is scaled by as[r, block] in one f32
-//     FMA.  scale2 multiplies the final sum (exact for power-of-two scale2; otherwise within one
-//     f32 rounding of the per-group scale, inside the accuracy bound).
-//   MXFP4: one block-scaled MFMA 16x16x128 per column tile, raw E4M3 activation bytes and raw
-//     nibbles, E8M0 weight scales and the activation scale's exponent as the E8M0 row scale: no
-//     conversion work at all.
+//     scale in f16 (exact); activation bytes -> f16 (exact).  MFMA i of the block pairs lane group g
+//     with k = k0 + 32g + 8i .. +8, so the block's four MFMAs cover one activation-scale group and
+//     accumulate a partial tile that is scaled by as[r, block] in one f32 FMA.  scale2 multiplies
+//     the final sum (exact for power-of-two scale2; otherwise within one f32 rounding of the
+//     per-group weight scale, inside the accuracy bound).
+//   MXFP4: one block-scaled MFMA 16x16x128 per column tile on raw E4M3 activation bytes and raw
+//     nibbles, with the E8M0 weight scales and the activation scale's exponent as E8M0 row scale.
 //
 // Workgroup order is XCD-aware when there are >= 8 experts: consecutive workgroup ids go to
-// different XCDs, so the ids are arranged such that every column tile of one expert lands on the
-// same XCD and the expert's activation rows are fetched into one L2 only.
+// different XCDs, so ids are arranged such that all column tiles of one expert land on one XCD and
+// the expert's activation rows are fetched into one L2 only.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -36,18 +42,29 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kTileN = 64;
-constexpr int kCT = kTileN / 16;
-constexpr int kRowsPerPass = 32;
+constexpr int kCT = 4;                       // MFMA column tiles per wavefront
+constexpr int kWaveCols = 16 * kCT;          // 64
+constexpr int kTileN = kWaves * kWaveCols;   // 256 columns per workgroup
+constexpr int kRows = 32;                    // rows per pass (2 MFMA row tiles)
+constexpr int kChunkK = 512;                 // k per LDS stage
+constexpr int kBlk = kChunkK / 128;          // 4 blocks of 128 per stage = register ring depth
+constexpr int kARow = kChunkK + 16;          // padded LDS row of activation codes (bank spread)
+constexpr int kSCol = 40;                    // padded LDS column of one chunk's weight scales
 constexpr int kNV = 0;
 constexpr int kMX = 1;
+
+struct Stage {
+  uint8_t a[kRows * kARow];                  // activation codes, [row][512 (+16 pad)]
+  float as[kBlk * kRows];                    // activation scales, [block][row]
+  uint8_t s[kTileN * kSCol];                 // weight scales, [column][chunk bytes (+pad)]
+};
 
 struct ExpertView {
   const uint8_t* w;
   const uint8_t* s;
   float scale2;
   int kind;
-  int rb, re;          // packed rows [rb, re)
+  int rb, re;                                // packed rows [rb, re)
 };
 
 // Activation row of packed row `prow`: row_ids[prow] (or prow), -2 when the entry is out of range.
@@ -57,76 +74,113 @@ __device__ __forceinline__ int act_row(const GemmArgs& p, int prow) {
   return (r >= 0 && r < p.a_rows) ? r : -2;
 }
 
-// Buffer descriptors of one pass (uniform per workgroup).
-struct PassRsrc {
+// Workgroup barrier that waits for this wavefront's LDS operations only (__syncthreads would also
+// wait for every outstanding global load and drain the weight ring).  The memory clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Per-thread staging registers of one chunk, and their global byte offsets for chunk 0.
+template <int KIND>
+struct StageRegs {
+  u32x4 a[4];                                 // activation codes: 4 x 16 bytes
+  u32x4 s[KIND == kNV ? 2 : 1];               // weight scales: 16 bytes per column half (NV) / column (MX)
+  float as;                                   // one activation scale (threads < 128)
+};
+
+template <int KIND>
+struct StageOffsets {
+  uint32_t a[4];                              // row * k + 16 * part, or kOffNone
+  uint32_t s[KIND == kNV ? 2 : 1];            // column * k/gs + 16 * half, or kOffNone
+  uint32_t as;                                // (row * nblk + blk) * 4, or kOffNone
+};
+
+struct Rsrc {
   rsrc_t w, s, a, as;
 };
 
-template <int MT>
-struct BlockData {
-  u32x4 wq[kCT];          // 32 nibbles of each column tile
-  uint32_t sc[kCT];       // NVFP4: 2 E4M3 scale bytes; MXFP4: 1 E8M0 byte
-  u32x4 aq[MT][2];        // 32 activation bytes per row tile
-  float asa[MT];          // activation scale of this lane's operand row (row l%16) for the block
-};
-
-// Per-lane byte offsets of block 0; block b adds b times the per-block strides.
-template <int MT>
-struct PassOffsets {
-  uint32_t w[kCT], s[kCT], a[MT], as[MT];
-};
-
-// Loads of block b.  Every load is issued even when b is past the last block: its offset is then
-// out of range and the load returns zeros without touching memory, so the number of outstanding
-// loads is the same on every path and the compiler's wait counts stay exact.
-template <int MT, int KIND>
-__device__ __forceinline__ void load_block(const PassRsrc& r, const PassOffsets<MT>& o, int b,
-                                           bool valid, BlockData<MT>& d) {
-  const uint32_t ub = (uint32_t)b;
+template <int KIND>
+__device__ __forceinline__ void stage_load(const Rsrc& r, const StageOffsets<KIND>& o, int c, bool valid,
+                                           StageRegs<KIND>& d) {
+  const uint32_t uc = (uint32_t)c;
 #pragma unroll
-  for (int ct = 0; ct < kCT; ++ct) {
-    d.wq[ct] = buf_load_x4(r.w, valid ? o.w[ct] + ub * 64u : kOffNone);
-    d.sc[ct] = (KIND == kNV) ? buf_load_u16(r.s, valid ? o.s[ct] + ub * 8u : kOffNone)
-                             : buf_load_u8(r.s, valid ? o.s[ct] + ub * 4u : kOffNone);
+  for (int j = 0; j < 4; ++j) d.a[j] = buf_load_x4(r.a, valid ? o.a[j] + uc * kChunkK : kOffNone);
+#pragma unroll
+  for (int h = 0; h < (KIND == kNV ? 2 : 1); ++h)
+    d.s[h] = buf_load_x4(r.s, valid ? o.s[h] + uc * (KIND == kNV ? 32u : 16u) : kOffNone);
+  d.as = u2f(buf_load_u32(r.as, valid ? o.as + uc * (uint32_t)(kBlk * 4) : kOffNone));
+}
+
+// Store one chunk's staged data into an LDS stage.
+template <int KIND>
+__device__ __forceinline__ void stage_store(Stage& st, const StageRegs<KIND>& d) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q = tid + kThreads * j, row = q >> 5, part = q & 31;
+    *reinterpret_cast<u32x4*>(st.a + row * kARow + part * 16) = d.a[j];
   }
+  if (tid < kRows * kBlk) st.as[(tid & 3) * kRows + (tid >> 2)] = d.as;
+  if constexpr (KIND == kNV) {
+    // The thread holds 16 bytes of one column = blocks {2h, 2h+1} x 4 ushort scale pairs (lane
+    // groups g = 0..3).  For each g, the two pairs become one dword at [col][8g + 4h], so the
+    // reader lane (column, g) finds the pairs of blocks 0..3 in 8 contiguous bytes.
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const uint32_t ab = valid ? o.a[mt] + ub * 128u : kOffNone;
-    d.aq[mt][0] = buf_load_x4(r.a, ab);
-    d.aq[mt][1] = buf_load_x4(r.a, ab + (KIND == kNV ? 16u : 64u));
-    d.asa[mt] = u2f(buf_load_u32(r.as, valid ? o.as[mt] + ub * 4u : kOffNone));
+    for (int hh = 0; hh < 2; ++hh) {
+      const int q = tid + kThreads * hh, col = q >> 1, h = q & 1;
+      const u32x4 v = d.s[hh];
+      uint32_t* base = reinterpret_cast<uint32_t*>(st.s + col * kSCol + 4 * h);
+      base[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);   // g0: lo16(v0) | lo16(v2) << 16
+      base[2] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);   // g1: hi16(v0) | hi16(v2) << 16
+      base[4] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);   // g2
+      base[6] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);   // g3
+    }
+  } else {
+    // MXFP4: 16 bytes = blocks 0..3 x 4 lane groups, stored as is at [col][0..15].
+    uint64_t* base = reinterpret_cast<uint64_t*>(st.s + tid * kSCol);
+    base[0] = ((uint64_t)d.s[0][1] << 32) | d.s[0][0];
+    base[1] = ((uint64_t)d.s[0][3] << 32) | d.s[0][2];
   }
 }
 
 template <int MT>
-__device__ __forceinline__ void compute_block_nv(const BlockData<MT>& d, f32x4 (&acc)[MT][kCT]) {
-  const int g = (threadIdx.x & 63) >> 4;
+__device__ __forceinline__ void compute_block_nv(const Stage& st, int bq, const u32x4 (&wq)[kCT],
+                                                 const uint32_t (&sc)[kCT], f32x4 (&acc)[MT][kCT]) {
+  const int lane = threadIdx.x & 63, c16 = lane & 15, g = lane >> 4;
   f32x4 part[MT][kCT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct) part[mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 aq[MT][2];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const uint8_t* ap = st.a + (16 * mt + c16) * kARow + bq * 128 + 32 * g;
+    aq[mt][0] = *reinterpret_cast<const u32x4*>(ap);
+    aq[mt][1] = *reinterpret_cast<const u32x4*>(ap + 16);
+  }
+  h16x2 ws[kCT];
+#pragma unroll
+  for (int ct = 0; ct < kCT; ++ct) ws[ct] = e4m3x2_to_f16<false>(sc[ct]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     h16x8 af[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-      af[mt] = e4m3x8_to_f16(d.aq[mt][i >> 1][2 * (i & 1)], d.aq[mt][i >> 1][2 * (i & 1) + 1]);
+      af[mt] = e4m3x8_to_f16(aq[mt][i >> 1][2 * (i & 1)], aq[mt][i >> 1][2 * (i & 1) + 1]);
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct) {
-      const h16x2 ws = e4m3x2_to_f16<false>(d.sc[ct]);
-      const h16x8 bf = e2m1x8_scaled_f16(d.wq[ct][i], ws[i >> 1]);
+      const h16x8 bf = e2m1x8_scaled_f16(wq[ct][i], ws[ct][i >> 1]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) part[mt][ct] = mfma16x16x32_f16(af[mt], bf, part[mt][ct]);
     }
   }
-  // The partial tile covers exactly one 128-wide activation-scale group: scale its rows.  Result
-  // row 4g+v of the tile is operand row 4g+v, whose scale sits in lane 4g+v.
+  // The partial tile covers exactly one 128-wide activation-scale group: result row 4g+v of row
+  // tile mt is scaled by as[16mt + 4g + v, block].
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    float as[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) as[v] = __shfl(d.asa[mt], 4 * g + v, 64);
+    const f32x4 as = *reinterpret_cast<const f32x4*>(st.as + bq * kRows + 16 * mt + 4 * g);
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct)
 #pragma unroll
@@ -135,55 +189,71 @@ __device__ __forceinline__ void compute_block_nv(const BlockData<MT>& d, f32x4 (
 }
 
 template <int MT>
-__device__ __forceinline__ void compute_block_mx(const BlockData<MT>& d, f32x4 (&acc)[MT][kCT]) {
+__device__ __forceinline__ void compute_block_mx(const Stage& st, int bq, int wave, const u32x4 (&wq)[kCT],
+                                                 f32x4 (&acc)[MT][kCT]) {
+  const int lane = threadIdx.x & 63, c16 = lane & 15, g = lane >> 4;
+  int sb[kCT];
+#pragma unroll
+  for (int ct = 0; ct < kCT; ++ct) sb[ct] = st.s[(wave * kWaveCols + 16 * ct + c16) * kSCol + 4 * bq + g];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const i32x8 a = {(int)d.aq[mt][0][0], (int)d.aq[mt][0][1], (int)d.aq[mt][0][2], (int)d.aq[mt][0][3],
-                     (int)d.aq[mt][1][0], (int)d.aq[mt][1][1], (int)d.aq[mt][1][2], (int)d.aq[mt][1][3]};
-    const int sa = (int)((f2u(d.asa[mt]) >> 23) & 0xFFu);   // power-of-two scale -> E8M0
+    const uint8_t* ap = st.a + (16 * mt + c16) * kARow + bq * 128 + 16 * g;
+    const u32x4 a0 = *reinterpret_cast<const u32x4*>(ap);
+    const u32x4 a1 = *reinterpret_cast<const u32x4*>(ap + 64);
+    const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    const int sa = (int)((f2u(st.as[bq * kRows + 16 * mt + c16]) >> 23) & 0xFFu);   // 2^e -> E8M0
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct) {
-      const i32x8 bw = {(int)d.wq[ct][0], (int)d.wq[ct][1], (int)d.wq[ct][2], (int)d.wq[ct][3], 0, 0, 0, 0};
-      acc[mt][ct] = mfma16x16x128_f8f4(a, bw, acc[mt][ct], sa, (int)d.sc[ct]);
+      const i32x8 bw = {(int)wq[ct][0], (int)wq[ct][1], (int)wq[ct][2], (int)wq[ct][3], 0, 0, 0, 0};
+      acc[mt][ct] = mfma16x16x128_f8f4(a, bw, acc[mt][ct], sa, sb[ct]);
     }
   }
 }
 
+// One pass over the packed rows [m0, mend) (at most 32) for the 256 columns starting at n0.
 template <int MT, int KIND>
-__device__ __forceinline__ void compute_block(const BlockData<MT>& d, f32x4 (&acc)[MT][kCT]) {
-  if constexpr (KIND == kNV) compute_block_nv<MT>(d, acc);
-  else compute_block_mx<MT>(d, acc);
-}
-
-// One pass over the packed rows [m0, mend) (at most 32) for the 64 columns starting at n0.
-template <int MT, int KIND>
-__device__ void run_pass(const GemmArgs& p, const ExpertView& ex, int n0, int m0, int mend,
-                         f32x4 (*red)[2][kCT][64]) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
-  const int c16 = lane & 15, g = lane >> 4;
+__device__ void run_pass(const GemmArgs& p, const ExpertView& ex, int n0, int m0, int mend, Stage (&st)[2]) {
+  const int tid = threadIdx.x, lane = tid & 63, c16 = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int k = p.k, nblk = k >> 7;
+  const int nch = (nblk + kBlk - 1) / kBlk;
   constexpr int GS = (KIND == kNV) ? 16 : 32;
 
-  PassRsrc r;
+  Rsrc r;
   r.w = make_rsrc(ex.w, (uint32_t)p.n * (uint32_t)(k / 2));
   r.s = make_rsrc(ex.s, (uint32_t)p.n * (uint32_t)(k / GS));
   r.a = make_rsrc(p.a_codes, (uint32_t)p.a_rows * (uint32_t)k);
   r.as = make_rsrc(p.a_scales, (uint32_t)p.a_rows * (uint32_t)nblk * 4u);
-  PassOffsets<MT> o;
+
+  // Staging offsets for chunk 0.  Rows beyond the pass, and rows whose row_ids entry is invalid,
+  // load zeros.  A partial last chunk reads zeros past k (the descriptors end at the planes' ends,
+  // and every row's data beyond k belongs to the next row, so those lanes are also masked below by
+  // the block check: blocks >= nblk are never computed).
+  StageOffsets<KIND> so;
 #pragma unroll
-  for (int ct = 0; ct < kCT; ++ct) {
-    const int col = n0 + 16 * ct + c16;
-    const bool ok = col < p.n;
-    o.w[ct] = ok ? (uint32_t)col * (uint32_t)(k / 2) + 16u * g : kOffNone;
-    o.s[ct] = ok ? (uint32_t)col * (uint32_t)(k / GS) + (KIND == kNV ? 2u * g : (uint32_t)g) : kOffNone;
+  for (int j = 0; j < 4; ++j) {
+    const int q = tid + kThreads * j, row = q >> 5, part = q & 31;
+    const int prow = m0 + row;
+    const int ar = (row < MT * 16 && prow < mend) ? act_row(p, prow) : -1;
+    so.a[j] = ar >= 0 ? (uint32_t)ar * (uint32_t)k + 16u * part : kOffNone;
+  }
+  {
+    const int row = tid >> 2, blk = tid & 3, prow = m0 + row;
+    const int ar = (tid < kRows * kBlk && row < MT * 16 && prow < mend) ? act_row(p, prow) : -1;
+    so.as = ar >= 0 ? ((uint32_t)ar * (uint32_t)nblk + blk) * 4u : kOffNone;
   }
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int prow = m0 + 16 * mt + c16;
-    const int ar = prow < mend ? act_row(p, prow) : -1;
-    o.a[mt] = ar >= 0 ? (uint32_t)ar * (uint32_t)k + (KIND == kNV ? 32u * g : 16u * g) : kOffNone;
-    o.as[mt] = ar >= 0 ? (uint32_t)ar * (uint32_t)nblk * 4u : kOffNone;
+  for (int h = 0; h < (KIND == kNV ? 2 : 1); ++h) {
+    const int q = tid + kThreads * h;
+    const int col = KIND == kNV ? (q >> 1) : q, half = KIND == kNV ? (q & 1) : 0;
+    so.s[h] = (n0 + col < p.n) ? (uint32_t)(n0 + col) * (uint32_t)(k / GS) + 16u * half : kOffNone;
+  }
+  // Weight stream offsets of this wavefront's 4 column tiles.
+  uint32_t wo[kCT];
+#pragma unroll
+  for (int ct = 0; ct < kCT; ++ct) {
+    const int col = n0 + wave * kWaveCols + 16 * ct + c16;
+    wo[ct] = col < p.n ? (uint32_t)col * (uint32_t)(k / 2) + 16u * g : kOffNone;
   }
 
   f32x4 acc[MT][kCT];
@@ -192,69 +262,90 @@ __device__ void run_pass(const GemmArgs& p, const ExpertView& ex, int n0, int m0
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct) acc[mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Blocks wave, wave+4, ... through a ring of D register buffers: the loads of the next D-1
-  // blocks are in flight while one block is computed (the stream is latency-bound otherwise).
-  constexpr int D = (MT == 1) ? 4 : 2;
-  BlockData<MT> buf[D];
+  // Prologue: chunk 0 staged into LDS stage 0, chunk 1 loaded into the staging registers, then the
+  // weight ring for the blocks of chunk 0 -- the same order of outstanding loads as at the top of
+  // every loop iteration (staged chunk first, then 4 blocks of weights), so that the compiler's
+  // wait counts, merged over the loop entry and the back edge, stay exact.  Every group of loads is
+  // pinned where it is written (sched_barrier): the machine scheduler would otherwise sink loads
+  // toward their first use.  All loads are issued on every path (out-of-range ones return zero
+  // without touching memory).
+  StageRegs<KIND> sr;
+  stage_load<KIND>(r, so, 0, true, sr);
+  __builtin_amdgcn_sched_barrier(0);
+  stage_store<KIND>(st[0], sr);
+  stage_load<KIND>(r, so, 1, 1 < nch, sr);
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 wq[kBlk][kCT];
 #pragma unroll
-  for (int j = 0; j < D; ++j) {
-    const int bj = wave + kWaves * j;
-    load_block<MT, KIND>(r, o, bj, bj < nblk, buf[j]);
-    // Pin every group of loads where it is written: the machine scheduler would otherwise sink
-    // loads toward their first use (the loop latch) or reorder the prologue, and the wait counts
-    // at the loop head would then drain the whole ring.
+  for (int j = 0; j < kBlk; ++j) {
+#pragma unroll
+    for (int ct = 0; ct < kCT; ++ct) wq[j][ct] = buf_load_x4(r.w, j < nblk ? wo[ct] + (uint32_t)j * 64u : kOffNone);
     __builtin_amdgcn_sched_barrier(0);
   }
-  for (int b0 = wave; b0 < nblk; b0 += kWaves * D) {
+
+  for (int c = 0; c < nch; ++c) {
+    lds_barrier();                           // stage c&1 complete; stage (c+1)&1 no longer read
+    stage_store<KIND>(st[(c + 1) & 1], sr);  // chunk c+1 (zeros past the end)
+    stage_load<KIND>(r, so, c + 2, c + 2 < nch, sr);
+    __builtin_amdgcn_sched_barrier(0);
+    const Stage& cur = st[c & 1];
+    uint2 scp[kCT];                          // NVFP4 scale pairs of blocks 0..3 of this chunk
+    if constexpr (KIND == kNV) {
 #pragma unroll
-    for (int j = 0; j < D; ++j) {
-      const int bb = b0 + kWaves * j;
-      if (bb < nblk) compute_block<MT, KIND>(buf[j], acc);
-      const int bn = bb + kWaves * D;
-      load_block<MT, KIND>(r, o, bn, bn < nblk, buf[j]);
+      for (int ct = 0; ct < kCT; ++ct)
+        scp[ct] = *reinterpret_cast<const uint2*>(cur.s + (wave * kWaveCols + 16 * ct + c16) * kSCol + 8 * g);
+    }
+#pragma unroll
+    for (int bq = 0; bq < kBlk; ++bq) {
+      const int b = c * kBlk + bq;
+      if (b < nblk) {
+        if constexpr (KIND == kNV) {
+          uint32_t sc[kCT];
+#pragma unroll
+          for (int ct = 0; ct < kCT; ++ct) sc[ct] = (bq < 2 ? scp[ct].x : scp[ct].y) >> (16 * (bq & 1));
+          compute_block_nv<MT>(cur, bq, wq[bq], sc, acc);
+        } else {
+          compute_block_mx<MT>(cur, bq, wave, wq[bq], acc);
+        }
+      }
+      const int bn = b + kBlk;
+#pragma unroll
+      for (int ct = 0; ct < kCT; ++ct)
+        wq[bq][ct] = buf_load_x4(r.w, bn < nblk ? wo[ct] + (uint32_t)bn * 64u : kOffNone);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // Fixed-order reduction of the 4 wavefronts' partial tiles.
+  // Store: the lane holds column (16ct + c16) and rows 4g+v of each row tile.
+  const float post = (KIND == kNV) ? ex.scale2 : 1.0f;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int ct = 0; ct < kCT; ++ct) red[wave][mt][ct][lane] = acc[mt][ct];
-  __syncthreads();
-  const float post = (KIND == kNV) ? ex.scale2 : 1.0f;
-  for (int t = wave; t < MT * kCT; t += kWaves) {
-    const int mt = t / kCT, ct = t % kCT;
-    f32x4 sum = red[0][mt][ct][lane];
-    sum += red[1][mt][ct][lane];
-    sum += red[2][mt][ct][lane];
-    sum += red[3][mt][ct][lane];
-    const int col = n0 + 16 * ct + c16;
-    if (col < p.n) {
+    for (int v = 0; v < 4; ++v) {
+      const int prow = m0 + 16 * mt + 4 * g + v;
+      if (prow < mend) {
+        const bool bad = act_row(p, prow) < 0;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int crow = m0 + 16 * mt + 4 * g + v;
-        if (crow < mend) {
-          const int ar = act_row(p, crow);
-          p.out[(size_t)crow * p.n + col] = ar >= 0 ? sum[v] * post : __builtin_nanf("");
+        for (int ct = 0; ct < kCT; ++ct) {
+          const int col = n0 + wave * kWaveCols + 16 * ct + c16;
+          if (col < p.n) p.out[(size_t)prow * p.n + col] = bad ? __builtin_nanf("") : acc[mt][ct][v] * post;
         }
       }
     }
-  }
-  __syncthreads();
 }
 
 template <int KIND>
-__device__ void run_expert(const GemmArgs& p, const ExpertView& ex, int n0, f32x4 (*red)[2][kCT][64]) {
-  for (int m0 = ex.rb; m0 < ex.re; m0 += kRowsPerPass) {
-    const int mend = min(m0 + kRowsPerPass, ex.re);
-    if (mend - m0 > 16) run_pass<2, KIND>(p, ex, n0, m0, mend, red);
-    else run_pass<1, KIND>(p, ex, n0, m0, mend, red);
+__device__ void run_expert(const GemmArgs& p, const ExpertView& ex, int n0, Stage (&st)[2]) {
+  for (int m0 = ex.rb; m0 < ex.re; m0 += kRows) {
+    const int mend = min(m0 + kRows, ex.re);
+    if (m0 > ex.rb) lds_barrier();           // the previous pass may still be reading the stages
+    if (mend - m0 > 16) run_pass<2, KIND>(p, ex, n0, m0, mend, st);
+    else run_pass<1, KIND>(p, ex, n0, m0, mend, st);
   }
 }
 
 __global__ __launch_bounds__(kThreads, 2) void gemm_decode_kernel(GemmArgs p, int ntn, int xcd_map) {
-  __shared__ f32x4 red[kWaves][2][kCT][64];
+  __shared__ Stage st[2];
   const int L = blockIdx.x;
   int e, nt;
   if (xcd_map) {
@@ -278,9 +369,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_decode_kernel(GemmArgs p, in
   if (ex.rb >= ex.re) return;
   const int n0 = nt * kTileN;
   if (ex.kind == kNV) {
-    run_expert<kNV>(p, ex, n0, red);
+    run_expert<kNV>(p, ex, n0, st);
   } else if (ex.kind == kMX) {
-    run_expert<kMX>(p, ex, n0, red);
+    run_expert<kMX>(p, ex, n0, st);
   } else {
     for (int i = threadIdx.x; i < (ex.re - ex.rb) * kTileN; i += kThreads) {
       const int r = ex.rb + i / kTileN, col = n0 + i % kTileN;
