@@ -122,6 +122,9 @@ def main():
     ap.add_argument("--workload", default="config3", choices=["config3", "config4"])
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 disables it)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="after timing, run 3 plain device copies of MIB MiB (a known-size kernel "
+                         "for scaling the HBM byte counters of a profiler run)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -221,6 +224,14 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if args.calibrate_copy > 0:
+        nbytes = args.calibrate_copy << 20
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)          # an elementwise kernel: reads and writes nbytes
+        torch.cuda.synchronize()
+        log(f"calibration: 3 copies of {nbytes} bytes (read {nbytes}, write {nbytes} each)")
     if args.cpu_budget > 0:
         if args.workload == "config3":
             log(f"cpu_baseline: timing the oracle for about {args.cpu_budget:.0f} s ...")

@@ -45,12 +45,22 @@ def lib() -> ctypes.CDLL:
         L.fp4moe_last_error.restype = ctypes.c_char_p
         L.fp4moe_version.argtypes = []
         L.fp4moe_version.restype = ctypes.c_char_p
+        L.fp4moe_set_gemm_schedule.argtypes = [I32]
+        L.fp4moe_set_gemm_schedule.restype = ctypes.c_int
         _lib = L
     return _lib
 
 
 def version() -> str:
     return lib().fp4moe_version().decode()
+
+
+SCHEDULE_AUTO, SCHEDULE_ROWSTREAM, SCHEDULE_TILED = 0, 1, 2
+
+
+def set_gemm_schedule(schedule: int) -> None:
+    """Force the GEMM kernel choice (0 automatic, 1 row-streaming, 2 tiled); a test hook."""
+    _check(lib().fp4moe_set_gemm_schedule(int(schedule)), "fp4moe_set_gemm_schedule")
 
 
 def _check(rc: int, what: str):

@@ -1,5 +1,6 @@
 // capi.hip -- the extern "C" entry points of libfp4moe (declared and documented in
 // include/fp4moe.h): host-side argument validation, kernel dispatch, per-thread error messages.
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 
@@ -47,6 +48,17 @@ int check_planes(int64_t a_rows, int32_t n, int32_t k, const char* what) {
   return FP4MOE_OK;
 }
 
+// GEMM schedule: row-streaming (decode) kernel for at most 32 rows per expert on average, tiled
+// (prefill) kernel otherwise.  Both compute the same definition; the choice only changes the
+// order of the f32 additions.  fp4moe_set_gemm_schedule forces one of them (test hook).
+std::atomic<int> g_schedule{FP4MOE_SCHEDULE_AUTO};
+
+hipError_t launch_gemm(const fp4moe::GemmArgs& a, int64_t rows, int64_t experts, hipStream_t stream) {
+  int s = g_schedule.load(std::memory_order_relaxed);
+  if (s == FP4MOE_SCHEDULE_AUTO) s = (rows <= 32 * experts) ? FP4MOE_SCHEDULE_ROWSTREAM : FP4MOE_SCHEDULE_TILED;
+  return s == FP4MOE_SCHEDULE_TILED ? fp4moe::launch_gemm_prefill(a, stream) : fp4moe::launch_gemm_decode(a, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -86,7 +98,7 @@ int fp4_expert_gemm(const uint8_t* a_codes, const float* a_scales, const uint8_t
   a.out = out;
   a.n = n;
   a.k = k;
-  return launched(fp4moe::launch_gemm_decode(a, stream), "fp4_expert_gemm");
+  return launched(launch_gemm(a, g, 1, stream), "fp4_expert_gemm");
 }
 
 int fp4_grouped_gemm(const uint8_t* a_codes, const float* a_scales, int32_t a_rows,
@@ -123,7 +135,14 @@ int fp4_grouped_gemm(const uint8_t* a_codes, const float* a_scales, int32_t a_ro
   a.out = out;
   a.n = n;
   a.k = k;
-  return launched(fp4moe::launch_gemm_decode(a, stream), "fp4_grouped_gemm");
+  return launched(launch_gemm(a, total_rows, num_experts, stream), "fp4_grouped_gemm");
+}
+
+int fp4moe_set_gemm_schedule(int32_t schedule) {
+  if (schedule < FP4MOE_SCHEDULE_AUTO || schedule > FP4MOE_SCHEDULE_TILED)
+    return fail(FP4MOE_EINVAL, "fp4moe_set_gemm_schedule: schedule = %d is not 0, 1 or 2", (int)schedule);
+  g_schedule.store(schedule, std::memory_order_relaxed);
+  return ok();
 }
 
 const char* fp4moe_last_error(void) { return g_err; }

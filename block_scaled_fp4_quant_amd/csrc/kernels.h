@@ -37,4 +37,7 @@ hipError_t launch_act_quant(const float* x, uint8_t* codes, float* scales, int64
 // pass of 32 rows.
 hipError_t launch_gemm_decode(const GemmArgs& a, hipStream_t stream);
 
+// Tiled matrix-core kernel for many rows per expert (prefill): 128 x 256 output tiles.
+hipError_t launch_gemm_prefill(const GemmArgs& a, hipStream_t stream);
+
 }  // namespace fp4moe

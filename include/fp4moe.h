@@ -105,6 +105,18 @@ FP4MOE_API int fp4_grouped_gemm(const uint8_t* a_codes, const float* a_scales, i
                      const int32_t* kinds, const float* scale2, float* out, int32_t n, int32_t k,
                      hipStream_t stream);
 
+/*
+ * fp4moe_set_gemm_schedule -- test and benchmark hook (not part of the method).  The GEMM calls
+ * pick a kernel from the host-known rows per expert: a row-streaming kernel (each expert's weights
+ * read once per pass of 32 rows; used when total rows <= 32 x experts) or a tiled matrix-core
+ * kernel (128 x 256 output tiles).  Both compute the same definition to the same accuracy bound;
+ * only the order of the f32 additions differs.  schedule: 0 = automatic (default), 1 = always
+ * row-streaming, 2 = always tiled.  Process-wide; affects calls made after it returns.
+ * Errors: EINVAL for any other value.
+ */
+enum { FP4MOE_SCHEDULE_AUTO = 0, FP4MOE_SCHEDULE_ROWSTREAM = 1, FP4MOE_SCHEDULE_TILED = 2 };
+FP4MOE_API int fp4moe_set_gemm_schedule(int32_t schedule);
+
 /* Message for the last nonzero return code of a call made by this thread ("" if none). */
 FP4MOE_API const char* fp4moe_last_error(void);
 

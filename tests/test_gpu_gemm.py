@@ -13,6 +13,14 @@ pytestmark = pytest.mark.gpu
 NV, MX = workloads.NVFP4, workloads.MXFP4
 
 
+@pytest.fixture(params=[fp4.SCHEDULE_ROWSTREAM, fp4.SCHEDULE_TILED], ids=["rowstream", "tiled"])
+def schedule(request):
+    """Run the test with each GEMM kernel forced (both must meet the same contract)."""
+    fp4.set_gemm_schedule(request.param)
+    yield request.param
+    fp4.set_gemm_schedule(fp4.SCHEDULE_AUTO)
+
+
 def run_single(wl, orc, check_codes=True):
     """act_quant + fp4_expert_gemm on the GPU; full oracle comparison."""
     x = dev(wl.x)
@@ -49,26 +57,27 @@ def test_config2(orc):
 
 
 SHAPES = [(1, 16, 128), (5, 200, 256), (16, 64, 640), (17, 72, 384), (31, 130, 512),
-          (32, 256, 1024), (33, 96, 256), (50, 64, 2048), (100, 48, 384)]
+          (32, 256, 1024), (33, 96, 256), (50, 64, 2048), (100, 48, 384), (129, 300, 256),
+          (300, 520, 640)]
 
 
 @pytest.mark.parametrize("kind", [NV, MX])
 @pytest.mark.parametrize("g,n,k", SHAPES)
-def test_random_shapes(orc, kind, g, n, k):
+def test_random_shapes(orc, schedule, kind, g, n, k):
     wl = workloads.single_random(1000 + g * 7 + n + k, g, n, k, kind, scale2=2.0 ** -5, x_scale=2.0)
     got, ref, absp = run_single(wl, orc)
     check_bound(got, ref, absp, k, f"g={g} n={n} k={k} kind={kind}")
 
 
-def test_non_pow2_scale2(orc):
+def test_non_pow2_scale2(orc, schedule):
     wl = workloads.single_random(77, 9, 80, 512, NV, scale2=0.37)
     got, ref, absp = run_single(wl, orc)
     check_bound(got, ref, absp, 512, "scale2=0.37")
 
 
 @pytest.mark.parametrize("kind", [NV, MX])
-@pytest.mark.parametrize("g,n,k", [(3, 48, 512), (16, 64, 7168), (29, 130, 2048)])
-def test_exact_arm_bit_identity(orc, kind, g, n, k):
+@pytest.mark.parametrize("g,n,k", [(3, 48, 512), (16, 64, 7168), (29, 130, 2048), (200, 260, 1024)])
+def test_exact_arm_bit_identity(orc, schedule, kind, g, n, k):
     a_codes, a_scales, ex = workloads.exact_arm(g + n, g, n, k, kind)
     out = fp4.fp4_expert_gemm(dev(a_codes), dev(a_scales), dev(ex.w), dev(ex.s), ex.scale2, kind)
     ref, _ = orc.expert_gemm(a_codes, a_scales, ex.w, ex.s, ex.scale2, kind)
@@ -77,7 +86,7 @@ def test_exact_arm_bit_identity(orc, kind, g, n, k):
         f"{int(np.sum(got != ref))} outputs differ; max diff {np.max(np.abs(got - ref))}"
 
 
-def test_determinism_and_row_invariance(orc):
+def test_determinism_and_row_invariance(orc, schedule):
     wl = workloads.single_random(5, 24, 256, 1024, NV)
     codes, scales = fp4.act_quant_fp8(dev(wl.x))
     w, s = dev(wl.expert.w), dev(wl.expert.s)
@@ -107,8 +116,8 @@ def grouped_check(gd: GroupedDevice, orc, out, rows=None):
 
 
 @pytest.mark.parametrize("seed,T,E,top,n,k", [(1, 40, 8, 2, 96, 512), (2, 64, 16, 4, 200, 384),
-                                              (3, 300, 12, 3, 64, 1024)])
-def test_grouped_small_mixed(orc, seed, T, E, top, n, k):
+                                              (3, 300, 12, 3, 64, 1024), (8, 700, 6, 2, 272, 384)])
+def test_grouped_small_mixed(orc, schedule, seed, T, E, top, n, k):
     kinds = [NV if e % 3 else MX for e in range(E)]
     wl = workloads.grouped_random(seed, T, E, top, n, k, kinds=kinds, empty_experts=(1, E - 2))
     gd = GroupedDevice(wl)
@@ -116,7 +125,7 @@ def test_grouped_small_mixed(orc, seed, T, E, top, n, k):
     grouped_check(gd, orc, out)
 
 
-def test_grouped_matches_single_expert_bits(orc):
+def test_grouped_matches_single_expert_bits(orc, schedule):
     wl = workloads.grouped_random(4, 96, 8, 3, 128, 512, kinds=[NV, MX] * 4)
     gd = GroupedDevice(wl)
     codes, scales, out = gd.step()
@@ -130,7 +139,7 @@ def test_grouped_matches_single_expert_bits(orc):
         assert torch.equal(o, out[lo:hi]), f"expert {e}"
 
 
-def test_grouped_without_row_ids(orc):
+def test_grouped_without_row_ids(orc, schedule):
     wl = workloads.grouped_random(5, 32, 4, 2, 64, 256, kinds=[NV, MX, NV, MX])
     gd = GroupedDevice(wl)
     codes, scales = fp4.act_quant_fp8(gd.x)
@@ -141,7 +150,7 @@ def test_grouped_without_row_ids(orc):
     assert torch.equal(out, ref_out)
 
 
-def test_grouped_invalid_entries_give_nan(orc):
+def test_grouped_invalid_entries_give_nan(orc, schedule):
     wl = workloads.grouped_random(6, 24, 4, 2, 64, 256)
     gd = GroupedDevice(wl)
     codes, scales, good = gd.step()
@@ -161,7 +170,7 @@ def test_grouped_invalid_entries_give_nan(orc):
             assert torch.equal(out[r], good[r]), r
 
 
-def test_grouped_offsets_are_clamped(orc):
+def test_grouped_offsets_are_clamped(orc, schedule):
     # offsets past total_rows are clamped: rows beyond R are never touched and every row is written
     wl = workloads.grouped_random(7, 16, 4, 2, 32, 128)
     gd = GroupedDevice(wl)
@@ -206,6 +215,24 @@ def test_config3_sampled(orc, config3_dev):
     rows, cols = _sample(gd.R, gd.n, 16384, 3)
     worst = grouped_check(gd, orc, out, (rows, cols))
     print(f"config3 worst err / (2^-24 sum|p|) over {rows.size} samples = {worst:.2f}")
+
+
+def test_schedules_agree_within_bound(orc):
+    """The two kernels on the same large-row grouped input: both within the bound of the oracle,
+    each bit-reproducible run to run."""
+    wl = workloads.grouped_random(9, 600, 8, 2, 512, 1024, kinds=[NV] * 7 + [MX], zipf=1.1, x_dist="t3")
+    gd = GroupedDevice(wl)
+    outs = []
+    for sch in (fp4.SCHEDULE_ROWSTREAM, fp4.SCHEDULE_TILED):
+        fp4.set_gemm_schedule(sch)
+        try:
+            _, _, o1 = gd.step()
+            _, _, o2 = gd.step()
+        finally:
+            fp4.set_gemm_schedule(fp4.SCHEDULE_AUTO)
+        assert torch.equal(o1, o2)
+        grouped_check(gd, orc, o1)
+        outs.append(o1)
 
 
 def test_config4_sampled(orc, config4_dev):
