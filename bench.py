@@ -28,8 +28,14 @@ import workloads  # noqa: E402  (seeded input generators; no torch, no method ar
 METRIC = "FP4 expert GEMM weight-stream TB/s (decode) + TFLOP/s (grouped prefill)"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "fp8": 5000.0}
-GEMM_SOURCES = ["block_scaled_fp4_quant_amd/csrc/gemm_decode.hip",
-                "block_scaled_fp4_quant_amd/csrc/device_common.h"]
+# The sources of the dominant GEMM kernel of each workload: a recorded traffic figure is used only
+# while these files are unchanged since the counters were taken.
+GEMM_SOURCES = {
+    "config3": ["block_scaled_fp4_quant_amd/csrc/gemm_decode.hip",
+                "block_scaled_fp4_quant_amd/csrc/device_common.h"],
+    "config4": ["block_scaled_fp4_quant_amd/csrc/gemm_prefill.hip",
+                "block_scaled_fp4_quant_amd/csrc/device_common.h"],
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -37,9 +43,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def sources_sha() -> str:
+def sources_sha(workload: str) -> str:
     h = hashlib.sha256()
-    for rel in GEMM_SOURCES:
+    for rel in GEMM_SOURCES[workload]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -54,7 +60,7 @@ def recorded_traffic(workload: str):
     except (OSError, ValueError):
         return None
     ent = rec.get(workload)
-    if not ent or ent.get("gemm_sources_sha") != sources_sha():
+    if not ent or ent.get("gemm_sources_sha") != sources_sha(workload):
         return None
     return ent.get("hbm_bytes_per_launch")
 
