@@ -6,7 +6,7 @@
 // grouped GEMM section).  Here the work is a dense contraction, so the kernel is built around the
 // matrix cores.
 //
-// Arithmetic (bf16 MFMA 16x16x32, every operand exact):
+// Arithmetic (bf16 MFMA 32x32x16, every operand exact):
 //   A: E4M3 activation byte times its power-of-two row scale as[r, block], converted once per
 //      workgroup into LDS with the hardware scaled conversion (the scale only moves the exponent,
 //      so the bf16 value is exact).  Folding `as` into A removes any per-block partial sums.
@@ -15,19 +15,26 @@
 //      scale applied by the hardware conversion (a pure exponent: exact).  scale2 multiplies the
 //      final f32 sum (exact for power-of-two scale2, otherwise within one f32 rounding of the
 //      per-group weight scale).  Products of these bf16 values are exact in f32.
+//   On gfx950 the 32x32x16 and 16x16x32 bf16 MFMAs issue at the same rate (about 32 cycles), so
+//   the 32x32 shape does twice the work per instruction.
 //
 // Tiling.  A workgroup of 4 wavefronts computes a 128-row x 256-column output tile of one expert:
-// each wavefront owns 64 columns (4 MFMA column tiles) of all 128 rows (8 row tiles), 128 f32
-// accumulators per lane.  Per 128-wide k block, each wavefront streams and dequantizes its own
-// weights in registers (one 16-byte load per column tile per lane, a 2-block ring), while the bf16
-// activation tile and the block's weight scales sit in a two-stage LDS ring shared by the 4
-// wavefronts.  128-row tiles keep the padding of the skewed per-expert row counts small.
+// each wavefront owns 64 columns (2 MFMA column tiles of 32) of all 128 rows (4 row tiles), 128 f32
+// accumulators per lane.  Per 128-wide k block (8 steps of 16), each wavefront streams and
+// dequantizes its own weights in registers (a 2-block ring of 32 nibble bytes + scale bytes per
+// column tile per lane), while the bf16 activation tile sits in a two-stage LDS ring shared by the
+// 4 wavefronts.  Inside a block the steps are software-pipelined: the MFMAs of step s run while
+// the LDS reads and weight dequantization of step s+1 are issued, and the conversion of the next
+// block's activations into the other LDS stage is spread over the first four steps.  One barrier
+// per block.  Two workgroups share a compute unit (256 registers per lane, 139 KB of LDS), so each
+// SIMD interleaves two independent wavefronts.  128-row tiles keep the padding of the skewed
+// per-expert row counts small.
 //
 // Work list.  Tiles are (expert, 128-row slice, 256-column slice).  Each workgroup finds its tile by
 // a prefix scan of ceil(rows_e / 128) over the device-side offsets (no workspace, no host read of
 // the offsets); the grid is sized for the bound ceil(R / 128) + E row slices and surplus workgroups
-// exit.  Consecutive workgroups share the row slice (activation reuse in L2); a column slice stays
-// on one XCD across row slices (weight reuse in L2).
+// exit.  Consecutive workgroups share the row slice (activation reuse in L2); with a multiple of 8
+// column slices, a column slice stays on one XCD across row slices (weight reuse in that L2).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -37,21 +44,23 @@ namespace {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kBM = 128;                     // rows per tile
-constexpr int kMT = kBM / 16;                // 8 MFMA row tiles per wavefront
-constexpr int kNT = 4;                       // 4 MFMA column tiles per wavefront
-constexpr int kWaveCols = 16 * kNT;          // 64
+constexpr int kMT = kBM / 32;                // 4 MFMA row tiles (32 rows) per wavefront
+constexpr int kNT = 2;                       // 2 MFMA column tiles (32 columns) per wavefront
+constexpr int kWaveCols = 32 * kNT;          // 64
 constexpr int kBN = kWaves * kWaveCols;      // 256 columns per tile
+constexpr int kSteps = 8;                    // 16-wide k steps per 128-wide block
 constexpr int kARow = 128 * 2 + 16;          // bf16 activation row of one block, padded (272 B)
+constexpr int kDepth = 2;                    // register sets in the activation and weight load rings
 constexpr int kNV = 0;
 constexpr int kMX = 1;
 
 struct Stage {
   uint8_t a[kBM * kARow];                    // bf16 activations (as folded), [row][128 k]
-  uint8_t s[kBN * 8];                        // weight-scale bytes of the block, [column][8 | 4]
 };
 
 struct ExpertView {
@@ -71,125 +80,180 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__device__ __forceinline__ f32x4 mfma16x16x32_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+// 32x32x16 bf16 MFMA.  Lane l holds A row l%32 (B column l%32) for k = 8*(l/32) .. +8; the f32
+// result holds column l%32, rows 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.
+__device__ __forceinline__ f32x16 mfma32x32x16_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Per-thread staging of one block: 64 activation bytes of one row (half of the block), that row's
-// activation scale, and the weight-scale bytes of one column.
+// The k order inside a 128-wide block.  Both operands use the same order, so the sum is the same
+// set of products: lane half h = l/32 covers k = 64h .. 64h+63, and step s takes k = 64h + 8s .. +8.
+// For the weights that is nibble bytes 32h + 4s .. +4 of the column's 64-byte block, i.e. dword s%4
+// of the 16-byte chunk s/4 of the lane's 32 bytes; its NVFP4 group is 4h + s/2 (byte s/2 of the
+// lane's 4 scale bytes), its MXFP4 group 2h + s/4 (byte s/4 of the lane's 2 scale bytes).
+
+// Per-thread staging of one block: 64 activation bytes of one row (half of the block) and that
+// row's activation scale.
 struct StageRegs {
   u32x4 a[4];
   float as;
-  uint32_t s0, s1;
+};
+
+// Weights of one block for one lane: 32 nibble bytes per column tile and its scale bytes.
+struct WRegs {
+  u32x4 w[kNT][2];
+  uint32_t s[kNT];
 };
 
 struct Rsrc {
   rsrc_t w, s, a, as;
 };
 
-struct StageOffsets {
-  uint32_t a, as, s;                         // block-0 offsets (or kOffNone)
-};
-
-template <int KIND>
-__device__ __forceinline__ void stage_load(const Rsrc& r, const StageOffsets& o, int b, bool valid,
-                                           int nblk, StageRegs& d) {
-  const uint32_t ub = (uint32_t)b;
-  const uint32_t a = valid ? o.a + ub * 128u : kOffNone;
+__device__ __forceinline__ void stage_load(const Rsrc& r, uint32_t a_off, uint32_t as_off, int b, int nblk,
+                                           StageRegs& d) {
+  const bool valid = b < nblk;
+  const uint32_t a = valid ? a_off + (uint32_t)b * 128u : kOffNone;
 #pragma unroll
   for (int j = 0; j < 4; ++j) d.a[j] = buf_load_x4(r.a, a + 16u * j);
-  d.as = u2f(buf_load_u32(r.as, valid ? o.as + ub * 4u : kOffNone));
-  if constexpr (KIND == kNV) {
-    const uint32_t so = valid ? o.s + ub * 8u : kOffNone;
-    d.s0 = buf_load_u32(r.s, so);
-    d.s1 = buf_load_u32(r.s, so + 4u);
-  } else {
-    d.s0 = buf_load_u32(r.s, valid ? o.s + ub * 4u : kOffNone);
-    d.s1 = 0u;
-  }
-  (void)nblk;
+  d.as = u2f(buf_load_u32(r.as, valid ? as_off + (uint32_t)b * 4u : kOffNone));
 }
 
-// Convert the staged activation bytes (with their power-of-two scale folded in) to bf16 and store
-// them, with the weight-scale bytes, into an LDS stage.
 template <int KIND>
-__device__ __forceinline__ void stage_store(Stage& st, const StageRegs& d) {
-  const int tid = threadIdx.x, row = tid >> 1, half = tid & 1;
-  u32x4 out[8];
+__device__ __forceinline__ void w_load(const Rsrc& r, const uint32_t (&wo)[kNT], const uint32_t (&so)[kNT],
+                                       int b, int nblk, WRegs& d) {
+  const bool valid = b < nblk;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int nt = 0; nt < kNT; ++nt) {
+    const uint32_t o = valid ? wo[nt] + (uint32_t)b * 64u : kOffNone;
+    d.w[nt][0] = buf_load_x4(r.w, o);
+    d.w[nt][1] = buf_load_x4(r.w, o + 16u);
+  }
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d.a[j][w], d.as, false);
-      const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d.a[j][w], d.as, true);
-      out[2 * j + (w >> 1)][2 * (w & 1)] = __builtin_bit_cast(uint32_t, lo);
-      out[2 * j + (w >> 1)][2 * (w & 1) + 1] = __builtin_bit_cast(uint32_t, hi);
+  for (int nt = 0; nt < kNT; ++nt) {
+    if constexpr (KIND == kNV) {
+      d.s[nt] = buf_load_u32(r.s, valid ? so[nt] + (uint32_t)b * 8u : kOffNone);
+    } else {
+      d.s[nt] = buf_load_u16(r.s, valid ? so[nt] + (uint32_t)b * 4u : kOffNone);
     }
   }
-  u32x4* dst = reinterpret_cast<u32x4*>(st.a + row * kARow + half * 128);
-#pragma unroll
-  for (int q = 0; q < 8; ++q) dst[q] = out[q];
-  uint32_t* sd = reinterpret_cast<uint32_t*>(st.s + tid * 8);
-  sd[0] = d.s0;
-  if constexpr (KIND == kNV) sd[1] = d.s1;
 }
 
-// Eight nibbles (k = 8 consecutive) of one column, dequantized to bf16.
-template <int KIND>
-__device__ __forceinline__ bf16x8 dequant8(uint32_t w, float sv) {
+// Quarter q (16 activation bytes) of the staged row half: converted to bf16 with the power-of-two
+// row scale folded in (exact: the scale only moves the exponent) and written to the LDS stage.
+__device__ __forceinline__ void stage_store_q(Stage& st, const StageRegs& d, int q) {
+  const int tid = threadIdx.x, row = tid & (kBM - 1), half = tid >> 7;
+  u32x4 lo, hi;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d.a[q][w], d.as, false);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d.a[q][w], d.as, true);
+    if (w < 2) {
+      lo[2 * w] = __builtin_bit_cast(uint32_t, p0);
+      lo[2 * w + 1] = __builtin_bit_cast(uint32_t, p1);
+    } else {
+      hi[2 * (w - 2)] = __builtin_bit_cast(uint32_t, p0);
+      hi[2 * (w - 2) + 1] = __builtin_bit_cast(uint32_t, p1);
+    }
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(st.a + row * kARow + half * 128 + q * 32);
+  dst[0] = lo;
+  dst[1] = hi;
+}
+
+// Eight nibbles (k = 8 of one column) of step s, dequantized to bf16.
+template <int KIND, int S>
+__device__ __forceinline__ bf16x8 dequant_step(const WRegs& w, int nt) {
+  const uint32_t q = w.w[nt][S >> 2][S & 3];
   if constexpr (KIND == kNV) {
-    const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-    const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-    const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
-    const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
-    return bf16x8{(__bf16)(p0[0] * sv), (__bf16)(p0[1] * sv), (__bf16)(p1[0] * sv), (__bf16)(p1[1] * sv),
-                  (__bf16)(p2[0] * sv), (__bf16)(p2[1] * sv), (__bf16)(p3[0] * sv), (__bf16)(p3[1] * sv)};
+    // E2M1 -> f32 (exact), times the E4M3 group scale (<= 6 significant bits: exact), -> bf16 (exact)
+    const float sv = __builtin_amdgcn_cvt_f32_fp8((int)w.s[nt], S >> 1);
+    const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 0);
+    const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 1);
+    const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 2);
+    const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 3);
+    const bf16x2 b0 = {(__bf16)(p0[0] * sv), (__bf16)(p0[1] * sv)};
+    const bf16x2 b1 = {(__bf16)(p1[0] * sv), (__bf16)(p1[1] * sv)};
+    const bf16x2 b2 = {(__bf16)(p2[0] * sv), (__bf16)(p2[1] * sv)};
+    const bf16x2 b3 = {(__bf16)(p3[0] * sv), (__bf16)(p3[1] * sv)};
+    return bf16x8{b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
   } else {
-    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sv, 0);
-    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sv, 1);
-    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sv, 2);
-    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sv, 3);
+    // The E8M0 byte is the exponent field of the scale operand (the conversion applies only it).
+    const float sv = u2f(((w.s[nt] >> (8 * (S >> 2))) & 0xFFu) << 23);
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sv, 0);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sv, 1);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sv, 2);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sv, 3);
     return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
   }
 }
 
+__device__ __forceinline__ bf16x8 lds_a(const Stage& st, int mt, int s) {
+  const int lane = threadIdx.x & 63;
+  return *reinterpret_cast<const bf16x8*>(st.a + (32 * mt + (lane & 31)) * kARow + 128 * (lane >> 5) + 16 * s);
+}
+
+// Fragments of the step the MFMAs consume next.
+struct Frags {
+  bf16x8 a[kMT];
+  bf16x8 b[kNT];
+};
+
+// One 128-wide k block.  Step s issues its 8 MFMAs while the operands of step s+1 are prepared
+// (4 LDS reads, 2 weight dequantizations); steps 0-3 also convert and store the next block's
+// activation quarter, step 4 issues the loads of the block after, and before step 7 the workgroup
+// meets at the barrier that publishes the next stage.  Step 7 prepares step 0 of the next block.
 template <int KIND>
-__device__ __forceinline__ void compute_block(const Stage& st, int wave, const u32x4 (&wq)[kNT],
-                                              f32x4 (&acc)[kMT][kNT]) {
-  const int lane = threadIdx.x & 63, c16 = lane & 15, g = lane >> 4;
-  // Weight scales of this lane's two 16-groups (k = 32g .. 32g+31 of the block) per column tile.
-  float sv[kNT][2];
+__device__ __forceinline__ void run_block(const Stage& cur, Stage& nxt, const WRegs& w, const WRegs& wn,
+                                          StageRegs& store_src, StageRegs& load_dst, const Rsrc& r,
+                                          uint32_t a_off, uint32_t as_off, int b, int nblk, WRegs& wload,
+                                          const uint32_t (&wo)[kNT], const uint32_t (&so)[kNT], Frags& f,
+                                          f32x16 (&acc)[kMT][kNT]) {
 #pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) {
-    const int col = wave * kWaveCols + 16 * nt + c16;
-    if constexpr (KIND == kNV) {
-      const uint32_t pair = *reinterpret_cast<const uint16_t*>(st.s + col * 8 + 2 * g);
-      sv[nt][0] = __builtin_amdgcn_cvt_f32_fp8((int)pair, 0);
-      sv[nt][1] = __builtin_amdgcn_cvt_f32_fp8((int)pair, 1);
-    } else {
-      const uint32_t e8 = st.s[col * 8 + g];             // E8M0 byte of k = 32g .. +32
-      sv[nt][0] = u2f(e8 << 23);
-      sv[nt][1] = sv[nt][0];
+  for (int s = 0; s < kSteps; ++s) {
+    Frags g;
+    if (s == kSteps - 1) {
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();                         // next stage complete; this stage fully read
+      __builtin_amdgcn_sched_barrier(0);
     }
-  }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    bf16x8 bf[kNT];
+    for (int mt = 0; mt < kMT; ++mt) g.a[mt] = (s + 1 < kSteps) ? lds_a(cur, mt, s + 1) : lds_a(nxt, mt, 0);
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) bf[nt] = dequant8<KIND>(wq[nt][i], sv[nt][i >> 1]);
-#pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) {
-      const bf16x8 af = *reinterpret_cast<const bf16x8*>(st.a + (16 * mt + c16) * kARow + 64 * g + 16 * i);
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = mfma16x16x32_bf16(af, bf[nt], acc[mt][nt]);
+    for (int nt = 0; nt < kNT; ++nt) {
+      switch (s) {
+        case 0: g.b[nt] = dequant_step<KIND, 1>(w, nt); break;
+        case 1: g.b[nt] = dequant_step<KIND, 2>(w, nt); break;
+        case 2: g.b[nt] = dequant_step<KIND, 3>(w, nt); break;
+        case 3: g.b[nt] = dequant_step<KIND, 4>(w, nt); break;
+        case 4: g.b[nt] = dequant_step<KIND, 5>(w, nt); break;
+        case 5: g.b[nt] = dequant_step<KIND, 6>(w, nt); break;
+        case 6: g.b[nt] = dequant_step<KIND, 7>(w, nt); break;
+        default: g.b[nt] = dequant_step<KIND, 0>(wn, nt); break;
+      }
     }
+    if (s < 4) stage_store_q(nxt, store_src, s);
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = mfma32x32x16_bf16(f.a[mt], f.b[nt], acc[mt][nt]);
+    if (s == 4) {
+      __builtin_amdgcn_sched_barrier(0);
+      stage_load(r, a_off, as_off, b + 1 + kDepth, nblk, load_dst);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (s == kSteps - 1) {
+      __builtin_amdgcn_sched_barrier(0);
+      w_load<KIND>(r, wo, so, b + kDepth, nblk, wload);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    f = g;
   }
 }
 
 // One 128 x 256 output tile: packed rows [m0, m0 + mrows) of expert `ex`, columns [n0, n0 + 256).
 template <int KIND>
 __device__ void run_tile(const GemmArgs& p, const ExpertView& ex, int m0, int mrows, int n0, Stage (&st)[2]) {
-  const int tid = threadIdx.x, lane = tid & 63, c16 = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, c32 = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int k = p.k, nblk = k >> 7;
   constexpr int GS = (KIND == kNV) ? 16 : 32;
@@ -200,60 +264,67 @@ __device__ void run_tile(const GemmArgs& p, const ExpertView& ex, int m0, int mr
   r.a = make_rsrc(p.a_codes, (uint32_t)p.a_rows * (uint32_t)k);
   r.as = make_rsrc(p.a_scales, (uint32_t)p.a_rows * (uint32_t)nblk * 4u);
 
-  StageOffsets so;
+  uint32_t a_off, as_off;
   {
-    const int row = tid >> 1, half = tid & 1;
+    const int row = tid & (kBM - 1), half = tid >> 7;
     const int ar = row < mrows ? act_row(p, m0 + row) : -1;
-    so.a = ar >= 0 ? (uint32_t)ar * (uint32_t)k + 64u * half : kOffNone;
-    so.as = ar >= 0 ? (uint32_t)ar * (uint32_t)nblk * 4u : kOffNone;
-    const int col = n0 + tid;
-    so.s = col < p.n ? (uint32_t)col * (uint32_t)(k / GS) : kOffNone;
+    a_off = ar >= 0 ? (uint32_t)ar * (uint32_t)k + 64u * half : kOffNone;
+    as_off = ar >= 0 ? (uint32_t)ar * (uint32_t)nblk * 4u : kOffNone;
   }
-  uint32_t wo[kNT];
+  uint32_t wo[kNT], so[kNT];
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) {
-    const int col = n0 + wave * kWaveCols + 16 * nt + c16;
-    wo[nt] = col < p.n ? (uint32_t)col * (uint32_t)(k / 2) + 16u * g : kOffNone;
+    const int col = n0 + wave * kWaveCols + 32 * nt + c32;
+    wo[nt] = col < p.n ? (uint32_t)col * (uint32_t)(k / 2) + 32u * h : kOffNone;
+    so[nt] = col < p.n ? (uint32_t)col * (uint32_t)(k / GS) + (KIND == kNV ? 4u : 2u) * h : kOffNone;
   }
 
-  f32x4 acc[kMT][kNT];
+  f32x16 acc[kMT][kNT];
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mt][nt][v] = 0.f;
 
-  // Prologue in the steady-state load order (weights of block b, staging of block b+1, weights of
-  // block b+1), each group pinned in place (see the decode kernel for why).
-  StageRegs sr;
-  stage_load<KIND>(r, so, 0, true, nblk, sr);
-  __builtin_amdgcn_sched_barrier(0);
-  stage_store<KIND>(st[0], sr);
-  u32x4 wq[2][kNT];
-#pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) wq[0][nt] = buf_load_x4(r.w, wo[nt]);
-  __builtin_amdgcn_sched_barrier(0);
-  stage_load<KIND>(r, so, 1, 1 < nblk, nblk, sr);
+  // Prologue, in the steady-state load order (block b loads the activations of block b+1+kDepth,
+  // then the weights of block b+kDepth).  Loads past the last block return zeros.
+  StageRegs sr[kDepth];
+  WRegs wr[kDepth];
+  stage_load(r, a_off, as_off, 0, nblk, sr[0]);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) wq[1][nt] = buf_load_x4(r.w, 1 < nblk ? wo[nt] + 64u : kOffNone);
+  for (int j = 0; j + 1 < kDepth; ++j) {
+    stage_load(r, a_off, as_off, j + 1, nblk, sr[j + 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    w_load<KIND>(r, wo, so, j, nblk, wr[j]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) stage_store_q(st[0], sr[0], q);
   __builtin_amdgcn_sched_barrier(0);
+  stage_load(r, a_off, as_off, kDepth, nblk, sr[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  w_load<KIND>(r, wo, so, kDepth - 1, nblk, wr[kDepth - 1]);
+  __builtin_amdgcn_sched_barrier(0);
+  lds_barrier();
+  Frags f;
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt) f.a[mt] = lds_a(st[0], mt, 0);
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) f.b[nt] = dequant_step<KIND, 0>(wr[0], nt);
 
-  for (int b = 0; b < nblk; b += 2) {
+  // Block b reads LDS stage b&1 and weights wr[b%kDepth]; it stores block b+1 (staged in
+  // sr[(b+1)%kDepth]) into the other LDS stage, refills those staging registers with block
+  // b+1+kDepth and, at its end, refills wr[b%kDepth] with block b+kDepth.  A block count that is not
+  // a multiple of kDepth runs up to kDepth-1 all-zero blocks.
+  const int nblk_r = (nblk + kDepth - 1) / kDepth * kDepth;
+  for (int b = 0; b < nblk_r; b += kDepth) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int bb = b + j;
-      if (bb < nblk) {
-        lds_barrier();                       // stage bb&1 ready, stage (bb+1)&1 free
-        stage_store<KIND>(st[(bb + 1) & 1], sr);
-        stage_load<KIND>(r, so, bb + 2, bb + 2 < nblk, nblk, sr);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_block<KIND>(st[bb & 1], wave, wq[j], acc);
-        const int bn = bb + 2;
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt)
-          wq[j][nt] = buf_load_x4(r.w, bn < nblk ? wo[nt] + (uint32_t)bn * 64u : kOffNone);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int j = 0; j < kDepth; ++j) {
+      const int jn = (j + 1) % kDepth;
+      run_block<KIND>(st[j & 1], st[(j + 1) & 1], wr[j], wr[jn], sr[jn], sr[jn], r, a_off, as_off, b + j, nblk,
+                      wr[j], wo, so, f, acc);
     }
   }
 
@@ -261,21 +332,21 @@ __device__ void run_tile(const GemmArgs& p, const ExpertView& ex, int m0, int mr
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = 16 * mt + 4 * g + v;
+    for (int v = 0; v < 16; ++v) {
+      const int row = 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3);
       if (row < mrows) {
         const int prow = m0 + row;
         const bool bad = act_row(p, prow) < 0;
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
-          const int col = n0 + wave * kWaveCols + 16 * nt + c16;
+          const int col = n0 + wave * kWaveCols + 32 * nt + c32;
           if (col < p.n) p.out[(size_t)prow * p.n + col] = bad ? __builtin_nanf("") : acc[mt][nt][v] * post;
         }
       }
     }
 }
 
-__global__ __launch_bounds__(kThreads, 1) void gemm_prefill_kernel(GemmArgs p, int ntn) {
+__global__ __launch_bounds__(kThreads, 2) void gemm_prefill_kernel(GemmArgs p, int ntn) {
   __shared__ Stage st[2];
   __shared__ int s_tile[3];
   const int L = blockIdx.x;
