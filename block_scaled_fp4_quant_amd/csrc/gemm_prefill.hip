@@ -27,8 +27,10 @@
 // the LDS reads and weight dequantization of step s+1 are issued, and the conversion of the next
 // block's activations into the other LDS stage is spread over the first four steps.  One barrier
 // per block.  Two workgroups share a compute unit (256 registers per lane, 139 KB of LDS), so each
-// SIMD interleaves two independent wavefronts.  128-row tiles keep the padding of the skewed
-// per-expert row counts small.
+// SIMD interleaves two independent wavefronts.  An expert's last row slice computes only 64 rows
+// when it holds no more, which keeps the padding of the skewed per-expert row counts small.
+// Activations are staged with 8 lanes per row, so each 16-byte load instruction touches 8 cache
+// lines.
 //
 // Work list.  Tiles are (expert, 128-row slice, 256-column slice).  Each workgroup finds its tile by
 // a prefix scan of ceil(rows_e / 128) over the device-side offsets (no workspace, no host read of
@@ -55,7 +57,9 @@ constexpr int kWaveCols = 32 * kNT;          // 64
 constexpr int kBN = kWaves * kWaveCols;      // 256 columns per tile
 constexpr int kSteps = 8;                    // 16-wide k steps per 128-wide block
 constexpr int kARow = 128 * 2 + 16;          // bf16 activation row of one block, padded (272 B)
-constexpr int kDepth = 2;                    // register sets in the activation and weight load rings
+constexpr int kWDepth = 2;                   // register sets in the weight load ring
+constexpr int kADepth = 1;                   // register sets in the activation load ring
+constexpr int kUnroll = 2;                   // blocks per loop iteration (a multiple of both depths and of the 2 LDS stages)
 constexpr int kNV = 0;
 constexpr int kMX = 1;
 
@@ -92,11 +96,17 @@ __device__ __forceinline__ f32x16 mfma32x32x16_bf16(bf16x8 a, bf16x8 b, f32x16 c
 // of the 16-byte chunk s/4 of the lane's 32 bytes; its NVFP4 group is 4h + s/2 (byte s/2 of the
 // lane's 4 scale bytes), its MXFP4 group 2h + s/4 (byte s/4 of the lane's 2 scale bytes).
 
-// Per-thread staging of one block: 64 activation bytes of one row (half of the block) and that
-// row's activation scale.
+// Per-thread staging of one block.  Eight lanes cover one row's 128 block bytes (one cache line), so
+// a 16-byte load instruction touches 8 lines: thread t holds bytes 16*(t%8) .. +16 of rows
+// t/8 + 32*i (i = 0..3) and those rows' activation scales.
 struct StageRegs {
   u32x4 a[4];
-  float as;
+  float as[4];
+};
+
+// Per-thread block-0 offsets of the staged rows (kOffNone for rows past the tile or invalid).
+struct AOffs {
+  uint32_t a[4], as[4];
 };
 
 // Weights of one block for one lane: 32 nibble bytes per column tile and its scale bytes.
@@ -109,13 +119,12 @@ struct Rsrc {
   rsrc_t w, s, a, as;
 };
 
-__device__ __forceinline__ void stage_load(const Rsrc& r, uint32_t a_off, uint32_t as_off, int b, int nblk,
-                                           StageRegs& d) {
+__device__ __forceinline__ void stage_load(const Rsrc& r, const AOffs& o, int b, int nblk, StageRegs& d) {
   const bool valid = b < nblk;
-  const uint32_t a = valid ? a_off + (uint32_t)b * 128u : kOffNone;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) d.a[j] = buf_load_x4(r.a, a + 16u * j);
-  d.as = u2f(buf_load_u32(r.as, valid ? as_off + (uint32_t)b * 4u : kOffNone));
+  for (int i = 0; i < 4; ++i) d.a[i] = buf_load_x4(r.a, valid ? o.a[i] + (uint32_t)b * 128u : kOffNone);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d.as[i] = u2f(buf_load_u32(r.as, valid ? o.as[i] + (uint32_t)b * 4u : kOffNone));
 }
 
 template <int KIND>
@@ -138,15 +147,16 @@ __device__ __forceinline__ void w_load(const Rsrc& r, const uint32_t (&wo)[kNT],
   }
 }
 
-// Quarter q (16 activation bytes) of the staged row half: converted to bf16 with the power-of-two
-// row scale folded in (exact: the scale only moves the exponent) and written to the LDS stage.
-__device__ __forceinline__ void stage_store_q(Stage& st, const StageRegs& d, int q) {
-  const int tid = threadIdx.x, row = tid & (kBM - 1), half = tid >> 7;
+// Row i of the staged rows (16 activation bytes): converted to bf16 with the power-of-two row
+// scale folded in (exact: the scale only moves the exponent) and written to the LDS stage.  The two
+// 16-byte halves are written in an order that puts the 8 lanes of a row on distinct banks.
+__device__ __forceinline__ void stage_store_q(Stage& st, const StageRegs& d, int i) {
+  const int tid = threadIdx.x, c = tid & 7, row = (tid >> 3) + 32 * i;
   u32x4 lo, hi;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d.a[q][w], d.as, false);
-    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d.a[q][w], d.as, true);
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d.a[i][w], d.as[i], false);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d.a[i][w], d.as[i], true);
     if (w < 2) {
       lo[2 * w] = __builtin_bit_cast(uint32_t, p0);
       lo[2 * w + 1] = __builtin_bit_cast(uint32_t, p1);
@@ -155,9 +165,10 @@ __device__ __forceinline__ void stage_store_q(Stage& st, const StageRegs& d, int
       hi[2 * (w - 2) + 1] = __builtin_bit_cast(uint32_t, p1);
     }
   }
-  u32x4* dst = reinterpret_cast<u32x4*>(st.a + row * kARow + half * 128 + q * 32);
-  dst[0] = lo;
-  dst[1] = hi;
+  uint8_t* dst = st.a + row * kARow + 32 * c;
+  const bool swap = (c >> 2) & 1;
+  *reinterpret_cast<u32x4*>(dst + (swap ? 16 : 0)) = swap ? hi : lo;
+  *reinterpret_cast<u32x4*>(dst + (swap ? 0 : 16)) = swap ? lo : hi;
 }
 
 // Eight nibbles (k = 8 of one column) of step s, dequantized to bf16.
@@ -198,14 +209,14 @@ struct Frags {
   bf16x8 b[kNT];
 };
 
-// One 128-wide k block.  Step s issues its 8 MFMAs while the operands of step s+1 are prepared
-// (4 LDS reads, 2 weight dequantizations); steps 0-3 also convert and store the next block's
-// activation quarter, step 4 issues the loads of the block after, and before step 7 the workgroup
-// meets at the barrier that publishes the next stage.  Step 7 prepares step 0 of the next block.
-template <int KIND>
+// One 128-wide k block.  Step s issues its MFMAs while the operands of step s+1 are prepared
+// (LDS reads, 2 weight dequantizations); steps 0-3 also convert and store the next block's
+// activations, step 4 issues the loads of the block after, and before step 7 the workgroup meets
+// at the barrier that publishes the next stage.  Step 7 prepares step 0 of the next block.
+template <int KIND, int NMT>
 __device__ __forceinline__ void run_block(const Stage& cur, Stage& nxt, const WRegs& w, const WRegs& wn,
                                           StageRegs& store_src, StageRegs& load_dst, const Rsrc& r,
-                                          uint32_t a_off, uint32_t as_off, int b, int nblk, WRegs& wload,
+                                          const AOffs& ao, int b, int nblk, WRegs& wload,
                                           const uint32_t (&wo)[kNT], const uint32_t (&so)[kNT], Frags& f,
                                           f32x16 (&acc)[kMT][kNT]) {
 #pragma unroll
@@ -217,7 +228,7 @@ __device__ __forceinline__ void run_block(const Stage& cur, Stage& nxt, const WR
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) g.a[mt] = (s + 1 < kSteps) ? lds_a(cur, mt, s + 1) : lds_a(nxt, mt, 0);
+    for (int mt = 0; mt < NMT; ++mt) g.a[mt] = (s + 1 < kSteps) ? lds_a(cur, mt, s + 1) : lds_a(nxt, mt, 0);
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
       switch (s) {
@@ -233,26 +244,29 @@ __device__ __forceinline__ void run_block(const Stage& cur, Stage& nxt, const WR
     }
     if (s < 4) stage_store_q(nxt, store_src, s);
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt)
+    for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = mfma32x32x16_bf16(f.a[mt], f.b[nt], acc[mt][nt]);
     if (s == 4) {
       __builtin_amdgcn_sched_barrier(0);
-      stage_load(r, a_off, as_off, b + 1 + kDepth, nblk, load_dst);
+      stage_load(r, ao, b + 1 + kADepth, nblk, load_dst);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (s == kSteps - 1) {
       __builtin_amdgcn_sched_barrier(0);
-      w_load<KIND>(r, wo, so, b + kDepth, nblk, wload);
+      w_load<KIND>(r, wo, so, b + kWDepth, nblk, wload);
       __builtin_amdgcn_sched_barrier(0);
     }
-    f = g;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) f.a[mt] = g.a[mt];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) f.b[nt] = g.b[nt];
   }
 }
 
 // One 128 x 256 output tile: packed rows [m0, m0 + mrows) of expert `ex`, columns [n0, n0 + 256).
-template <int KIND>
-__device__ void run_tile(const GemmArgs& p, const ExpertView& ex, int m0, int mrows, int n0, Stage (&st)[2]) {
+template <int KIND, int NMT>
+__device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex, int m0, int mrows, int n0, Stage (&st)[2]) {
   const int tid = threadIdx.x, lane = tid & 63, c32 = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int k = p.k, nblk = k >> 7;
@@ -264,12 +278,13 @@ __device__ void run_tile(const GemmArgs& p, const ExpertView& ex, int m0, int mr
   r.a = make_rsrc(p.a_codes, (uint32_t)p.a_rows * (uint32_t)k);
   r.as = make_rsrc(p.a_scales, (uint32_t)p.a_rows * (uint32_t)nblk * 4u);
 
-  uint32_t a_off, as_off;
-  {
-    const int row = tid & (kBM - 1), half = tid >> 7;
+  AOffs ao;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (tid >> 3) + 32 * i;
     const int ar = row < mrows ? act_row(p, m0 + row) : -1;
-    a_off = ar >= 0 ? (uint32_t)ar * (uint32_t)k + 64u * half : kOffNone;
-    as_off = ar >= 0 ? (uint32_t)ar * (uint32_t)nblk * 4u : kOffNone;
+    ao.a[i] = ar >= 0 ? (uint32_t)ar * (uint32_t)k + 16u * (tid & 7) : kOffNone;
+    ao.as[i] = ar >= 0 ? (uint32_t)ar * (uint32_t)nblk * 4u : kOffNone;
   }
   uint32_t wo[kNT], so[kNT];
 #pragma unroll
@@ -287,50 +302,53 @@ __device__ void run_tile(const GemmArgs& p, const ExpertView& ex, int m0, int mr
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mt][nt][v] = 0.f;
 
-  // Prologue, in the steady-state load order (block b loads the activations of block b+1+kDepth,
-  // then the weights of block b+kDepth).  Loads past the last block return zeros.
-  StageRegs sr[kDepth];
-  WRegs wr[kDepth];
-  stage_load(r, a_off, as_off, 0, nblk, sr[0]);
+  // Prologue, in the steady-state load order (block b loads the activations of block b+1+kADepth,
+  // then the weights of block b+kWDepth).  Loads past the last block return zeros.
+  StageRegs sr[kADepth];
+  WRegs wr[kWDepth];
+  stage_load(r, ao, 0, nblk, sr[0]);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int j = 0; j + 1 < kDepth; ++j) {
-    stage_load(r, a_off, as_off, j + 1, nblk, sr[j + 1]);
+  for (int j = 1; j < kADepth; ++j) {
+    stage_load(r, ao, j, nblk, sr[j]);
     __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int j = 0; j + 1 < kWDepth; ++j) {
     w_load<KIND>(r, wo, so, j, nblk, wr[j]);
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) stage_store_q(st[0], sr[0], q);
   __builtin_amdgcn_sched_barrier(0);
-  stage_load(r, a_off, as_off, kDepth, nblk, sr[0]);
+  stage_load(r, ao, kADepth, nblk, sr[0]);
   __builtin_amdgcn_sched_barrier(0);
-  w_load<KIND>(r, wo, so, kDepth - 1, nblk, wr[kDepth - 1]);
+  w_load<KIND>(r, wo, so, kWDepth - 1, nblk, wr[kWDepth - 1]);
   __builtin_amdgcn_sched_barrier(0);
   lds_barrier();
   Frags f;
 #pragma unroll
-  for (int mt = 0; mt < kMT; ++mt) f.a[mt] = lds_a(st[0], mt, 0);
+  for (int mt = 0; mt < NMT; ++mt) f.a[mt] = lds_a(st[0], mt, 0);
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) f.b[nt] = dequant_step<KIND, 0>(wr[0], nt);
 
-  // Block b reads LDS stage b&1 and weights wr[b%kDepth]; it stores block b+1 (staged in
-  // sr[(b+1)%kDepth]) into the other LDS stage, refills those staging registers with block
-  // b+1+kDepth and, at its end, refills wr[b%kDepth] with block b+kDepth.  A block count that is not
-  // a multiple of kDepth runs up to kDepth-1 all-zero blocks.
-  const int nblk_r = (nblk + kDepth - 1) / kDepth * kDepth;
-  for (int b = 0; b < nblk_r; b += kDepth) {
+  // Block b reads LDS stage b&1 and weights wr[b%kWDepth]; it stores block b+1 (staged in
+  // sr[(b+1)%kADepth]) into the other LDS stage, refills those staging registers with block
+  // b+1+kADepth and, at its end, refills wr[b%kWDepth] with block b+kWDepth.  A block count that is
+  // not a multiple of kUnroll runs up to kUnroll-1 all-zero blocks.
+  const int nblk_r = (nblk + kUnroll - 1) / kUnroll * kUnroll;
+  for (int b = 0; b < nblk_r; b += kUnroll) {
 #pragma unroll
-    for (int j = 0; j < kDepth; ++j) {
-      const int jn = (j + 1) % kDepth;
-      run_block<KIND>(st[j & 1], st[(j + 1) & 1], wr[j], wr[jn], sr[jn], sr[jn], r, a_off, as_off, b + j, nblk,
-                      wr[j], wo, so, f, acc);
+    for (int j = 0; j < kUnroll; ++j) {
+      const int ja = (j + 1) % kADepth;
+      run_block<KIND, NMT>(st[j & 1], st[(j + 1) & 1], wr[j % kWDepth], wr[(j + 1) % kWDepth], sr[ja], sr[ja], r, ao,
+                      b + j, nblk, wr[j % kWDepth], wo, so, f, acc);
     }
   }
 
   const float post = (KIND == kNV) ? ex.scale2 : 1.0f;
 #pragma unroll
-  for (int mt = 0; mt < kMT; ++mt)
+  for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int row = 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3);
@@ -393,9 +411,11 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill_kernel(GemmArgs p, i
     if (lane == 0 && t >= base) s_tile[0] = -1;
   }
   __syncthreads();
-  const int e = s_tile[0];
+  // The tile is the same for the whole workgroup: keep it (and everything derived from it, such as
+  // the buffer descriptors) in scalar registers.
+  const int e = __builtin_amdgcn_readfirstlane(s_tile[0]);
   if (e < 0) return;
-  const int m0 = s_tile[1], mrows = s_tile[2];
+  const int m0 = __builtin_amdgcn_readfirstlane(s_tile[1]), mrows = __builtin_amdgcn_readfirstlane(s_tile[2]);
   ExpertView ex;
   if (p.offsets) {
     ex = ExpertView{reinterpret_cast<const uint8_t*>(p.w_ptrs[e]), reinterpret_cast<const uint8_t*>(p.s_ptrs[e]),
@@ -404,10 +424,17 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill_kernel(GemmArgs p, i
     ex = ExpertView{p.w, p.s, p.scale2, p.kind};
   }
   const int n0 = nt * kBN;
+  // The last slice of an expert may hold fewer than 128 rows: only its occupied 32-row MFMA tiles
+  // are computed.
+  const int nmt = (mrows + 31) >> 5;
   if (ex.kind == kNV) {
-    run_tile<kNV>(p, ex, m0, mrows, n0, st);
+    if (nmt <= 2) {
+      run_tile<kNV, 2>(p, ex, m0, mrows, n0, st);
+    } else {
+      run_tile<kNV, 4>(p, ex, m0, mrows, n0, st);
+    }
   } else if (ex.kind == kMX) {
-    run_tile<kMX>(p, ex, m0, mrows, n0, st);
+    run_tile<kMX, 4>(p, ex, m0, mrows, n0, st);
   } else {
     for (int i = threadIdx.x; i < mrows * kBN; i += kThreads) {
       const int rr = m0 + i / kBN, col = n0 + i % kBN;
