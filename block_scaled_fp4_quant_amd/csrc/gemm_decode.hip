@@ -14,7 +14,8 @@
 // Data movement (the path is HBM-bound; what costs is the number and geometry of load requests):
 //   weights: each lane streams 16 bytes per column tile per 128-wide k block straight into a ring of
 //     4 register slots (one per block of a 512-wide k chunk); a load instruction covers 16 column
-//     rows x 64 contiguous bytes.
+//     rows x 64 contiguous bytes, and the ring is refilled two blocks at a time so that both halves
+//     of a column's 128-byte line are requested together.
 //   activation codes, activation scales and weight scales: staged per 512-wide k chunk through a
 //     two-stage LDS ring shared by the 4 wavefronts, loaded as contiguous row pieces (512 bytes of
 //     activation codes, 32 or 16 bytes of weight scales per column row).  One activation load serves
@@ -277,9 +278,12 @@ __device__ void run_pass(const GemmArgs& p, const ExpertView& ex, int n0, int m0
   __builtin_amdgcn_sched_barrier(0);
   u32x4 wq[kBlk][kCT];
 #pragma unroll
-  for (int j = 0; j < kBlk; ++j) {
+  for (int j = 0; j < kBlk; j += 2) {
 #pragma unroll
-    for (int ct = 0; ct < kCT; ++ct) wq[j][ct] = buf_load_x4(r.w, j < nblk ? wo[ct] + (uint32_t)j * 64u : kOffNone);
+    for (int ct = 0; ct < kCT; ++ct) {
+      wq[j][ct] = buf_load_x4(r.w, j < nblk ? wo[ct] + (uint32_t)j * 64u : kOffNone);
+      wq[j + 1][ct] = buf_load_x4(r.w, j + 1 < nblk ? wo[ct] + (uint32_t)(j + 1) * 64u : kOffNone);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -308,10 +312,16 @@ __device__ void run_pass(const GemmArgs& p, const ExpertView& ex, int n0, int m0
           compute_block_mx<MT>(cur, bq, wave, wq[bq], acc);
         }
       }
-      const int bn = b + kBlk;
+      // Refill the ring two blocks at a time: the two 64-byte halves of each column's 128-byte
+      // line are requested back to back, so the line is fetched from HBM once.
+      if (bq & 1) {
+        const int bn = b + kBlk;
 #pragma unroll
-      for (int ct = 0; ct < kCT; ++ct)
-        wq[bq][ct] = buf_load_x4(r.w, bn < nblk ? wo[ct] + (uint32_t)bn * 64u : kOffNone);
+        for (int ct = 0; ct < kCT; ++ct) {
+          wq[bq - 1][ct] = buf_load_x4(r.w, bn - 1 < nblk ? wo[ct] + (uint32_t)(bn - 1) * 64u : kOffNone);
+          wq[bq][ct] = buf_load_x4(r.w, bn < nblk ? wo[ct] + (uint32_t)bn * 64u : kOffNone);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
