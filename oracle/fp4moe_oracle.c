@@ -13,6 +13,9 @@
  *            decode closure (sign, 4-bit exponent with bias 7, 3-bit mantissa, subnormals, NaN);
  *            f16g grouped GEMM section (CSR row offsets per expert).
  *   [QWEN]   memra-engine 0.125.0, src/bin/qwen4exp_gpu_gate.rs -- NVFP4 synthetic checkpoint rows.
+ *   [GATE] also supplies the expert activation between the projections: the swiglu_limit
+ *            saturation cell (its clamp math and its swiglu call, whose last pointer argument is
+ *            an optional per-row weight).
  *
  * Readings where the pages are silent (each is listed with its reason in the design notes):
  *   - E2M1 values: the pages import a table without printing it; the OCP MX E2M1 grid
@@ -319,4 +322,31 @@ void or_dequant_acts(const uint8_t* a_codes, const float* a_scales, int64_t g, i
     for (int64_t r = 0; r < g; ++r)
         for (int64_t kk = 0; kk < k; ++kk)
             ad[r * k + kk] = or_e4m3_value(a_codes[r * k + kk]) * (double)a_scales[r * (k / 128) + kk / 128];
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * Expert activation between the gate/up and the down projection [GATE: the swiglu_limit
+ * saturation cell -- its clamp math and its swiglu call]
+ * ------------------------------------------------------------------------------------------- */
+
+/* h[r, i] = silu(min(g, limit)) * clamp(u, -limit, limit) * w[r], computed in f64, where
+ * g = gu[r, i] and u = gu[r, inter + i] (gu f32 [rows, 2*inter]: the fused gate/up GEMM output,
+ * gate columns first), silu(t) = t / (1 + exp(-t)), and w[r] = 1 when w is NULL.  The gate is
+ * clamped from above only and the up projection on both sides, both before the product.  The
+ * routing weight is a per-row factor applied before the result is quantized again. */
+void or_swiglu(const float* gu, int64_t rows, int64_t inter, const float* w, float limit, double* h) {
+    const double lim = (double)limit;
+    for (int64_t r = 0; r < rows; ++r) {
+        const double wr = w ? (double)w[r] : 1.0;
+        const float* gate = gu + r * 2 * inter;
+        const float* up = gate + inter;
+        for (int64_t i = 0; i < inter; ++i) {
+            double g = (double)gate[i];
+            double u = (double)up[i];
+            if (g > lim) g = lim;
+            if (u > lim) u = lim;
+            if (u < -lim) u = -lim;
+            h[r * inter + i] = g / (1.0 + exp(-g)) * u * wr;
+        }
+    }
 }

@@ -77,6 +77,8 @@ def _load():
             lib.or_dequant_weights.argtypes = [P, P, ctypes.c_float, ctypes.c_int, I64, I64, P]
             lib.or_dequant_acts.restype = None
             lib.or_dequant_acts.argtypes = [P, P, I64, I64, P]
+            lib.or_swiglu.restype = None
+            lib.or_swiglu.argtypes = [P, I64, I64, P, ctypes.c_float, P]
             _lib = lib
     return _lib
 
@@ -277,3 +279,23 @@ def pages_op_count(kind, k) -> float:
     (reported as a diagnostic only)."""
     gs = GROUP_SIZE[kind]
     return (gs - 1) + np.ceil((k / gs) / 128.0) + 7
+
+
+# --------------------------------------------------------------------------- expert activation
+
+def swiglu(gu, inter: int, limit: float, weights=None) -> np.ndarray:
+    """h = silu(min(gate, limit)) * clamp(up, -limit, limit) * weight per row, in f64.
+
+    gu: f32 [rows, 2*inter] (gate columns first, then up); weights: f32 [rows] or None."""
+    gu, pg = _c(gu, np.float32)
+    rows = gu.shape[0]
+    if gu.shape != (rows, 2 * inter):
+        raise ValueError("gu must be [rows, 2*inter]")
+    pw = None
+    if weights is not None:
+        weights, pw = _c(weights, np.float32)
+        if weights.shape != (rows,):
+            raise ValueError("weights must be [rows]")
+    h = np.empty((rows, inter), dtype=np.float64)
+    _load().or_swiglu(pg, rows, inter, pw, float(limit), h.ctypes.data)
+    return h
