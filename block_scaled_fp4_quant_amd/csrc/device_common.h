@@ -7,9 +7,10 @@
 namespace fp4moe {
 
 typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------------------- buffer loads
@@ -103,6 +104,27 @@ __device__ __forceinline__ h16x8 e2m1x8_scaled_f16(uint32_t w, _Float16 s) {
   return h16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// --------------------------------------------------------------------------- FP8 / FP4 -> bf16
+// Eight E4M3 bytes (two dwords, byte order = element order) -> exact bf16x8 operand.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Eight E2M1 nibbles (one dword, low nibble first) times a power of two -> bf16x8.  The hardware
+// conversion applies the exponent field of `pow2` (an E8M0 scale placed in the f32 exponent bits),
+// so the result is exact.
+__device__ __forceinline__ bf16x8 e2m1x8_pow2_bf16(uint32_t w, float pow2) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, pow2, 0);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, pow2, 1);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, pow2, 2);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, pow2, 3);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 // ------------------------------------------------------------------------------ matrix cores
 // 16x16x32 f16 MFMA.  Lane l holds A row l%16 (B column l%16) for k = 8*(l/16) .. +8; the f32
 // result holds column l%16, rows 4*(l/16) .. +4.
@@ -110,12 +132,9 @@ __device__ __forceinline__ f32x4 mfma16x16x32_f16(h16x8 a, h16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// 16x16x128 block-scaled MFMA, A = FP8 E4M3, B = FP4 E2M1.  B lane l holds column l%16 for
-// k = 32*(l/16) .. +32 (16 bytes, low nibble first); A lane l holds row l%16 for
-// k = 16*(l/16) .. +16 (bytes 0..15) and 64 + 16*(l/16) .. +16 (bytes 16..31); lane r + 16q carries
-// the E8M0 scale of row/column r for k-block q (k = 32q .. +32).  Result layout as above.
-__device__ __forceinline__ f32x4 mfma16x16x128_f8f4(i32x8 a, i32x8 b, f32x4 c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, sa, 0, sb);
+// 16x16x32 bf16 MFMA, same lane layout as the f16 one.
+__device__ __forceinline__ f32x4 mfma16x16x32_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 }  // namespace fp4moe

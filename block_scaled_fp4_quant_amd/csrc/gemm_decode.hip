@@ -29,8 +29,11 @@
 //     accumulate a partial tile that is scaled by as[r, block] in one f32 FMA.  scale2 multiplies
 //     the final sum (exact for power-of-two scale2; otherwise within one f32 rounding of the
 //     per-group weight scale, inside the accuracy bound).
-//   MXFP4: one block-scaled MFMA 16x16x128 per column tile on raw E4M3 activation bytes and raw
-//     nibbles, with the E8M0 weight scales and the activation scale's exponent as E8M0 row scale.
+//   MXFP4: bf16 MFMA 16x16x32 with the same block structure.  Activation bytes -> bf16 (exact);
+//     nibbles -> bf16 with the E8M0 scale applied by the conversion (a pure exponent: exact; bf16
+//     because an E8M0 scale can leave the f16 range).  The block-scaled FP8 x FP4 MFMA is not used:
+//     it aligns its products to the largest one and drops the low bits of the others before
+//     summing (measured: 448 + 2^-6 -> 448), which breaks the f32-accumulation error bound.
 //
 // Workgroup order is XCD-aware when there are >= 8 experts: consecutive workgroup ids go to
 // different XCDs, so ids are arranged such that all column tiles of one expert land on one XCD and
@@ -189,25 +192,50 @@ __device__ __forceinline__ void compute_block_nv(const Stage& st, int bq, const 
   }
 }
 
+// MXFP4 block: exact bf16 operands (E4M3 activation bytes -> bf16; nibbles -> bf16 with the E8M0
+// scale applied by the conversion, a pure exponent) and the same per-block partial tile as NVFP4.
+// bf16 rather than f16 because an E8M0 scale can lie outside the f16 range.
 template <int MT>
 __device__ __forceinline__ void compute_block_mx(const Stage& st, int bq, int wave, const u32x4 (&wq)[kCT],
                                                  f32x4 (&acc)[MT][kCT]) {
   const int lane = threadIdx.x & 63, c16 = lane & 15, g = lane >> 4;
-  int sb[kCT];
+  f32x4 part[MT][kCT];
 #pragma unroll
-  for (int ct = 0; ct < kCT; ++ct) sb[ct] = st.s[(wave * kWaveCols + 16 * ct + c16) * kSCol + 4 * bq + g];
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int ct = 0; ct < kCT; ++ct) part[mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 aq[MT][2];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const uint8_t* ap = st.a + (16 * mt + c16) * kARow + bq * 128 + 16 * g;
-    const u32x4 a0 = *reinterpret_cast<const u32x4*>(ap);
-    const u32x4 a1 = *reinterpret_cast<const u32x4*>(ap + 64);
-    const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-    const int sa = (int)((f2u(st.as[bq * kRows + 16 * mt + c16]) >> 23) & 0xFFu);   // 2^e -> E8M0
+    const uint8_t* ap = st.a + (16 * mt + c16) * kARow + bq * 128 + 32 * g;
+    aq[mt][0] = *reinterpret_cast<const u32x4*>(ap);
+    aq[mt][1] = *reinterpret_cast<const u32x4*>(ap + 16);
+  }
+  // The lane's k = 32g .. +32 of the block is one MXFP4 group: E8M0 byte 4*bq + g of the column's
+  // chunk scales, used as the exponent field of the conversion's scale operand.
+  float sv[kCT];
+#pragma unroll
+  for (int ct = 0; ct < kCT; ++ct)
+    sv[ct] = u2f((uint32_t)st.s[(wave * kWaveCols + 16 * ct + c16) * kSCol + 4 * bq + g] << 23);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    bf16x8 af[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) af[mt] = e4m3x8_to_bf16(aq[mt][i >> 1][2 * (i & 1)], aq[mt][i >> 1][2 * (i & 1) + 1]);
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct) {
-      const i32x8 bw = {(int)wq[ct][0], (int)wq[ct][1], (int)wq[ct][2], (int)wq[ct][3], 0, 0, 0, 0};
-      acc[mt][ct] = mfma16x16x128_f8f4(a, bw, acc[mt][ct], sa, sb[ct]);
+      const bf16x8 bf = e2m1x8_pow2_bf16(wq[ct][i], sv[ct]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) part[mt][ct] = mfma16x16x32_bf16(af[mt], bf, part[mt][ct]);
     }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const f32x4 as = *reinterpret_cast<const f32x4*>(st.as + bq * kRows + 16 * mt + 4 * g);
+#pragma unroll
+    for (int ct = 0; ct < kCT; ++ct)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[mt][ct][v] = fmaf(part[mt][ct][v], as[v], acc[mt][ct][v]);
   }
 }
 

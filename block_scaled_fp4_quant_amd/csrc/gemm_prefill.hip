@@ -14,8 +14,10 @@
 //      (<= 6 significant bits: exact), packed to bf16 (exact).  scale2 multiplies the final f32 sum
 //      (exact for power-of-two scale2, otherwise within one f32 rounding of the per-group weight
 //      scale).  Products of these bf16 values are exact in f32.
-//   MXFP4 tiles take a separate route (below): the block-scaled FP8 x FP4 MFMA on raw activation
-//   bytes and raw nibbles, both scales applied natively as E8M0.
+//   MXFP4: nibble -> bf16 with the E8M0 scale applied by the hardware conversion (a pure exponent:
+//      exact).  The block-scaled FP8 x FP4 MFMA is not used: it aligns its products to the largest
+//      one before summing and drops the low bits of the others (measured: 448 + 2^-6 -> 448), which
+//      breaks the f32-accumulation error bound; the bf16 and f16 MFMAs sum exactly.
 //   On gfx950 the 32x32x16 and 16x16x32 bf16 MFMAs issue at the same rate (about 32 cycles), so
 //   the 32x32 shape does twice the work per instruction.
 //
@@ -44,8 +46,6 @@
 namespace fp4moe {
 namespace {
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -365,171 +365,6 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
     }
 }
 
-// ------------------------------------------------------------------------------------------------
-// MXFP4 tiles: both scales are powers of two that the block-scaled FP8 x FP4 MFMA applies natively
-// (E8M0 per 32 k for the weights; the activation scale's exponent field for the rows), so the raw
-// activation bytes and raw nibbles go straight into v_mfma_scale_f32_16x16x128_f8f6f4: no
-// conversion work, and four times the MACs per instruction of the bf16 route.
-//
-// Same 128 x 256 tile and 4 wavefronts x 64 columns, computed as up to two 64-row passes over k
-// (the weights of an MXFP4 tile are read once per pass): per wavefront 4 row tiles of 16 x 4 column
-// tiles of 16 (64 f32 accumulators per lane), one MFMA per (row tile, column tile) per 128-wide k
-// block.  The matrix cores do a quarter of the bf16 route's cycles per MAC, so the second pass
-// costs less than the dequantization it replaces.  Operand layout (measured): B lane (c, g) holds column c, k = 32g .. +32 (the column's 16
-// block bytes 16g .. +16, low nibble first) and the E8M0 scale of k-block g; A lane (r, g) holds row
-// r, k = 16g .. +16 and 64 + 16g .. +16, and the row's scale.
-constexpr int kMxRows = 64;                  // rows per pass
-constexpr int kMxMT = kMxRows / 16;          // 4 row tiles of 16
-constexpr int kMxCT = kWaveCols / 16;        // 4 column tiles of 16 per wavefront
-constexpr int kMxARow = 128 + 16;            // raw activation bytes of one block, padded
-
-struct MxStage {
-  uint8_t a[kMxRows * kMxARow];              // raw E4M3 activation codes, [row][128 k]
-  uint8_t ae[kMxRows];                       // activation scale exponent (E8M0) per row
-};
-static_assert(sizeof(MxStage) <= sizeof(Stage), "the MXFP4 stage overlays the bf16 stage");
-
-struct MxWRegs {
-  u32x4 w[kMxCT];                            // 16 nibble bytes per column tile
-  uint32_t s[kMxCT];                         // the column's 4 E8M0 bytes of the block
-};
-
-__device__ __forceinline__ void mx_w_load(const Rsrc& r, const uint32_t (&wo)[kMxCT], const uint32_t (&so)[kMxCT],
-                                          int b, int nblk, MxWRegs& d) {
-  const bool valid = b < nblk;
-#pragma unroll
-  for (int ct = 0; ct < kMxCT; ++ct) d.w[ct] = buf_load_x4(r.w, valid ? wo[ct] + (uint32_t)b * 64u : kOffNone);
-#pragma unroll
-  for (int ct = 0; ct < kMxCT; ++ct) d.s[ct] = buf_load_u32(r.s, valid ? so[ct] + (uint32_t)b * 4u : kOffNone);
-}
-
-// The staged activation bytes go to LDS unchanged; the first lane of each row also stores the
-// exponent field of the row's power-of-two scale, which is its E8M0 code.
-__device__ __forceinline__ void mx_stage_store(MxStage& st, const StageRegs& d) {
-  const int tid = threadIdx.x, c = tid & 7;
-#pragma unroll
-  for (int i = 0; i < kMxRows / 32; ++i) {
-    const int row = (tid >> 3) + 32 * i;
-    *reinterpret_cast<u32x4*>(st.a + row * kMxARow + 16 * c) = d.a[i];
-    if (c == 0) st.ae[row] = (uint8_t)((f2u(d.as[i]) >> 23) & 0xFFu);
-  }
-}
-
-__device__ __forceinline__ void mx_compute_block(const MxStage& st, const MxWRegs& w, f32x4 (&acc)[kMxMT][kMxCT]) {
-  const int lane = threadIdx.x & 63, c16 = lane & 15, g = lane >> 4;
-  i32x8 bw[kMxCT];
-  int sb[kMxCT];
-#pragma unroll
-  for (int ct = 0; ct < kMxCT; ++ct) {
-    bw[ct] = i32x8{(int)w.w[ct][0], (int)w.w[ct][1], (int)w.w[ct][2], (int)w.w[ct][3], 0, 0, 0, 0};
-    sb[ct] = (int)((w.s[ct] >> (8 * g)) & 0xFFu);
-  }
-#pragma unroll
-  for (int mt = 0; mt < kMxMT; ++mt) {
-    const uint8_t* ap = st.a + (16 * mt + c16) * kMxARow + 16 * g;
-    const u32x4 a0 = *reinterpret_cast<const u32x4*>(ap);
-    const u32x4 a1 = *reinterpret_cast<const u32x4*>(ap + 64);
-    const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-    const int sa = st.ae[16 * mt + c16];
-#pragma unroll
-    for (int ct = 0; ct < kMxCT; ++ct) acc[mt][ct] = mfma16x16x128_f8f4(a, bw[ct], acc[mt][ct], sa, sb[ct]);
-    // One row tile's activation fragment at a time: this path shares the kernel's register budget
-    // with the bf16 paths.
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// One 64-row pass of an MXFP4 tile: packed rows [m0, m0 + mrows), mrows <= 64.  Block b: barrier
-// (stage b&1 complete, stage (b+1)&1 free), store block b+1 from the staging registers, load block
-// b+2 into them, compute block b, refill the weight ring slot of block b with block b+2.
-__device__ __forceinline__ void run_pass_mx(const GemmArgs& p, const ExpertView& ex, int m0, int mrows, int n0,
-                                            MxStage (&st)[2]) {
-  const int tid = threadIdx.x, lane = tid & 63, c16 = lane & 15, g = lane >> 4;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int k = p.k, nblk = k >> 7;
-
-  Rsrc r;
-  r.w = make_rsrc(ex.w, (uint32_t)p.n * (uint32_t)(k / 2));
-  r.s = make_rsrc(ex.s, (uint32_t)p.n * (uint32_t)(k / 32));
-  r.a = make_rsrc(p.a_codes, (uint32_t)p.a_rows * (uint32_t)k);
-  r.as = make_rsrc(p.a_scales, (uint32_t)p.a_rows * (uint32_t)nblk * 4u);
-
-  AOffs ao;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (tid >> 3) + 32 * i;
-    const int ar = (i < kMxRows / 32 && row < mrows) ? act_row(p, m0 + row) : -1;
-    ao.a[i] = ar >= 0 ? (uint32_t)ar * (uint32_t)k + 16u * (tid & 7) : kOffNone;
-    ao.as[i] = ar >= 0 ? (uint32_t)ar * (uint32_t)nblk * 4u : kOffNone;
-  }
-  uint32_t wo[kMxCT], so[kMxCT];
-#pragma unroll
-  for (int ct = 0; ct < kMxCT; ++ct) {
-    const int col = n0 + wave * kWaveCols + 16 * ct + c16;
-    wo[ct] = col < p.n ? (uint32_t)col * (uint32_t)(k / 2) + 16u * g : kOffNone;
-    so[ct] = col < p.n ? (uint32_t)col * (uint32_t)(k / 32) : kOffNone;
-  }
-
-  f32x4 acc[kMxMT][kMxCT];
-#pragma unroll
-  for (int mt = 0; mt < kMxMT; ++mt)
-#pragma unroll
-    for (int ct = 0; ct < kMxCT; ++ct) acc[mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  StageRegs sr;
-  MxWRegs wr[2];
-  stage_load(r, ao, 0, nblk, sr);
-  __builtin_amdgcn_sched_barrier(0);
-  mx_stage_store(st[0], sr);
-  stage_load(r, ao, 1, nblk, sr);
-  __builtin_amdgcn_sched_barrier(0);
-  mx_w_load(r, wo, so, 0, nblk, wr[0]);
-  __builtin_amdgcn_sched_barrier(0);
-  mx_w_load(r, wo, so, 1, nblk, wr[1]);
-  __builtin_amdgcn_sched_barrier(0);
-
-  for (int b = 0; b < nblk; b += 2) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int bb = b + j;
-      lds_barrier();
-      mx_stage_store(st[(j + 1) & 1], sr);   // block bb+1 (zeros past the end)
-      stage_load(r, ao, bb + 2, nblk, sr);
-      __builtin_amdgcn_sched_barrier(0);
-      if (bb < nblk) mx_compute_block(st[j & 1], wr[j], acc);
-      __builtin_amdgcn_sched_barrier(0);
-      mx_w_load(r, wo, so, bb + 2, nblk, wr[j]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-
-#pragma unroll
-  for (int mt = 0; mt < kMxMT; ++mt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = 16 * mt + 4 * g + v;
-      if (row < mrows) {
-        const int prow = m0 + row;
-        const bool bad = act_row(p, prow) < 0;
-#pragma unroll
-        for (int ct = 0; ct < kMxCT; ++ct) {
-          const int col = n0 + wave * kWaveCols + 16 * ct + c16;
-          if (col < p.n) p.out[(size_t)prow * p.n + col] = bad ? __builtin_nanf("") : acc[mt][ct][v];
-        }
-      }
-    }
-}
-
-// An MXFP4 tile of up to 128 rows as up to two 64-row passes.
-__device__ __forceinline__ void run_tile_mx(const GemmArgs& p, const ExpertView& ex, int m0, int mrows, int n0,
-                                            Stage (&stb)[2]) {
-  MxStage (&st)[2] = reinterpret_cast<MxStage (&)[2]>(stb);
-  for (int h = 0; h < mrows; h += kMxRows) {
-    if (h > 0) lds_barrier();                // every wavefront is done with the previous pass's stages
-    run_pass_mx(p, ex, m0 + h, min(kMxRows, mrows - h), n0, st);
-  }
-}
-
 __global__ __launch_bounds__(kThreads, 2) void gemm_prefill_kernel(GemmArgs p, int ntn) {
   __shared__ Stage st[2];
   __shared__ int s_tile[3];
@@ -600,7 +435,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill_kernel(GemmArgs p, i
       run_tile<kNV, 4>(p, ex, m0, mrows, n0, st);
     }
   } else if (ex.kind == kMX) {
-    run_tile_mx(p, ex, m0, mrows, n0, st);
+    run_tile<kMX, 4>(p, ex, m0, mrows, n0, st);
   } else {
     for (int i = threadIdx.x; i < mrows * kBN; i += kThreads) {
       const int rr = m0 + i / kBN, col = n0 + i % kBN;
