@@ -37,6 +37,8 @@ def lib() -> ctypes.CDLL:
         P, I32, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
         L.act_quant_fp8.argtypes = [P, P, P, I32, I32, P]
         L.act_quant_fp8.restype = ctypes.c_int
+        L.swiglu_quant_fp8.argtypes = [P, P, F32, P, P, P, I32, I32, P]
+        L.swiglu_quant_fp8.restype = ctypes.c_int
         L.fp4_expert_gemm.argtypes = [P, P, P, P, F32, I32, P, I32, I32, I32, P]
         L.fp4_expert_gemm.restype = ctypes.c_int
         L.fp4_grouped_gemm.argtypes = [P, P, I32, P, P, I32, I32, P, P, P, P, P, I32, I32, P]
@@ -103,6 +105,37 @@ def act_quant_fp8(x: torch.Tensor, codes=None, scales=None, stream=None):
         raise ValueError("codes/scales shapes do not match x")
     _check(lib().act_quant_fp8(_ptr(x), _ptr(codes), _ptr(scales), rows, k, _stream(stream)),
            "act_quant_fp8")
+    return codes, scales
+
+
+def swiglu_quant_fp8(gu: torch.Tensor, limit: float, row_weights=None, codes=None, scales=None,
+                     h_out=None, stream=None):
+    """gu f32 [rows, 2*inter] (gate columns first, then up) -> (codes u8 [rows, inter],
+    scales f32 [rows, inter/128]) of h = silu(min(gate, limit)) * clamp(up, +-limit) * row weight.
+    h_out (f32 [rows, inter]) receives h itself when given."""
+    _dev(gu, torch.float32, "gu", 2)
+    rows, two_inter = gu.shape
+    if two_inter % 2:
+        raise ValueError("gu must have 2*inter columns")
+    inter = two_inter // 2
+    if row_weights is not None:
+        _dev(row_weights, torch.float32, "row_weights", 1)
+        if row_weights.shape != (rows,):
+            raise ValueError("row_weights must be [rows]")
+    if codes is None:
+        codes = torch.empty((rows, inter), dtype=torch.uint8, device=gu.device)
+    if scales is None:
+        scales = torch.empty((rows, inter // 128), dtype=torch.float32, device=gu.device)
+    _dev(codes, torch.uint8, "codes", 2)
+    _dev(scales, torch.float32, "scales", 2)
+    if codes.shape != (rows, inter) or scales.shape != (rows, inter // 128):
+        raise ValueError("codes/scales shapes do not match gu")
+    if h_out is not None:
+        _dev(h_out, torch.float32, "h_out", 2)
+        if h_out.shape != (rows, inter):
+            raise ValueError("h_out must be [rows, inter]")
+    _check(lib().swiglu_quant_fp8(_ptr(gu), _ptr(row_weights), float(limit), _ptr(codes), _ptr(scales),
+                                  _ptr(h_out), rows, inter, _stream(stream)), "swiglu_quant_fp8")
     return codes, scales
 
 

@@ -73,6 +73,18 @@ int act_quant_fp8(const float* x, uint8_t* codes, float* scales, int32_t rows, i
   return launched(fp4moe::launch_act_quant(x, codes, scales, ngroups, stream), "act_quant_fp8");
 }
 
+int swiglu_quant_fp8(const float* gu, const float* row_weights, float limit, uint8_t* codes,
+                     float* scales, float* h_out, int32_t rows, int32_t inter, hipStream_t stream) {
+  if (rows < 0) return fail(FP4MOE_EINVAL, "swiglu_quant_fp8: rows = %d < 0", (int)rows);
+  if (inter <= 0 || inter % 128 != 0)
+    return fail(FP4MOE_EINVAL, "swiglu_quant_fp8: inter = %d must be a positive multiple of 128", (int)inter);
+  if (!(limit > 0.0f)) return fail(FP4MOE_EINVAL, "swiglu_quant_fp8: limit must be > 0");
+  if (rows == 0) return ok();
+  if (!gu || !codes || !scales) return fail(FP4MOE_EINVAL, "swiglu_quant_fp8: NULL buffer with rows > 0");
+  return launched(fp4moe::launch_swiglu_quant(gu, row_weights, limit, codes, scales, h_out, rows, inter, stream),
+                  "swiglu_quant_fp8");
+}
+
 int fp4_expert_gemm(const uint8_t* a_codes, const float* a_scales, const uint8_t* w_packed,
                     const uint8_t* w_scales, float scale2, int32_t kind, float* out, int32_t g,
                     int32_t n, int32_t k, hipStream_t stream) {

@@ -33,6 +33,12 @@ struct GemmArgs {
 hipError_t launch_act_quant(const float* x, uint8_t* codes, float* scales, int64_t ngroups,
                             hipStream_t stream);
 
+// The expert activation (swiglu with limit, optional row weight) fused with the FP8 quantization
+// of its result; inter % 128 == 0.
+hipError_t launch_swiglu_quant(const float* gu, const float* weights, float limit, uint8_t* codes,
+                               float* scales, float* h_out, int64_t rows, int32_t inter,
+                               hipStream_t stream);
+
 // Row-streaming kernel for few rows per expert (decode): every expert's weights are read once per
 // pass of 32 rows.
 hipError_t launch_gemm_decode(const GemmArgs& a, hipStream_t stream);

@@ -10,6 +10,8 @@
  *   [CHECK] memra-engine 0.71.0, src/bin/kernel_check.rs: f16g grouped GEMM section (rows packed
  *           per expert with a CSR offsets array) and the direct-from-quant section (a per-expert
  *           table of weight addresses).
+ *   [GATE]  also: the swiglu_limit saturation cell (the clamp math between the gate/up and the down
+ *           projection, and its swiglu call with an optional per-row weight).
  *
  * Conventions for every call:
  *   - All pointers are DEVICE pointers unless marked [host].  Buffers are row-major and densely
@@ -104,6 +106,27 @@ FP4MOE_API int fp4_grouped_gemm(const uint8_t* a_codes, const float* a_scales, i
                      int32_t total_rows, const uint64_t* w_ptrs, const uint64_t* s_ptrs,
                      const int32_t* kinds, const float* scale2, float* out, int32_t n, int32_t k,
                      hipStream_t stream);
+
+/*
+ * swiglu_quant_fp8 -- [GATE: the swiglu_limit saturation cell, then quant_rows].  The expert
+ * activation between the fused gate/up projection and the down projection, quantized for the down
+ * projection's GEMM.  For every row r and column i < inter:
+ *   g = min(gu[r, i], limit);  u = clamp(gu[r, inter + i], -limit, limit);
+ *   h[r, i] = g * (1 / (1 + exp(-g))) * u * w[r]      (f32 operations in this order; w[r] = 1 when
+ *                                                       row_weights is NULL)
+ * then codes/scales = act_quant_fp8(h) (same definition as above, per 128 columns of h).
+ * gu:          f32 [rows, 2*inter], read only: the gate/up GEMM output, gate columns first.
+ * row_weights: f32 [rows] or NULL: a per-row factor (e.g. the routing weight of the packed row).
+ * limit:       [host] f32 > 0 (may be +Inf: no clamping).
+ * codes:       u8  [rows, inter], written.   scales: f32 [rows, inter/128], written.
+ * h_out:       f32 [rows, inter] or NULL: when given, receives h before quantization.
+ * Errors: EINVAL if rows < 0, inter <= 0, inter % 128 != 0, limit is not > 0, or a required
+ * pointer is NULL while rows > 0.  rows == 0 is a no-op.  exp is the device library's f32 expf, so
+ * h agrees with an exact evaluation to a few f32 ulps; inputs must be finite.
+ */
+FP4MOE_API int swiglu_quant_fp8(const float* gu, const float* row_weights, float limit, uint8_t* codes,
+                                float* scales, float* h_out, int32_t rows, int32_t inter,
+                                hipStream_t stream);
 
 /*
  * fp4moe_set_gemm_schedule -- test and benchmark hook (not part of the method).  The GEMM calls

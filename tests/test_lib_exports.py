@@ -30,8 +30,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for fn in ("act_quant_fp8", "fp4_expert_gemm", "fp4_grouped_gemm", "fp4moe_last_error",
-               "fp4moe_version"):
+    for fn in ("act_quant_fp8", "swiglu_quant_fp8", "fp4_expert_gemm", "fp4_grouped_gemm",
+               "fp4moe_last_error", "fp4moe_version"):
         assert fn in names
 
 
@@ -58,6 +58,20 @@ def test_act_quant_rejects(lib, rows, k):
 def test_act_quant_null_and_noop(lib):
     assert lib.act_quant_fp8(NULL, BAD, BAD, 4, 128, NULL) == 1
     assert lib.act_quant_fp8(NULL, NULL, NULL, 0, 128, NULL) == 0      # rows == 0: no-op
+    assert lib.fp4moe_last_error().decode() == ""
+
+
+@pytest.mark.parametrize("rows,inter,limit", [(-1, 128, 7.0), (4, 0, 7.0), (4, 96, 7.0), (4, 200, 7.0),
+                                              (4, 128, 0.0), (4, 128, -1.0), (4, 128, float("nan"))])
+def test_swiglu_quant_rejects(lib, rows, inter, limit):
+    assert lib.swiglu_quant_fp8(BAD, NULL, limit, BAD, BAD, NULL, rows, inter, NULL) == 1
+    assert lib.fp4moe_last_error().decode().startswith("swiglu_quant_fp8")
+
+
+def test_swiglu_quant_null_and_noop(lib):
+    assert lib.swiglu_quant_fp8(NULL, NULL, 7.0, BAD, BAD, NULL, 4, 128, NULL) == 1
+    assert lib.swiglu_quant_fp8(BAD, NULL, 7.0, BAD, NULL, NULL, 4, 128, NULL) == 1
+    assert lib.swiglu_quant_fp8(NULL, NULL, 7.0, NULL, NULL, NULL, 0, 128, NULL) == 0   # no-op
     assert lib.fp4moe_last_error().decode() == ""
 
 

@@ -259,3 +259,56 @@ def config4() -> GroupedWorkload:
     return GroupedWorkload("config4: grouped prefill, 8192 tokens, E=256 (255 NVFP4 + 1 MXFP4), "
                            "Zipf(1.1) top-8, k=7168, n=4096, Student-t(3)",
                            x, row_ids, offsets, kinds, scale2, w_bank, s_bank, w_off, s_off, n, k)
+
+
+@dataclass
+class ExpertChainWorkload:
+    """One MoE expert layer: token activations x [T, hidden], top-k routing packed per expert, a
+    per-packed-row routing weight, the fused gate/up projection bank (n = 2*inter, k = hidden: gate
+    rows first, then up rows) and the down projection bank (n = hidden, k = inter)."""
+    name: str
+    x: np.ndarray
+    row_ids: np.ndarray
+    offsets: np.ndarray
+    route_w: np.ndarray            # f32 [R]
+    kinds: np.ndarray
+    limit: float
+    up: GroupedWorkload            # gate/up projection (shares x, row_ids, offsets)
+    down: GroupedWorkload          # down projection (its x is unused: it consumes the activation)
+
+    @property
+    def R(self): return int(self.offsets[-1])
+
+    @property
+    def hidden(self): return self.x.shape[1]
+
+    @property
+    def inter(self): return self.up.n // 2
+
+
+def expert_chain(seed: int, T: int, E: int, top: int, hidden: int, inter: int, kinds=None,
+                 x_scale: float = 1.0, limit: float = 7.0, zipf: float | None = None) -> ExpertChainWorkload:
+    """Seeded inputs for the gate/up -> activation -> down chain (parity cases).  Routing weights are
+    uniform draws in [0.05, 1]; x_scale multiplies the N(0,1) activations (x50 drives both clamps of
+    the activation, as in the pages' saturation cell)."""
+    rng = np.random.default_rng([SEED_BASE, 400, seed])
+    kinds = np.zeros(E, dtype=np.int32) if kinds is None else np.asarray(kinds, dtype=np.int32)
+    x = (rng.standard_normal((T, hidden)) * x_scale).astype(np.float32)
+    if zipf is not None:
+        ranks = rng.permutation(E) + 1
+        logits = -zipf * np.log(ranks)[None, :] + rng.gumbel(size=(T, E))
+    else:
+        logits = rng.standard_normal((T, E))
+    row_ids, offsets = route_topk(logits, top)
+    route_w = rng.uniform(0.05, 1.0, size=int(offsets[-1])).astype(np.float32)
+    banks = []
+    for n, k in ((2 * inter, hidden), (hidden, inter)):
+        scale2 = np.array(GROUPED_SCALE2_CHOICES, dtype=np.float32)[rng.integers(0, 4, size=E)]
+        scale2[kinds == MXFP4] = 0.0
+        w_bank, s_bank, w_off, s_off = _bank(rng, kinds, n, k)
+        banks.append(GroupedWorkload(f"chain seed={seed} n={n} k={k}", x if k == hidden else
+                                     np.zeros((0, k), np.float32), row_ids, offsets, kinds, scale2,
+                                     w_bank, s_bank, w_off, s_off, n, k))
+    return ExpertChainWorkload(f"expert chain seed={seed} T={T} E={E} top={top} hidden={hidden} "
+                               f"inter={inter} x_scale={x_scale}", x, row_ids, offsets, route_w, kinds,
+                               float(limit), banks[0], banks[1])
