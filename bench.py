@@ -128,7 +128,9 @@ def main():
     # before the rate settles; the default warm-up covers that so the timed steps see the steady
     # state.
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="config3", choices=["config3", "config4"])
+    ap.add_argument("--workload", default="config3", choices=["config3", "config4", "chain4"],
+                    help="config3: grouped decode GEMM; config4: grouped prefill GEMM; chain4: the "
+                         "whole prefill expert layer (gate/up GEMM -> swiglu+quant -> down GEMM)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 disables it)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -149,6 +151,9 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     log(f"library: {fp4.version()}  device: {torch.cuda.get_device_name(dev)}")
+
+    if args.workload == "chain4":
+        return run_chain(args, torch, fp4, dev)
 
     t0 = time.perf_counter()
     wl = workloads.config3() if args.workload == "config3" else workloads.config4()
@@ -246,6 +251,88 @@ def main():
             log(f"cpu_baseline: timing the oracle for about {args.cpu_budget:.0f} s ...")
             result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
             log(f"cpu_baseline: {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+
+
+def upload_bank(gw, torch, dev):
+    w_bank = torch.from_numpy(gw.w_bank).to(dev)
+    s_bank = torch.from_numpy(gw.s_bank).to(dev)
+    w_ptrs = torch.from_numpy((w_bank.data_ptr() + gw.w_off).astype(np.int64)).to(dev)
+    s_ptrs = torch.from_numpy((s_bank.data_ptr() + gw.s_off).astype(np.int64)).to(dev)
+    return w_bank, s_bank, w_ptrs, s_ptrs, torch.from_numpy(gw.scale2.astype(np.float32)).to(dev)
+
+
+def run_chain(args, torch, fp4, dev):
+    """The whole prefill expert layer: act_quant -> gate/up grouped GEMM -> swiglu_quant ->
+    down grouped GEMM.  value = TFLOP/s of the two GEMMs over the step; the roofline is the
+    dominant kernel's (the gate/up GEMM); the activation kernel's HBM rate is reported beside it."""
+    t0 = time.perf_counter()
+    ch = workloads.config4_chain()
+    log(f"workload: {ch.name}  (generated in {time.perf_counter() - t0:.1f} s)")
+    x = torch.from_numpy(ch.x).to(dev)
+    row_ids = torch.from_numpy(ch.row_ids).to(dev)
+    offsets = torch.from_numpy(ch.offsets).to(dev)
+    kinds = torch.from_numpy(ch.kinds).to(dev)
+    rw = torch.from_numpy(ch.route_w).to(dev)
+    up = upload_bank(ch.up, torch, dev)
+    dn = upload_bank(ch.down, torch, dev)
+    T, Hd = ch.x.shape
+    R, I = ch.R, ch.inter
+    codes = torch.empty((T, Hd), dtype=torch.uint8, device=dev)
+    scales = torch.empty((T, Hd // 128), dtype=torch.float32, device=dev)
+    gu = torch.empty((R, 2 * I), dtype=torch.float32, device=dev)
+    hc = torch.empty((R, I), dtype=torch.uint8, device=dev)
+    hs = torch.empty((R, I // 128), dtype=torch.float32, device=dev)
+    y = torch.empty((R, Hd), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def launches():
+        yield lambda: fp4.act_quant_fp8(x, codes, scales, stream=stream)
+        yield lambda: fp4.fp4_grouped_gemm(codes, scales, row_ids, offsets, up[2], up[3], kinds, up[4],
+                                           2 * I, out=gu, stream=stream)
+        yield lambda: fp4.swiglu_quant_fp8(gu, ch.limit, row_weights=rw, codes=hc, scales=hs, stream=stream)
+        yield lambda: fp4.fp4_grouped_gemm(hc, hs, None, offsets, dn[2], dn[3], kinds, dn[4], Hd, out=y,
+                                           stream=stream)
+
+    for _ in range(args.warmup):
+        for f in launches():
+            f()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    wall0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        for j, f in enumerate(launches()):
+            f()
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = ev[0][0].elapsed_time(ev[K - 1][4]) / K
+    part = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev])) for j in range(4)]
+    f_up, f_dn = 2.0 * R * Hd * 2 * I, 2.0 * R * I * Hd
+    sw_bytes = R * I * (8 + 1) + R * (I // 128) * 4 + R * 4
+    log(f"timed {K} steps: wall {wall * 1e3 / K:.3f} ms/step, events {step_ms:.3f} ms/step "
+        f"(act_quant {part[0] * 1e3:.1f} us, gate/up GEMM {part[1] * 1e3:.1f} us, swiglu+quant "
+        f"{part[2] * 1e3:.1f} us, down GEMM {part[3] * 1e3:.1f} us)")
+    tf_up = f_up / (part[1] * 1e-3) / 1e12
+    sw_gbs = sw_bytes / (part[2] * 1e-3) / 1e9
+    log(f"gate/up {tf_up:.1f} TFLOP/s, down {f_dn / (part[3] * 1e-3) / 1e12:.1f} TFLOP/s, swiglu+quant "
+        f"{sw_gbs:.0f} GB/s ({sw_gbs / HBM_PEAK_GBS:.1%} of 8 TB/s)")
+    value = (f_up + f_dn) / (step_ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC, "value": round(value, 4), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8xfp4->f32", "data": "synthetic",
+        "config": {"workload": ch.name, "tokens": int(T), "experts": int(len(ch.kinds)), "top_k": 8,
+                   "routed_rows": int(R), "hidden": int(Hd), "inter": int(I),
+                   "gateup_gemm_us": round(part[1] * 1e3, 2), "swiglu_quant_us": round(part[2] * 1e3, 2),
+                   "down_gemm_us": round(part[3] * 1e3, 2), "act_quant_us": round(part[0] * 1e3, 2),
+                   "swiglu_quant_gbs": round(sw_gbs, 1)},
+        "roofline": {"bound": "mfma", "achieved": round(tf_up, 1), "peak": MFMA_PEAK_TFLOPS["f16"],
+                     "unit": "TFLOP/s", "frac": round(tf_up / MFMA_PEAK_TFLOPS["f16"], 4), "traffic": None},
+        "cpu_baseline": None,
+    }
     print(json.dumps(result), flush=True)
 
 

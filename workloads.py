@@ -312,3 +312,21 @@ def expert_chain(seed: int, T: int, E: int, top: int, hidden: int, inter: int, k
     return ExpertChainWorkload(f"expert chain seed={seed} T={T} E={E} top={top} hidden={hidden} "
                                f"inter={inter} x_scale={x_scale}", x, row_ids, offsets, route_w, kinds,
                                float(limit), banks[0], banks[1])
+
+
+def config4_chain() -> ExpertChainWorkload:
+    """The grouped prefill layer as a whole expert chain: config4's tokens, routing and fused
+    gate/up bank (n = 4096 = 2 x 2048, k = 7168), plus a down projection bank (n = 7168, k = 2048)
+    in the same formats (255 NVFP4 + 1 MXFP4), routing weights uniform in [0.05, 1], limit 7."""
+    up = config4()
+    rng = rng_for(4, 1)
+    inter = up.n // 2
+    scale2 = np.array(GROUPED_SCALE2_CHOICES, dtype=np.float32)[rng.integers(0, 4, size=up.E)]
+    scale2[up.kinds == MXFP4] = 0.0
+    w_bank, s_bank, w_off, s_off = _bank(rng, up.kinds, up.k, inter)
+    down = GroupedWorkload("config4 down projection", np.zeros((0, inter), np.float32), up.row_ids,
+                           up.offsets, up.kinds, scale2, w_bank, s_bank, w_off, s_off, up.k, inter)
+    route_w = rng.uniform(0.05, 1.0, size=up.R).astype(np.float32)
+    return ExpertChainWorkload("config4 expert layer: gate/up (n=4096, k=7168) -> swiglu limit 7 -> "
+                               "down (n=7168, k=2048); 8192 tokens, E=256, Zipf(1.1) top-8",
+                               up.x, up.row_ids, up.offsets, route_w, up.kinds, 7.0, up, down)
