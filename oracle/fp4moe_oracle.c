@@ -12,7 +12,8 @@
  *   [CHECK]  memra-engine 0.71.0, src/bin/kernel_check.rs -- F8-E4M3 matvec section, the CPU e4m3
  *            decode closure (sign, 4-bit exponent with bias 7, 3-bit mantissa, subnormals, NaN);
  *            f16g grouped GEMM section (CSR row offsets per expert).
- *   [QWEN]   memra-engine 0.125.0, src/bin/qwen4exp_gpu_gate.rs -- NVFP4 synthetic checkpoint rows.
+ *   [QWEN]   memra-engine 0.125.0, src/bin/qwen4exp_gpu_gate.rs -- NVFP4 synthetic checkpoint rows;
+ *            the device-router arm (softmax top-k over router logits, ids and order exact, ties).
  *   [GATE] also supplies the expert activation between the projections: the swiglu_limit
  *            saturation cell (its clamp math and its swiglu call, whose last pointer argument is
  *            an optional per-row weight).
@@ -348,5 +349,124 @@ void or_swiglu(const float* gu, int64_t rows, int64_t inter, const float* w, flo
             if (u < -lim) u = -lim;
             h[r * inter + i] = g / (1.0 + exp(-g)) * u * wr;
         }
+    }
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * Routing around the grouped GEMM [QWEN: the device-router arm -- softmax top-k over the router
+ * logits, selected ids and their emitted order exact, weights to a few ulp, tie batteries of
+ * duplicates straddling the cut, all-equal rows and underflow; CHECK: f16g grouped GEMM section --
+ * routed rows packed per expert, CSR offsets].  Readings where the pages are silent:
+ *   - selection is on the logits (softmax is strictly increasing, so this is the top-k of the exact
+ *     probabilities, with no ties created by rounding or underflow of the probabilities);
+ *   - a logit ranks above another when it is larger; equal logits (+0 and -0 are equal) rank by
+ *     the lower expert id; NaN ranks below every number, NaNs among themselves by id;
+ *   - experts are emitted best first;
+ *   - weight = exp(l - m) / sum over all experts of exp(l' - m), m the largest logit (the softmax
+ *     probability of the selected expert); with `normalize`, the sum runs over the k selected
+ *     experts only (the probabilities renormalized over the selection);
+ *   - pairs (t, j) are packed per expert in ascending expert id, and inside one expert in
+ *     ascending (t, j) order, i.e. ascending token order; ids outside [0, E) are dropped;
+ *   - the combine sums, for each token, weight * expert output over its k pairs.
+ * ------------------------------------------------------------------------------------------- */
+
+/* 1 when logit a of expert ia ranks above logit b of expert ib. */
+static int ranks_above(float a, int64_t ia, float b, int64_t ib) {
+    const int na = isnan(a), nb = isnan(b);
+    if (na || nb) return (na && nb) ? ia < ib : nb;
+    if (a != b) return a > b;
+    return ia < ib;
+}
+
+/* ids[t, j]: the j-th best expert of token t; weights[t, j]: its softmax weight in f64.
+ * logits f32 [tokens, experts]; ids int32 and weights f64 [tokens, top_k]; taken: scratch of
+ * `experts` bytes. */
+void or_route_topk(const float* logits, int64_t tokens, int64_t experts, int64_t top_k,
+                   int normalize, uint8_t* taken, int32_t* ids, double* weights) {
+    for (int64_t t = 0; t < tokens; ++t) {
+        const float* l = logits + t * experts;
+        memset(taken, 0, (size_t)experts);
+        for (int64_t j = 0; j < top_k; ++j) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < experts; ++e)
+                if (!taken[e] && (best < 0 || ranks_above(l[e], e, l[best], best))) best = e;
+            taken[best] = 1;
+            ids[t * top_k + j] = (int32_t)best;
+        }
+        /* softmax over every expert; NaN in, NaN out, and an infinite maximum gives inf - inf */
+        double m = -INFINITY;
+        int any_nan = 0;
+        for (int64_t e = 0; e < experts; ++e) {
+            if (isnan(l[e])) any_nan = 1;
+            else if ((double)l[e] > m) m = (double)l[e];
+        }
+        double denom = 0.0;
+        if (normalize) {
+            for (int64_t j = 0; j < top_k; ++j) denom += exp((double)l[ids[t * top_k + j]] - m);
+        } else {
+            for (int64_t e = 0; e < experts; ++e) denom += exp((double)l[e] - m);
+        }
+        if (any_nan) denom = NAN;
+        for (int64_t j = 0; j < top_k; ++j)
+            weights[t * top_k + j] = exp((double)l[ids[t * top_k + j]] - m) / denom;
+    }
+}
+
+/* Packs the pairs p = t * top_k + j per expert.  offsets int32 [experts + 1]; row_ids int32
+ * [pairs]: token of each packed row; pair_rows int32 [pairs]: packed row of each pair, -1 when
+ * the pair's id is outside [0, experts); row_w f32 [pairs] (optional): w[p] moved to its row.
+ * Rows past offsets[experts] are left untouched. */
+void or_route_pack(const int32_t* ids, const float* w, int64_t tokens, int64_t top_k,
+                   int64_t experts, int32_t* offsets, int32_t* row_ids, int32_t* pair_rows,
+                   float* row_w) {
+    const int64_t pairs = tokens * top_k;
+    for (int64_t p = 0; p < pairs; ++p) pair_rows[p] = -1;
+    int64_t r = 0;
+    for (int64_t e = 0; e < experts; ++e) {
+        offsets[e] = (int32_t)r;
+        for (int64_t p = 0; p < pairs; ++p) {
+            if (ids[p] != e) continue;
+            row_ids[r] = (int32_t)(p / top_k);
+            pair_rows[p] = (int32_t)r;
+            if (row_w) row_w[r] = w[p];
+            ++r;
+        }
+    }
+    offsets[experts] = (int32_t)r;
+}
+
+/* out[t, c] = sum over j of w[t, j] * y[pair_rows[t, j], c] in f64 (w = 1 when NULL), and
+ * abs_out[t, c] the same sum of magnitudes.  Pairs with pair_rows < 0 are skipped; a row index
+ * at or past y_rows makes the token's outputs NaN. */
+void or_combine(const float* y, int64_t y_rows, int64_t n, const int32_t* pair_rows,
+                const float* w, int64_t tokens, int64_t top_k, double* out, double* abs_out) {
+    for (int64_t t = 0; t < tokens; ++t)
+        for (int64_t c = 0; c < n; ++c) {
+            double s = 0.0, a = 0.0;
+            for (int64_t j = 0; j < top_k; ++j) {
+                const int64_t p = t * top_k + j;
+                const int64_t r = pair_rows[p];
+                if (r < 0) continue;
+                if (r >= y_rows) { s = NAN; a = NAN; break; }
+                const double term = (w ? (double)w[p] : 1.0) * (double)y[r * n + c];
+                s += term;
+                a += fabs(term);
+            }
+            out[t * n + c] = s;
+            abs_out[t * n + c] = a;
+        }
+}
+
+/* out_codes[p] = codes[row_ids[p]] and out_scales[p] = scales[row_ids[p]] row by row (k code
+ * bytes and k/128 scales per row); a row id outside [0, a_rows) gives code bytes 0 and NaN
+ * scales. */
+void or_gather_rows(const uint8_t* codes, const float* scales, int64_t a_rows, int64_t k,
+                    const int32_t* row_ids, int64_t rows, uint8_t* out_codes, float* out_scales) {
+    const int64_t nq = k / 128;
+    for (int64_t p = 0; p < rows; ++p) {
+        const int64_t r = row_ids[p];
+        const int ok = r >= 0 && r < a_rows;
+        for (int64_t i = 0; i < k; ++i) out_codes[p * k + i] = ok ? codes[r * k + i] : 0;
+        for (int64_t q = 0; q < nq; ++q) out_scales[p * nq + q] = ok ? scales[r * nq + q] : NAN;
     }
 }

@@ -79,6 +79,14 @@ def _load():
             lib.or_dequant_acts.argtypes = [P, P, I64, I64, P]
             lib.or_swiglu.restype = None
             lib.or_swiglu.argtypes = [P, I64, I64, P, ctypes.c_float, P]
+            lib.or_route_topk.restype = None
+            lib.or_route_topk.argtypes = [P, I64, I64, I64, ctypes.c_int, P, P, P]
+            lib.or_route_pack.restype = None
+            lib.or_route_pack.argtypes = [P, P, I64, I64, I64, P, P, P, P]
+            lib.or_combine.restype = None
+            lib.or_combine.argtypes = [P, I64, I64, P, P, I64, I64, P, P]
+            lib.or_gather_rows.restype = None
+            lib.or_gather_rows.argtypes = [P, P, I64, I64, P, I64, P, P]
             _lib = lib
     return _lib
 
@@ -299,3 +307,76 @@ def swiglu(gu, inter: int, limit: float, weights=None) -> np.ndarray:
     h = np.empty((rows, inter), dtype=np.float64)
     _load().or_swiglu(pg, rows, inter, pw, float(limit), h.ctypes.data)
     return h
+
+
+# --------------------------------------------------------------------------- routing
+
+def route_topk(logits, top_k: int, normalize: bool = False):
+    """Top-k experts per token by logit (best first; equal logits by the lower id; NaN last) and
+    their softmax weights in f64 (over all experts, or over the k selected with `normalize`).
+
+    logits: f32 [T, E].  Returns (ids int32 [T, k], weights f64 [T, k])."""
+    logits, pl = _c(logits, np.float32)
+    T, E = logits.shape
+    if not 1 <= top_k <= E:
+        raise ValueError("top_k must be in [1, E]")
+    ids = np.empty((T, top_k), dtype=np.int32)
+    w = np.empty((T, top_k), dtype=np.float64)
+    taken = np.empty(max(E, 1), dtype=np.uint8)
+    _load().or_route_topk(pl, T, E, top_k, int(bool(normalize)), taken.ctypes.data, ids.ctypes.data,
+                          w.ctypes.data)
+    return ids, w
+
+
+def route_pack(ids, experts: int, weights=None):
+    """Packs the pairs of ids int32 [T, k] per expert (ascending id, then ascending token).
+
+    Returns (offsets int32 [E+1], row_ids int32 [R], pair_rows int32 [T, k], row_w f32 [R] or None),
+    R = offsets[E]; pairs whose id is outside [0, E) are dropped (pair_rows -1)."""
+    ids, pi = _c(ids, np.int32)
+    T, k = ids.shape
+    pw = None
+    if weights is not None:
+        weights, pw = _c(weights, np.float32)
+        if weights.shape != (T, k):
+            raise ValueError("weights must be [T, k]")
+    offsets = np.empty(experts + 1, dtype=np.int32)
+    row_ids = np.empty(T * k, dtype=np.int32)
+    pair_rows = np.empty((T, k), dtype=np.int32)
+    row_w = np.empty(T * k, dtype=np.float32) if weights is not None else None
+    _load().or_route_pack(pi, pw, T, k, experts, offsets.ctypes.data, row_ids.ctypes.data,
+                          pair_rows.ctypes.data, None if row_w is None else row_w.ctypes.data)
+    R = int(offsets[-1])
+    return offsets, row_ids[:R].copy(), pair_rows, None if row_w is None else row_w[:R].copy()
+
+
+def combine(y, pair_rows, weights=None):
+    """out[t] = sum_j weights[t, j] * y[pair_rows[t, j]] in f64 (weights 1 when None), and the
+    matching sum of magnitudes.  y: f32 [R, n]; pair_rows int32 [T, k] (-1 = dropped pair)."""
+    y, py = _c(y, np.float32)
+    pair_rows, pp = _c(pair_rows, np.int32)
+    T, k = pair_rows.shape
+    n = y.shape[1]
+    pw = None
+    if weights is not None:
+        weights, pw = _c(weights, np.float32)
+        if weights.shape != (T, k):
+            raise ValueError("weights must be [T, k]")
+    out = np.empty((T, n), dtype=np.float64)
+    absout = np.empty((T, n), dtype=np.float64)
+    _load().or_combine(py, y.shape[0], n, pp, pw, T, k, out.ctypes.data, absout.ctypes.data)
+    return out, absout
+
+
+def gather_rows(codes, scales, row_ids):
+    """Rows row_ids of the act-quant codes [a_rows, k] and scales [a_rows, k/128]; a row id
+    outside [0, a_rows) gives zero codes and NaN scales."""
+    codes, pc = _c(codes, np.uint8)
+    scales, ps = _c(scales, np.float32)
+    row_ids, pr = _c(row_ids, np.int32)
+    a_rows, k = codes.shape
+    rows = row_ids.shape[0]
+    oc = np.empty((rows, k), dtype=np.uint8)
+    osc = np.empty((rows, k // 128), dtype=np.float32)
+    _load().or_gather_rows(pc, ps, a_rows, k, pr, rows, oc.ctypes.data, osc.ctypes.data)
+    return oc, osc
