@@ -43,6 +43,16 @@ def lib() -> ctypes.CDLL:
         L.fp4_expert_gemm.restype = ctypes.c_int
         L.fp4_grouped_gemm.argtypes = [P, P, I32, P, P, I32, I32, P, P, P, P, P, I32, I32, P]
         L.fp4_grouped_gemm.restype = ctypes.c_int
+        L.route_softmax_topk.argtypes = [P, I32, I32, I32, I32, P, P, P]
+        L.route_softmax_topk.restype = ctypes.c_int
+        L.route_pack_workspace_size.argtypes = [I32, I32]
+        L.route_pack_workspace_size.restype = ctypes.c_int64
+        L.route_pack.argtypes = [P, P, I32, I32, I32, P, P, P, P, P, P]
+        L.route_pack.restype = ctypes.c_int
+        L.gather_quant_rows.argtypes = [P, P, I32, I32, P, I32, P, P, P]
+        L.gather_quant_rows.restype = ctypes.c_int
+        L.moe_combine.argtypes = [P, I32, I32, P, P, I32, I32, P, P]
+        L.moe_combine.restype = ctypes.c_int
         L.fp4moe_last_error.argtypes = []
         L.fp4moe_last_error.restype = ctypes.c_char_p
         L.fp4moe_version.argtypes = []
@@ -198,4 +208,110 @@ def fp4_grouped_gemm(a_codes, a_scales, row_ids, offsets, w_ptrs, s_ptrs, kinds,
                                   _ptr(offsets), E, R, _ptr(w_ptrs), _ptr(s_ptrs), _ptr(kinds),
                                   _ptr(scale2), _ptr(out), int(n), k, _stream(stream)),
            "fp4_grouped_gemm")
+    return out
+
+
+# --------------------------------------------------------------------------- routing
+
+def route_softmax_topk(logits, top_k: int, normalize: bool = False, ids=None, weights=None, stream=None):
+    """logits f32 [T, E] -> (ids int32 [T, top_k], weights f32 [T, top_k]): the top_k experts per
+    token, best first (equal logits by the lower id), with their softmax weights (over all experts,
+    or over the selection with normalize)."""
+    _dev(logits, torch.float32, "logits", 2)
+    T, E = logits.shape
+    if ids is None:
+        ids = torch.empty((T, top_k), dtype=torch.int32, device=logits.device)
+    if weights is None:
+        weights = torch.empty((T, top_k), dtype=torch.float32, device=logits.device)
+    _dev(ids, torch.int32, "ids", 2)
+    _dev(weights, torch.float32, "weights", 2)
+    if ids.shape != (T, top_k) or weights.shape != (T, top_k):
+        raise ValueError("ids/weights must be [T, top_k]")
+    _check(lib().route_softmax_topk(_ptr(logits), T, E, int(top_k), int(bool(normalize)), _ptr(ids),
+                                    _ptr(weights), _stream(stream)), "route_softmax_topk")
+    return ids, weights
+
+
+def route_pack_workspace_size(tokens: int, experts: int) -> int:
+    return int(lib().route_pack_workspace_size(int(tokens), int(experts)))
+
+
+def route_pack(topk_ids, experts: int, topk_weights=None, offsets=None, row_ids=None, pair_rows=None,
+               row_weights=None, workspace=None, stream=None):
+    """topk_ids int32 [T, k] -> (offsets int32 [E+1], row_ids int32 [T*k], pair_rows int32 [T, k],
+    row_weights f32 [T*k] or None).  Rows 0 .. offsets[E]-1 of row_ids/row_weights are written."""
+    _dev(topk_ids, torch.int32, "topk_ids", 2)
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    if topk_weights is not None:
+        _dev(topk_weights, torch.float32, "topk_weights", 2)
+        if topk_weights.shape != (T, k):
+            raise ValueError("topk_weights must be [T, k]")
+        if row_weights is None:
+            row_weights = torch.empty(T * k, dtype=torch.float32, device=dev)
+        _dev(row_weights, torch.float32, "row_weights", 1)
+    if offsets is None:
+        offsets = torch.empty(experts + 1, dtype=torch.int32, device=dev)
+    if row_ids is None:
+        row_ids = torch.empty(T * k, dtype=torch.int32, device=dev)
+    if pair_rows is None:
+        pair_rows = torch.empty((T, k), dtype=torch.int32, device=dev)
+    _dev(offsets, torch.int32, "offsets", 1)
+    _dev(row_ids, torch.int32, "row_ids", 1)
+    _dev(pair_rows, torch.int32, "pair_rows", 2)
+    if offsets.shape != (experts + 1,) or row_ids.shape != (T * k,) or pair_rows.shape != (T, k):
+        raise ValueError("offsets must be [E+1], row_ids [T*k], pair_rows [T, k]")
+    if row_weights is not None and row_weights.shape != (T * k,):
+        raise ValueError("row_weights must be [T*k]")
+    need = route_pack_workspace_size(T, experts)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    _dev(workspace, torch.uint8, "workspace")
+    if workspace.numel() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    _check(lib().route_pack(_ptr(topk_ids), _ptr(topk_weights), T, k, int(experts), _ptr(offsets),
+                            _ptr(row_ids), _ptr(pair_rows), _ptr(row_weights), _ptr(workspace),
+                            _stream(stream)), "route_pack")
+    return offsets, row_ids, pair_rows, row_weights
+
+
+def gather_quant_rows(codes, scales, row_ids, out_codes=None, out_scales=None, stream=None):
+    """codes u8 [a_rows, k], scales f32 [a_rows, k/128], row_ids int32 [rows] -> the rows row_ids
+    (zero codes and NaN scales for ids outside [0, a_rows))."""
+    _dev(codes, torch.uint8, "codes", 2)
+    _dev(scales, torch.float32, "scales", 2)
+    _dev(row_ids, torch.int32, "row_ids", 1)
+    a_rows, k = codes.shape
+    rows = row_ids.shape[0]
+    if out_codes is None:
+        out_codes = torch.empty((rows, k), dtype=torch.uint8, device=codes.device)
+    if out_scales is None:
+        out_scales = torch.empty((rows, k // 128), dtype=torch.float32, device=codes.device)
+    _dev(out_codes, torch.uint8, "out_codes", 2)
+    _dev(out_scales, torch.float32, "out_scales", 2)
+    if scales.shape != (a_rows, k // 128) or out_codes.shape != (rows, k) or out_scales.shape != (rows, k // 128):
+        raise ValueError("shape mismatch between codes/scales and the outputs")
+    _check(lib().gather_quant_rows(_ptr(codes), _ptr(scales), a_rows, k, _ptr(row_ids), rows, _ptr(out_codes),
+                                   _ptr(out_scales), _stream(stream)), "gather_quant_rows")
+    return out_codes, out_scales
+
+
+def moe_combine(y, pair_rows, pair_weights=None, out=None, stream=None):
+    """y f32 [R, n] (packed expert outputs), pair_rows int32 [T, k] -> out f32 [T, n] with
+    out[t] = sum_j pair_weights[t, j] * y[pair_rows[t, j]] (weights 1 when None; rows < 0 skipped)."""
+    _dev(y, torch.float32, "y", 2)
+    _dev(pair_rows, torch.int32, "pair_rows", 2)
+    T, k = pair_rows.shape
+    y_rows, n = y.shape
+    if pair_weights is not None:
+        _dev(pair_weights, torch.float32, "pair_weights", 2)
+        if pair_weights.shape != (T, k):
+            raise ValueError("pair_weights must be [T, k]")
+    if out is None:
+        out = torch.empty((T, n), dtype=torch.float32, device=y.device)
+    _dev(out, torch.float32, "out", 2)
+    if out.shape != (T, n):
+        raise ValueError("out must be [T, n]")
+    _check(lib().moe_combine(_ptr(y), y_rows, n, _ptr(pair_rows), _ptr(pair_weights), T, k, _ptr(out),
+                             _stream(stream)), "moe_combine")
     return out

@@ -85,6 +85,81 @@ int swiglu_quant_fp8(const float* gu, const float* row_weights, float limit, uin
                   "swiglu_quant_fp8");
 }
 
+int route_softmax_topk(const float* logits, int32_t tokens, int32_t experts, int32_t top_k, int32_t normalize,
+                       int32_t* topk_ids, float* topk_weights, hipStream_t stream) {
+  const char* what = "route_softmax_topk";
+  if (tokens < 0) return fail(FP4MOE_EINVAL, "%s: tokens = %d < 0", what, (int)tokens);
+  if (experts < 1 || experts > 1024)
+    return fail(FP4MOE_EINVAL, "%s: experts = %d must be in [1, 1024]", what, (int)experts);
+  if (top_k < 1 || top_k > experts || top_k > 64)
+    return fail(FP4MOE_EINVAL, "%s: top_k = %d must be in [1, min(experts, 64)]", what, (int)top_k);
+  if (normalize != 0 && normalize != 1)
+    return fail(FP4MOE_EINVAL, "%s: normalize = %d must be 0 or 1", what, (int)normalize);
+  if ((int64_t)tokens * experts >= kMaxPlaneBytes)
+    return fail(FP4MOE_EINVAL, "%s: tokens x experts must stay below 2^31", what);
+  if (tokens == 0) return ok();
+  if (!logits || !topk_ids || !topk_weights) return fail(FP4MOE_EINVAL, "%s: NULL buffer with tokens > 0", what);
+  return launched(fp4moe::launch_route_topk(logits, tokens, experts, top_k, normalize, topk_ids, topk_weights,
+                                            stream),
+                  what);
+}
+
+int64_t route_pack_workspace_size(int32_t tokens, int32_t experts) {
+  if (tokens <= 0 || experts <= 0) return 0;
+  return 4 * fp4moe::route_pack_workspace_elems(tokens, experts);
+}
+
+int route_pack(const int32_t* topk_ids, const float* topk_weights, int32_t tokens, int32_t top_k, int32_t experts,
+               int32_t* offsets, int32_t* row_ids, int32_t* pair_rows, float* row_weights, void* workspace,
+               hipStream_t stream) {
+  const char* what = "route_pack";
+  if (tokens < 0) return fail(FP4MOE_EINVAL, "%s: tokens = %d < 0", what, (int)tokens);
+  if (top_k < 1 || top_k > 64) return fail(FP4MOE_EINVAL, "%s: top_k = %d must be in [1, 64]", what, (int)top_k);
+  if (experts < 1 || experts > 1024)
+    return fail(FP4MOE_EINVAL, "%s: experts = %d must be in [1, 1024]", what, (int)experts);
+  if ((int64_t)tokens * top_k >= kMaxPlaneBytes)
+    return fail(FP4MOE_EINVAL, "%s: tokens x top_k must stay below 2^31", what);
+  if (!offsets) return fail(FP4MOE_EINVAL, "%s: offsets is NULL", what);
+  if (tokens > 0 && (!topk_ids || !row_ids || !pair_rows || !workspace))
+    return fail(FP4MOE_EINVAL, "%s: NULL buffer with tokens > 0", what);
+  if (reinterpret_cast<uintptr_t>(workspace) & 3) return fail(FP4MOE_EINVAL, "%s: workspace not 4-byte aligned", what);
+  return launched(fp4moe::launch_route_pack(topk_ids, topk_weights, tokens, top_k, experts, offsets, row_ids,
+                                            pair_rows, topk_weights ? row_weights : nullptr,
+                                            static_cast<int32_t*>(workspace), stream),
+                  what);
+}
+
+int gather_quant_rows(const uint8_t* codes, const float* scales, int32_t a_rows, int32_t k, const int32_t* row_ids,
+                      int32_t rows, uint8_t* out_codes, float* out_scales, hipStream_t stream) {
+  const char* what = "gather_quant_rows";
+  if (a_rows < 0 || rows < 0)
+    return fail(FP4MOE_EINVAL, "%s: a_rows = %d, rows = %d must be >= 0", what, (int)a_rows, (int)rows);
+  if (int rc = check_k(k, what)) return rc;
+  if ((int64_t)a_rows * k >= kMaxPlaneBytes || (int64_t)rows * k >= kMaxPlaneBytes)
+    return fail(FP4MOE_EINVAL, "%s: a code plane of 2^31 bytes or more", what);
+  if (rows == 0) return ok();
+  if (!row_ids || !out_codes || !out_scales || (a_rows > 0 && (!codes || !scales)))
+    return fail(FP4MOE_EINVAL, "%s: NULL buffer with rows > 0", what);
+  if ((reinterpret_cast<uintptr_t>(codes) | reinterpret_cast<uintptr_t>(out_codes)) & 15)
+    return fail(FP4MOE_EINVAL, "%s: codes and out_codes must be 16-byte aligned", what);
+  return launched(fp4moe::launch_gather_rows(codes, scales, a_rows, k, row_ids, rows, out_codes, out_scales, stream),
+                  what);
+}
+
+int moe_combine(const float* y, int32_t y_rows, int32_t n, const int32_t* pair_rows, const float* pair_weights,
+                int32_t tokens, int32_t top_k, float* out, hipStream_t stream) {
+  const char* what = "moe_combine";
+  if (tokens < 0 || y_rows < 0)
+    return fail(FP4MOE_EINVAL, "%s: tokens = %d, y_rows = %d must be >= 0", what, (int)tokens, (int)y_rows);
+  if (n <= 0) return fail(FP4MOE_EINVAL, "%s: n = %d must be positive", what, (int)n);
+  if (top_k < 1 || top_k > 64) return fail(FP4MOE_EINVAL, "%s: top_k = %d must be in [1, 64]", what, (int)top_k);
+  if ((int64_t)tokens * n >= kMaxPlaneBytes || (int64_t)y_rows * n >= kMaxPlaneBytes)
+    return fail(FP4MOE_EINVAL, "%s: tokens x n and y_rows x n must stay below 2^31", what);
+  if (tokens == 0) return ok();
+  if (!pair_rows || !out || (y_rows > 0 && !y)) return fail(FP4MOE_EINVAL, "%s: NULL buffer with tokens > 0", what);
+  return launched(fp4moe::launch_combine(y, y_rows, n, pair_rows, pair_weights, tokens, top_k, out, stream), what);
+}
+
 int fp4_expert_gemm(const uint8_t* a_codes, const float* a_scales, const uint8_t* w_packed,
                     const uint8_t* w_scales, float scale2, int32_t kind, float* out, int32_t g,
                     int32_t n, int32_t k, hipStream_t stream) {

@@ -39,6 +39,21 @@ hipError_t launch_swiglu_quant(const float* gu, const float* weights, float limi
                                float* scales, float* h_out, int64_t rows, int32_t inter,
                                hipStream_t stream);
 
+// Routing (route.hip): top-k with softmax weights (experts <= 1024, top_k <= 64); packing of the
+// routed pairs per expert with a workspace of route_pack_workspace_elems int32; the row gather
+// (16-byte aligned codes); the combine of expert outputs in token order.
+hipError_t launch_route_topk(const float* logits, int32_t tokens, int32_t experts, int32_t top_k,
+                             int32_t normalize, int32_t* ids, float* weights, hipStream_t stream);
+int64_t route_pack_workspace_elems(int32_t tokens, int32_t experts);
+hipError_t launch_route_pack(const int32_t* ids, const float* w, int32_t tokens, int32_t top_k,
+                             int32_t experts, int32_t* offsets, int32_t* row_ids, int32_t* pair_rows,
+                             float* row_w, int32_t* workspace, hipStream_t stream);
+hipError_t launch_gather_rows(const uint8_t* codes, const float* scales, int32_t a_rows, int32_t k,
+                              const int32_t* row_ids, int32_t rows, uint8_t* out_codes, float* out_scales,
+                              hipStream_t stream);
+hipError_t launch_combine(const float* y, int32_t y_rows, int32_t n, const int32_t* pair_rows,
+                          const float* w, int32_t tokens, int32_t top_k, float* out, hipStream_t stream);
+
 // Row-streaming kernel for few rows per expert (decode): every expert's weights are read once per
 // pass of 32 rows.
 hipError_t launch_gemm_decode(const GemmArgs& a, hipStream_t stream);

@@ -12,6 +12,9 @@
  *           table of weight addresses).
  *   [GATE]  also: the swiglu_limit saturation cell (the clamp math between the gate/up and the down
  *           projection, and its swiglu call with an optional per-row weight).
+ *   [QWEN]  memra-engine 0.125.0, src/bin/qwen4exp_gpu_gate.rs: the device-router arm (softmax top-k
+ *           over router logits; selected ids and their emitted order exact, weights to a few ulp;
+ *           ties of duplicates across the cut, all-equal rows, underflow).
  *
  * Conventions for every call:
  *   - All pointers are DEVICE pointers unless marked [host].  Buffers are row-major and densely
@@ -127,6 +130,89 @@ FP4MOE_API int fp4_grouped_gemm(const uint8_t* a_codes, const float* a_scales, i
 FP4MOE_API int swiglu_quant_fp8(const float* gu, const float* row_weights, float limit, uint8_t* codes,
                                 float* scales, float* h_out, int32_t rows, int32_t inter,
                                 hipStream_t stream);
+
+/*
+ * route_softmax_topk -- [QWEN: the device-router arm].  For every token t, the top_k experts by
+ * router logit, best first, and their softmax weights:
+ *   ranking: a larger logit first; equal logits (+0 equal to -0) by the lower expert id; NaN below
+ *            every number (NaNs among themselves by id);
+ *   m = the largest logit of the row;  e_x = exp(x - m);
+ *   topk_weights[t, j] = e_{l[t, id_j]} / D, with D = sum of e over all experts of the row, or over
+ *            the top_k selected ones (in selection order) when normalize = 1.
+ *   A row holding a NaN, or whose largest logit is +Inf or every logit -Inf, gets NaN weights.
+ * logits:       f32 [tokens, experts], read only.
+ * topk_ids:     int32 [tokens, top_k], written.   topk_weights: f32 [tokens, top_k], written.
+ * normalize:    [host] 0 or 1.
+ * Selection compares the f32 logits exactly, so the ids and their order are the exact top-k of the
+ * softmax; the weights are f32 (device expf, a tree sum over the row, one division): they agree with
+ * an exact evaluation to a relative 2^-24 (|x - m| + mean |x' - m| + log2(experts) + 6) or so.
+ * Errors: EINVAL if tokens < 0, experts < 1 or > 1024, top_k < 1 or > min(experts, 64), normalize
+ * not 0/1, a pointer NULL while tokens > 0, or tokens*experts >= 2^31.  tokens == 0 is a no-op.
+ */
+FP4MOE_API int route_softmax_topk(const float* logits, int32_t tokens, int32_t experts, int32_t top_k,
+                                  int32_t normalize, int32_t* topk_ids, float* topk_weights,
+                                  hipStream_t stream);
+
+/*
+ * route_pack_workspace_size -- [host] bytes of device workspace route_pack needs for these sizes
+ * (4 x experts x ceil(tokens / 64)); 0 for tokens <= 0 or experts <= 0.
+ */
+FP4MOE_API int64_t route_pack_workspace_size(int32_t tokens, int32_t experts);
+
+/*
+ * route_pack -- [CHECK: f16g grouped GEMM section, rows packed per expert behind CSR offsets].  The
+ * pairs p = t * top_k + j of a routing table are packed per expert: expert e owns the packed rows
+ * offsets[e] .. offsets[e+1]-1, experts in ascending id, and inside one expert the pairs in
+ * ascending (t, j) order, i.e. ascending token order.  Pairs whose id lies outside [0, experts) are
+ * dropped.  The outputs feed fp4_grouped_gemm (row_ids gathers the activation rows, offsets delimits
+ * the experts) and moe_combine (pair_rows).
+ * topk_ids:     int32 [tokens, top_k], read only (ids of one token may repeat; each pair is a row).
+ * topk_weights: f32 [tokens, top_k] or NULL, read only.
+ * offsets:      int32 [experts + 1], written; offsets[experts] = the number of packed rows R.
+ * row_ids:      int32 [tokens * top_k], rows 0 .. R-1 written: the token of each packed row.
+ * pair_rows:    int32 [tokens, top_k], written: the packed row of each pair, -1 if dropped.
+ * row_weights:  f32 [tokens * top_k] or NULL: rows 0 .. R-1 receive topk_weights moved to their
+ *               packed row (ignored when topk_weights is NULL).
+ * workspace:    route_pack_workspace_size(tokens, experts) bytes of device memory, 4-byte aligned,
+ *               overwritten (no initial contents needed).
+ * Errors: EINVAL if tokens < 0, top_k < 1 or > 64, experts < 1 or > 1024, tokens*top_k >= 2^31, or
+ * a required pointer is NULL.  tokens == 0 writes offsets = 0 only.
+ */
+FP4MOE_API int route_pack(const int32_t* topk_ids, const float* topk_weights, int32_t tokens,
+                          int32_t top_k, int32_t experts, int32_t* offsets, int32_t* row_ids,
+                          int32_t* pair_rows, float* row_weights, void* workspace, hipStream_t stream);
+
+/*
+ * gather_quant_rows -- [CHECK: f16g grouped GEMM section; the packed activation rows].  Copies the
+ * act-quant rows row_ids[p] into packed row p: out_codes[p, :] = codes[row_ids[p], :] and
+ * out_scales[p, :] = scales[row_ids[p], :].  A row id outside [0, a_rows) gives zero code bytes and
+ * NaN scales.  fp4_grouped_gemm reads through row_ids itself; this call builds a contiguous copy
+ * (e.g. a send buffer of routed rows).
+ * codes:  u8 [a_rows, k], scales: f32 [a_rows, k/128], read only.  row_ids: int32 [rows].
+ * out_codes: u8 [rows, k], out_scales: f32 [rows, k/128], written.
+ * Errors: EINVAL if a_rows < 0, rows < 0, k <= 0, k % 128 != 0, a required pointer is NULL, codes
+ * or out_codes is not 16-byte aligned, or a_rows*k or rows*k >= 2^31.  rows == 0 is a no-op.
+ */
+FP4MOE_API int gather_quant_rows(const uint8_t* codes, const float* scales, int32_t a_rows, int32_t k,
+                                 const int32_t* row_ids, int32_t rows, uint8_t* out_codes,
+                                 float* out_scales, hipStream_t stream);
+
+/*
+ * moe_combine -- [QWEN: routing; CHECK: packed rows].  The expert outputs back in token order:
+ *   out[t, c] = sum over j < top_k of w[t, j] * y[pair_rows[t, j], c]
+ * added in j order, one f32 fused multiply-add per term (a plain f32 add when pair_weights is NULL,
+ * i.e. w = 1).  Pairs with pair_rows < 0 are skipped; a row at or past y_rows makes the token's whole
+ * output row NaN.  Deterministic: no atomics.
+ * y:            f32 [y_rows, n], read only (e.g. fp4_grouped_gemm's packed output).
+ * pair_rows:    int32 [tokens, top_k], read only (route_pack's output).
+ * pair_weights: f32 [tokens, top_k] or NULL.
+ * out:          f32 [tokens, n], written.
+ * Errors: EINVAL if tokens < 0, y_rows < 0, n <= 0, top_k < 1 or > 64, a required pointer is NULL,
+ * or tokens*n or y_rows*n >= 2^31.  tokens == 0 is a no-op.
+ */
+FP4MOE_API int moe_combine(const float* y, int32_t y_rows, int32_t n, const int32_t* pair_rows,
+                           const float* pair_weights, int32_t tokens, int32_t top_k, float* out,
+                           hipStream_t stream);
 
 /*
  * fp4moe_set_gemm_schedule -- test and benchmark hook (not part of the method).  The GEMM calls

@@ -109,3 +109,68 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(m, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(m.Fp4MoeError):
         m.lib()
+
+
+def test_routing_is_declared():
+    names = declared_functions()
+    for fn in ("route_softmax_topk", "route_pack_workspace_size", "route_pack", "gather_quant_rows",
+               "moe_combine"):
+        assert fn in names
+
+
+@pytest.mark.parametrize("tokens,experts,top_k,normalize", [(-1, 8, 2, 0), (4, 0, 1, 0), (4, 1025, 8, 0),
+                                                            (4, 8, 0, 0), (4, 8, 9, 0), (4, 100, 65, 0),
+                                                            (4, 8, 2, 2), (1 << 22, 1024, 8, 0)])
+def test_route_topk_rejects(lib, tokens, experts, top_k, normalize):
+    assert lib.route_softmax_topk(BAD, tokens, experts, top_k, normalize, BAD, BAD, NULL) == 1
+    assert lib.fp4moe_last_error().decode().startswith("route_softmax_topk")
+
+
+def test_route_topk_null_and_noop(lib):
+    assert lib.route_softmax_topk(NULL, 4, 8, 2, 0, BAD, BAD, NULL) == 1
+    assert lib.route_softmax_topk(NULL, 0, 8, 2, 0, NULL, NULL, NULL) == 0
+
+
+def test_route_pack_workspace_size(lib):
+    assert lib.route_pack_workspace_size(0, 256) == 0
+    assert lib.route_pack_workspace_size(1, 256) == 4 * 256
+    assert lib.route_pack_workspace_size(64, 256) == 4 * 256
+    assert lib.route_pack_workspace_size(65, 256) == 4 * 256 * 2
+    assert lib.route_pack_workspace_size(8192, 256) == 4 * 256 * 128
+
+
+@pytest.mark.parametrize("tokens,top_k,experts", [(-1, 8, 256), (4, 0, 256), (4, 65, 256), (4, 8, 0),
+                                                  (4, 8, 1025), (1 << 26, 64, 8)])
+def test_route_pack_rejects(lib, tokens, top_k, experts):
+    assert lib.route_pack(BAD, NULL, tokens, top_k, experts, BAD, BAD, BAD, NULL, BAD, NULL) == 1
+    assert lib.fp4moe_last_error().decode().startswith("route_pack")
+
+
+def test_route_pack_null_and_alignment(lib):
+    assert lib.route_pack(BAD, NULL, 4, 2, 8, NULL, BAD, BAD, NULL, BAD, NULL) == 1      # offsets
+    assert lib.route_pack(BAD, NULL, 4, 2, 8, BAD, BAD, BAD, NULL, NULL, NULL) == 1      # workspace
+    assert lib.route_pack(BAD, NULL, 4, 2, 8, BAD, BAD, BAD, NULL, ctypes.c_void_p(0x1002), NULL) == 1
+
+
+@pytest.mark.parametrize("a_rows,k,rows", [(-1, 128, 4), (4, 100, 4), (4, 128, -1), (1 << 24, 256, 4)])
+def test_gather_rejects(lib, a_rows, k, rows):
+    assert lib.gather_quant_rows(BAD, BAD, a_rows, k, BAD, rows, BAD, BAD, NULL) == 1
+    assert lib.fp4moe_last_error().decode().startswith("gather_quant_rows")
+
+
+def test_gather_null_alignment_noop(lib):
+    assert lib.gather_quant_rows(BAD, BAD, 4, 128, NULL, 2, BAD, BAD, NULL) == 1
+    assert lib.gather_quant_rows(ctypes.c_void_p(0x1008), BAD, 4, 128, BAD, 2, BAD, BAD, NULL) == 1
+    assert lib.gather_quant_rows(NULL, NULL, 4, 128, NULL, 0, NULL, NULL, NULL) == 0
+
+
+@pytest.mark.parametrize("y_rows,n,tokens,top_k", [(-1, 16, 4, 2), (8, 0, 4, 2), (8, 16, -1, 2),
+                                                   (8, 16, 4, 0), (8, 16, 4, 65), (1 << 20, 4096, 4, 2)])
+def test_combine_rejects(lib, y_rows, n, tokens, top_k):
+    assert lib.moe_combine(BAD, y_rows, n, BAD, NULL, tokens, top_k, BAD, NULL) == 1
+    assert lib.fp4moe_last_error().decode().startswith("moe_combine")
+
+
+def test_combine_null_and_noop(lib):
+    assert lib.moe_combine(BAD, 8, 16, NULL, NULL, 4, 2, BAD, NULL) == 1
+    assert lib.moe_combine(NULL, 0, 16, NULL, NULL, 0, 2, NULL, NULL) == 0

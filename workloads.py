@@ -96,6 +96,7 @@ class GroupedWorkload:
     n: int
     k: int
     extra: dict = field(default_factory=dict)
+    logits: np.ndarray | None = None   # f32 [T, E] router logits the tables were built from
 
     @property
     def E(self): return len(self.kinds)
@@ -221,6 +222,7 @@ def grouped_random(seed: int, T: int, E: int, top: int, n: int, k: int, kinds=No
         logits = -zipf * np.log(ranks)[None, :] + rng.gumbel(size=(T, E))
     else:
         logits = rng.standard_normal((T, E))
+    logits = logits.astype(np.float32)
     for e in empty_experts:
         logits[:, e] = -np.inf
     row_ids, offsets = route_topk(logits, top)
@@ -228,28 +230,51 @@ def grouped_random(seed: int, T: int, E: int, top: int, n: int, k: int, kinds=No
     scale2[kinds == MXFP4] = 0.0
     w_bank, s_bank, w_off, s_off = _bank(rng, kinds, n, k)
     return GroupedWorkload(f"grouped seed={seed} T={T} E={E} top={top} n={n} k={k}", x, row_ids,
-                           offsets, kinds, scale2, w_bank, s_bank, w_off, s_off, n, k)
+                           offsets, kinds, scale2, w_bank, s_bank, w_off, s_off, n, k, logits=logits)
+
+
+def _config3_tokens():
+    rng = rng_for(3)
+    T, E, k = 512, 256, 7168
+    x = rng.standard_normal((T, k), dtype=np.float32)
+    logits = rng.standard_normal((T, E), dtype=np.float32)
+    return rng, x, logits
+
+
+def config3_logits() -> np.ndarray:
+    """The decode workload's router logits alone (f32 [512, 256]), without its weight bank."""
+    return _config3_tokens()[2]
 
 
 def config3() -> GroupedWorkload:
-    rng = rng_for(3)
     T, E, top, n, k = 512, 256, 8, 2048, 7168
-    x = rng.standard_normal((T, k), dtype=np.float32)
-    logits = rng.standard_normal((T, E), dtype=np.float32)
+    rng, x, logits = _config3_tokens()
     row_ids, offsets = route_topk(logits, top)
     kinds = np.zeros(E, dtype=np.int32)
     scale2 = np.array(GROUPED_SCALE2_CHOICES, dtype=np.float32)[rng.integers(0, 4, size=E)]
     w_bank, s_bank, w_off, s_off = _bank(rng, kinds, n, k)
     return GroupedWorkload("config3: grouped NVFP4 decode, 512 tokens, E=256, top-8, k=7168, n=2048",
-                           x, row_ids, offsets, kinds, scale2, w_bank, s_bank, w_off, s_off, n, k)
+                           x, row_ids, offsets, kinds, scale2, w_bank, s_bank, w_off, s_off, n, k,
+                           logits=logits)
+
+
+def _config4_tokens():
+    rng = rng_for(4)
+    T, E, k = 8192, 256, 7168
+    x = rng.standard_t(3, size=(T, k)).astype(np.float32)
+    ranks = rng.permutation(E) + 1
+    logits = (-1.1 * np.log(ranks)[None, :] + rng.gumbel(size=(T, E))).astype(np.float32)
+    return rng, x, logits
+
+
+def config4_logits() -> np.ndarray:
+    """The prefill workload's Zipf(1.1) router logits alone (f32 [8192, 256]), without its bank."""
+    return _config4_tokens()[2]
 
 
 def config4() -> GroupedWorkload:
-    rng = rng_for(4)
     T, E, top, n, k = 8192, 256, 8, 4096, 7168
-    x = rng.standard_t(3, size=(T, k)).astype(np.float32)
-    ranks = rng.permutation(E) + 1
-    logits = -1.1 * np.log(ranks)[None, :] + rng.gumbel(size=(T, E))
+    rng, x, logits = _config4_tokens()
     row_ids, offsets = route_topk(logits, top)
     kinds = np.zeros(E, dtype=np.int32)
     kinds[E - 1] = MXFP4
@@ -258,7 +283,8 @@ def config4() -> GroupedWorkload:
     w_bank, s_bank, w_off, s_off = _bank(rng, kinds, n, k)
     return GroupedWorkload("config4: grouped prefill, 8192 tokens, E=256 (255 NVFP4 + 1 MXFP4), "
                            "Zipf(1.1) top-8, k=7168, n=4096, Student-t(3)",
-                           x, row_ids, offsets, kinds, scale2, w_bank, s_bank, w_off, s_off, n, k)
+                           x, row_ids, offsets, kinds, scale2, w_bank, s_bank, w_off, s_off, n, k,
+                           logits=logits)
 
 
 @dataclass
@@ -275,6 +301,7 @@ class ExpertChainWorkload:
     limit: float
     up: GroupedWorkload            # gate/up projection (shares x, row_ids, offsets)
     down: GroupedWorkload          # down projection (its x is unused: it consumes the activation)
+    logits: np.ndarray | None = None   # f32 [T, E] router logits the tables were built from
 
     @property
     def R(self): return int(self.offsets[-1])
@@ -299,6 +326,7 @@ def expert_chain(seed: int, T: int, E: int, top: int, hidden: int, inter: int, k
         logits = -zipf * np.log(ranks)[None, :] + rng.gumbel(size=(T, E))
     else:
         logits = rng.standard_normal((T, E))
+    logits = logits.astype(np.float32)
     row_ids, offsets = route_topk(logits, top)
     route_w = rng.uniform(0.05, 1.0, size=int(offsets[-1])).astype(np.float32)
     banks = []
@@ -311,7 +339,7 @@ def expert_chain(seed: int, T: int, E: int, top: int, hidden: int, inter: int, k
                                      w_bank, s_bank, w_off, s_off, n, k))
     return ExpertChainWorkload(f"expert chain seed={seed} T={T} E={E} top={top} hidden={hidden} "
                                f"inter={inter} x_scale={x_scale}", x, row_ids, offsets, route_w, kinds,
-                               float(limit), banks[0], banks[1])
+                               float(limit), banks[0], banks[1], logits)
 
 
 def config4_chain() -> ExpertChainWorkload:
@@ -329,4 +357,4 @@ def config4_chain() -> ExpertChainWorkload:
     route_w = rng.uniform(0.05, 1.0, size=up.R).astype(np.float32)
     return ExpertChainWorkload("config4 expert layer: gate/up (n=4096, k=7168) -> swiglu limit 7 -> "
                                "down (n=7168, k=2048); 8192 tokens, E=256, Zipf(1.1) top-8",
-                               up.x, up.row_ids, up.offsets, route_w, up.kinds, 7.0, up, down)
+                               up.x, up.row_ids, up.offsets, route_w, up.kinds, 7.0, up, down, up.logits)
