@@ -130,7 +130,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="config3", choices=["config3", "config4", "chain4"],
                     help="config3: grouped decode GEMM; config4: grouped prefill GEMM; chain4: the "
-                         "whole prefill expert layer (gate/up GEMM -> swiglu+quant -> down GEMM)")
+                         "whole prefill expert layer from router logits (top-k, packing, gate/up GEMM, "
+                         "swiglu+quant, down GEMM, combine)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 disables it)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -263,43 +264,58 @@ def upload_bank(gw, torch, dev):
 
 
 def run_chain(args, torch, fp4, dev):
-    """The whole prefill expert layer: act_quant -> gate/up grouped GEMM -> swiglu_quant ->
-    down grouped GEMM.  value = TFLOP/s of the two GEMMs over the step; the roofline is the
-    dominant kernel's (the gate/up GEMM); the activation kernel's HBM rate is reported beside it."""
+    """The whole prefill expert layer from router logits to the combined output: route_softmax_topk
+    -> route_pack -> act_quant -> gate/up grouped GEMM -> swiglu_quant (x routing weight) -> down
+    grouped GEMM -> moe_combine.  value = TFLOP/s of the two GEMMs over the whole step; the roofline
+    is the dominant kernel's (the gate/up GEMM); every other launch's time is reported beside it."""
     t0 = time.perf_counter()
     ch = workloads.config4_chain()
     log(f"workload: {ch.name}  (generated in {time.perf_counter() - t0:.1f} s)")
+    E, top = len(ch.kinds), 8
+    logits = torch.from_numpy(ch.logits).to(dev)
     x = torch.from_numpy(ch.x).to(dev)
-    row_ids = torch.from_numpy(ch.row_ids).to(dev)
-    offsets = torch.from_numpy(ch.offsets).to(dev)
     kinds = torch.from_numpy(ch.kinds).to(dev)
-    rw = torch.from_numpy(ch.route_w).to(dev)
     up = upload_bank(ch.up, torch, dev)
     dn = upload_bank(ch.down, torch, dev)
     T, Hd = ch.x.shape
-    R, I = ch.R, ch.inter
+    R, I = T * top, ch.inter
+    ids = torch.empty((T, top), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, top), dtype=torch.float32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    row_ids = torch.empty(R, dtype=torch.int32, device=dev)
+    pair_rows = torch.empty((T, top), dtype=torch.int32, device=dev)
+    rw = torch.empty(R, dtype=torch.float32, device=dev)
+    ws = torch.empty(fp4.route_pack_workspace_size(T, E), dtype=torch.uint8, device=dev)
     codes = torch.empty((T, Hd), dtype=torch.uint8, device=dev)
     scales = torch.empty((T, Hd // 128), dtype=torch.float32, device=dev)
     gu = torch.empty((R, 2 * I), dtype=torch.float32, device=dev)
     hc = torch.empty((R, I), dtype=torch.uint8, device=dev)
     hs = torch.empty((R, I // 128), dtype=torch.float32, device=dev)
     y = torch.empty((R, Hd), dtype=torch.float32, device=dev)
+    out = torch.empty((T, Hd), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    names = ["route_topk", "route_pack", "act_quant", "gate/up GEMM", "swiglu+quant", "down GEMM", "combine"]
 
     def launches():
+        yield lambda: fp4.route_softmax_topk(logits, top, ids=ids, weights=tw, stream=stream)
+        yield lambda: fp4.route_pack(ids, E, tw, offsets, row_ids, pair_rows, rw, ws, stream=stream)
         yield lambda: fp4.act_quant_fp8(x, codes, scales, stream=stream)
         yield lambda: fp4.fp4_grouped_gemm(codes, scales, row_ids, offsets, up[2], up[3], kinds, up[4],
                                            2 * I, out=gu, stream=stream)
         yield lambda: fp4.swiglu_quant_fp8(gu, ch.limit, row_weights=rw, codes=hc, scales=hs, stream=stream)
         yield lambda: fp4.fp4_grouped_gemm(hc, hs, None, offsets, dn[2], dn[3], kinds, dn[4], Hd, out=y,
                                            stream=stream)
+        yield lambda: fp4.moe_combine(y, pair_rows, out=out, stream=stream)
 
     for _ in range(args.warmup):
         for f in launches():
             f()
     torch.cuda.synchronize()
-    K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    if not (torch.equal(offsets.cpu(), torch.from_numpy(ch.offsets))
+            and torch.equal(row_ids.cpu(), torch.from_numpy(ch.row_ids))):
+        raise SystemExit("device routing tables differ from the workload's")
+    K, L = args.steps, len(names)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(L + 1)] for _ in range(K)]
     wall0 = time.perf_counter()
     for i in range(K):
         ev[i][0].record(stream)
@@ -308,27 +324,28 @@ def run_chain(args, torch, fp4, dev):
             ev[i][j + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    step_ms = ev[0][0].elapsed_time(ev[K - 1][4]) / K
-    part = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev])) for j in range(4)]
+    step_ms = ev[0][0].elapsed_time(ev[K - 1][L]) / K
+    part = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev])) for j in range(L)]
     f_up, f_dn = 2.0 * R * Hd * 2 * I, 2.0 * R * I * Hd
     sw_bytes = R * I * (8 + 1) + R * (I // 128) * 4 + R * 4
-    log(f"timed {K} steps: wall {wall * 1e3 / K:.3f} ms/step, events {step_ms:.3f} ms/step "
-        f"(act_quant {part[0] * 1e3:.1f} us, gate/up GEMM {part[1] * 1e3:.1f} us, swiglu+quant "
-        f"{part[2] * 1e3:.1f} us, down GEMM {part[3] * 1e3:.1f} us)")
-    tf_up = f_up / (part[1] * 1e-3) / 1e12
-    sw_gbs = sw_bytes / (part[2] * 1e-3) / 1e9
-    log(f"gate/up {tf_up:.1f} TFLOP/s, down {f_dn / (part[3] * 1e-3) / 1e12:.1f} TFLOP/s, swiglu+quant "
-        f"{sw_gbs:.0f} GB/s ({sw_gbs / HBM_PEAK_GBS:.1%} of 8 TB/s)")
+    cb_bytes = R * Hd * 4 + T * Hd * 4 + T * top * 4
+    log(f"timed {K} steps: wall {wall * 1e3 / K:.3f} ms/step, events {step_ms:.3f} ms/step")
+    log("  " + ", ".join(f"{n} {p * 1e3:.1f} us" for n, p in zip(names, part)))
+    tf_up = f_up / (part[3] * 1e-3) / 1e12
+    sw_gbs = sw_bytes / (part[4] * 1e-3) / 1e9
+    cb_gbs = cb_bytes / (part[6] * 1e-3) / 1e9
+    log(f"gate/up {tf_up:.1f} TFLOP/s, down {f_dn / (part[5] * 1e-3) / 1e12:.1f} TFLOP/s, swiglu+quant "
+        f"{sw_gbs:.0f} GB/s ({sw_gbs / HBM_PEAK_GBS:.1%} of 8 TB/s), combine {cb_gbs:.0f} GB/s "
+        f"({cb_gbs / HBM_PEAK_GBS:.1%})")
     value = (f_up + f_dn) / (step_ms * 1e-3) / 1e12
     result = {
         "metric": METRIC, "value": round(value, 4), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8xfp4->f32", "data": "synthetic",
-        "config": {"workload": ch.name, "tokens": int(T), "experts": int(len(ch.kinds)), "top_k": 8,
+        "config": {"workload": ch.name, "tokens": int(T), "experts": int(E), "top_k": top,
                    "routed_rows": int(R), "hidden": int(Hd), "inter": int(I),
-                   "gateup_gemm_us": round(part[1] * 1e3, 2), "swiglu_quant_us": round(part[2] * 1e3, 2),
-                   "down_gemm_us": round(part[3] * 1e3, 2), "act_quant_us": round(part[0] * 1e3, 2),
-                   "swiglu_quant_gbs": round(sw_gbs, 1)},
+                   "us": {n: round(p * 1e3, 2) for n, p in zip(names, part)},
+                   "swiglu_quant_gbs": round(sw_gbs, 1), "combine_gbs": round(cb_gbs, 1)},
         "roofline": {"bound": "mfma", "achieved": round(tf_up, 1), "peak": MFMA_PEAK_TFLOPS["f16"],
                      "unit": "TFLOP/s", "frac": round(tf_up / MFMA_PEAK_TFLOPS["f16"], 4), "traffic": None},
         "cpu_baseline": None,

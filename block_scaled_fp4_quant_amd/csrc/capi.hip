@@ -95,8 +95,8 @@ int route_softmax_topk(const float* logits, int32_t tokens, int32_t experts, int
     return fail(FP4MOE_EINVAL, "%s: top_k = %d must be in [1, min(experts, 64)]", what, (int)top_k);
   if (normalize != 0 && normalize != 1)
     return fail(FP4MOE_EINVAL, "%s: normalize = %d must be 0 or 1", what, (int)normalize);
-  if ((int64_t)tokens * experts >= kMaxPlaneBytes)
-    return fail(FP4MOE_EINVAL, "%s: tokens x experts must stay below 2^31", what);
+  if ((int64_t)tokens * experts * 4 >= kMaxPlaneBytes)
+    return fail(FP4MOE_EINVAL, "%s: the logits plane must stay below 2^31 bytes", what);
   if (tokens == 0) return ok();
   if (!logits || !topk_ids || !topk_weights) return fail(FP4MOE_EINVAL, "%s: NULL buffer with tokens > 0", what);
   return launched(fp4moe::launch_route_topk(logits, tokens, experts, top_k, normalize, topk_ids, topk_weights,
@@ -105,7 +105,7 @@ int route_softmax_topk(const float* logits, int32_t tokens, int32_t experts, int
 }
 
 int64_t route_pack_workspace_size(int32_t tokens, int32_t experts) {
-  if (tokens <= 0 || experts <= 0) return 0;
+  if (tokens < 0 || experts <= 0) return 0;
   return 4 * fp4moe::route_pack_workspace_elems(tokens, experts);
 }
 
@@ -119,8 +119,8 @@ int route_pack(const int32_t* topk_ids, const float* topk_weights, int32_t token
     return fail(FP4MOE_EINVAL, "%s: experts = %d must be in [1, 1024]", what, (int)experts);
   if ((int64_t)tokens * top_k >= kMaxPlaneBytes)
     return fail(FP4MOE_EINVAL, "%s: tokens x top_k must stay below 2^31", what);
-  if (!offsets) return fail(FP4MOE_EINVAL, "%s: offsets is NULL", what);
-  if (tokens > 0 && (!topk_ids || !row_ids || !pair_rows || !workspace))
+  if (!offsets || !workspace) return fail(FP4MOE_EINVAL, "%s: offsets or workspace is NULL", what);
+  if (tokens > 0 && (!topk_ids || !row_ids || !pair_rows))
     return fail(FP4MOE_EINVAL, "%s: NULL buffer with tokens > 0", what);
   if (reinterpret_cast<uintptr_t>(workspace) & 3) return fail(FP4MOE_EINVAL, "%s: workspace not 4-byte aligned", what);
   return launched(fp4moe::launch_route_pack(topk_ids, topk_weights, tokens, top_k, experts, offsets, row_ids,

@@ -147,15 +147,15 @@ FP4MOE_API int swiglu_quant_fp8(const float* gu, const float* row_weights, float
  * softmax; the weights are f32 (device expf, a tree sum over the row, one division): they agree with
  * an exact evaluation to a relative 2^-24 (|x - m| + mean |x' - m| + log2(experts) + 6) or so.
  * Errors: EINVAL if tokens < 0, experts < 1 or > 1024, top_k < 1 or > min(experts, 64), normalize
- * not 0/1, a pointer NULL while tokens > 0, or tokens*experts >= 2^31.  tokens == 0 is a no-op.
+ * not 0/1, a pointer NULL while tokens > 0, or 4*tokens*experts >= 2^31.  tokens == 0 is a no-op.
  */
 FP4MOE_API int route_softmax_topk(const float* logits, int32_t tokens, int32_t experts, int32_t top_k,
                                   int32_t normalize, int32_t* topk_ids, float* topk_weights,
                                   hipStream_t stream);
 
 /*
- * route_pack_workspace_size -- [host] bytes of device workspace route_pack needs for these sizes
- * (4 x experts x ceil(tokens / 64)); 0 for tokens <= 0 or experts <= 0.
+ * route_pack_workspace_size -- [host] bytes of device workspace route_pack needs for these sizes:
+ * 4 x experts x (ceil(tokens / 64) + 1); 0 for tokens < 0 or experts <= 0.
  */
 FP4MOE_API int64_t route_pack_workspace_size(int32_t tokens, int32_t experts);
 
@@ -176,7 +176,8 @@ FP4MOE_API int64_t route_pack_workspace_size(int32_t tokens, int32_t experts);
  * workspace:    route_pack_workspace_size(tokens, experts) bytes of device memory, 4-byte aligned,
  *               overwritten (no initial contents needed).
  * Errors: EINVAL if tokens < 0, top_k < 1 or > 64, experts < 1 or > 1024, tokens*top_k >= 2^31, or
- * a required pointer is NULL.  tokens == 0 writes offsets = 0 only.
+ * a required pointer is NULL (offsets and workspace always; the others when tokens > 0).
+ * tokens == 0 writes offsets = 0 only.
  */
 FP4MOE_API int route_pack(const int32_t* topk_ids, const float* topk_weights, int32_t tokens,
                           int32_t top_k, int32_t experts, int32_t* offsets, int32_t* row_ids,

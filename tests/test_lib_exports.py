@@ -132,11 +132,12 @@ def test_route_topk_null_and_noop(lib):
 
 
 def test_route_pack_workspace_size(lib):
-    assert lib.route_pack_workspace_size(0, 256) == 0
-    assert lib.route_pack_workspace_size(1, 256) == 4 * 256
-    assert lib.route_pack_workspace_size(64, 256) == 4 * 256
-    assert lib.route_pack_workspace_size(65, 256) == 4 * 256 * 2
-    assert lib.route_pack_workspace_size(8192, 256) == 4 * 256 * 128
+    assert lib.route_pack_workspace_size(-1, 256) == 0
+    assert lib.route_pack_workspace_size(0, 256) == 4 * 256
+    assert lib.route_pack_workspace_size(1, 256) == 4 * 256 * 2
+    assert lib.route_pack_workspace_size(64, 256) == 4 * 256 * 2
+    assert lib.route_pack_workspace_size(65, 256) == 4 * 256 * 3
+    assert lib.route_pack_workspace_size(8192, 256) == 4 * 256 * 129
 
 
 @pytest.mark.parametrize("tokens,top_k,experts", [(-1, 8, 256), (4, 0, 256), (4, 65, 256), (4, 8, 0),
@@ -149,6 +150,7 @@ def test_route_pack_rejects(lib, tokens, top_k, experts):
 def test_route_pack_null_and_alignment(lib):
     assert lib.route_pack(BAD, NULL, 4, 2, 8, NULL, BAD, BAD, NULL, BAD, NULL) == 1      # offsets
     assert lib.route_pack(BAD, NULL, 4, 2, 8, BAD, BAD, BAD, NULL, NULL, NULL) == 1      # workspace
+    assert lib.route_pack(NULL, NULL, 0, 2, 8, BAD, NULL, NULL, NULL, NULL, NULL) == 1   # even empty
     assert lib.route_pack(BAD, NULL, 4, 2, 8, BAD, BAD, BAD, NULL, ctypes.c_void_p(0x1002), NULL) == 1
 
 

@@ -343,9 +343,10 @@ def expert_chain(seed: int, T: int, E: int, top: int, hidden: int, inter: int, k
 
 
 def config4_chain() -> ExpertChainWorkload:
-    """The grouped prefill layer as a whole expert chain: config4's tokens, routing and fused
-    gate/up bank (n = 4096 = 2 x 2048, k = 7168), plus a down projection bank (n = 7168, k = 2048)
-    in the same formats (255 NVFP4 + 1 MXFP4), routing weights uniform in [0.05, 1], limit 7."""
+    """The grouped prefill layer as a whole expert chain: config4's tokens, router logits, routing and
+    fused gate/up bank (n = 4096 = 2 x 2048, k = 7168), plus a down projection bank (n = 7168,
+    k = 2048) in the same formats (255 NVFP4 + 1 MXFP4), limit 7.  route_w (uniform in [0.05, 1]) is
+    a stand-in per-row weight; a run that routes on the device takes the softmax weights instead."""
     up = config4()
     rng = rng_for(4, 1)
     inter = up.n // 2
