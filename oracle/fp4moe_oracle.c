@@ -470,3 +470,64 @@ void or_gather_rows(const uint8_t* codes, const float* scales, int64_t a_rows, i
         for (int64_t q = 0; q < nq; ++q) out_scales[p * nq + q] = ok ? scales[r * nq + q] : NAN;
     }
 }
+
+/* ---------------------------------------------------------------------------------------------
+ * The bf16-dequant rung [GATE: comparison 3 -- the unquantized activations converted to bf16, the
+ * expert weights dequantized to bf16, a bf16 GEMM with f32 output; the class shift of the native
+ * path against it].  Readings where the page is silent (it prints the calls, not the kernels):
+ *   - f32 -> bf16 rounds to nearest, ties to even; NaN stays NaN (sign and top payload bits kept,
+ *     quiet bit set);
+ *   - a weight's rung value is the f32 product E2M1 x ws (ws as in the GEMM), rounded to bf16;
+ *   - the bf16 GEMM sums the exact products of the bf16 values (here in f64).
+ * ------------------------------------------------------------------------------------------- */
+
+uint16_t or_bf16_bits(float x) {
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    if (isnan(x)) return (uint16_t)((u >> 16) | 0x0040u);
+    const uint32_t lower = u & 0xFFFFu, upper = u >> 16;
+    /* round to nearest; on an exact tie keep the even upper half */
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u))) return (uint16_t)(upper + 1u);
+    return (uint16_t)upper;
+}
+
+double or_bf16_value(uint16_t b) {
+    const uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+void or_cvt_bf16(const float* x, int64_t count, uint16_t* out) {
+    for (int64_t i = 0; i < count; ++i) out[i] = or_bf16_bits(x[i]);
+}
+
+void or_dequant_bf16(const uint8_t* w, const uint8_t* s, float scale2, int kind, int64_t n, int64_t k,
+                     uint16_t* out) {
+    const int64_t gs = (kind == OR_NVFP4) ? 16 : 32;
+    for (int64_t c = 0; c < n; ++c)
+        for (int64_t kk = 0; kk < k; ++kk) {
+            const uint8_t byte = w[c * (k / 2) + (kk >> 1)];
+            const unsigned code = (kk & 1) ? (byte >> 4) : (byte & 0x0Fu);
+            const float ws = (float)weight_scale(kind, s[c * (k / gs) + kk / gs], scale2);
+            const float v = (float)or_e2m1_value(code) * ws;
+            out[c * k + kk] = or_bf16_bits(v);
+        }
+}
+
+/* out[r, c] = sum over k of bf16(a[r, k]) * bf16(w[c, k]) in f64 (every product exact), and abs_out
+ * the sum of magnitudes. */
+void or_gemm_bf16(const uint16_t* a, const uint16_t* w, int64_t m, int64_t n, int64_t k, double* out,
+                  double* abs_out) {
+    for (int64_t r = 0; r < m; ++r)
+        for (int64_t c = 0; c < n; ++c) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t kk = 0; kk < k; ++kk) {
+                const double p = or_bf16_value(a[r * k + kk]) * or_bf16_value(w[c * k + kk]);
+                acc += p;
+                mag += fabs(p);
+            }
+            out[r * n + c] = acc;
+            abs_out[r * n + c] = mag;
+        }
+}

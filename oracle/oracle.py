@@ -87,6 +87,12 @@ def _load():
             lib.or_combine.argtypes = [P, I64, I64, P, P, I64, I64, P, P]
             lib.or_gather_rows.restype = None
             lib.or_gather_rows.argtypes = [P, P, I64, I64, P, I64, P, P]
+            lib.or_cvt_bf16.restype = None
+            lib.or_cvt_bf16.argtypes = [P, I64, P]
+            lib.or_dequant_bf16.restype = None
+            lib.or_dequant_bf16.argtypes = [P, P, ctypes.c_float, ctypes.c_int, I64, I64, P]
+            lib.or_gemm_bf16.restype = None
+            lib.or_gemm_bf16.argtypes = [P, P, I64, I64, I64, P, P]
             _lib = lib
     return _lib
 
@@ -380,3 +386,55 @@ def gather_rows(codes, scales, row_ids):
     osc = np.empty((rows, k // 128), dtype=np.float32)
     _load().or_gather_rows(pc, ps, a_rows, k, pr, rows, oc.ctypes.data, osc.ctypes.data)
     return oc, osc
+
+
+# --------------------------------------------------------------------------- the bf16-dequant rung
+
+U_FP8 = 2.0 ** -4   # unit roundoff of E4M3 (3 mantissa bits, round to nearest)
+
+
+def cvt_bf16(x) -> np.ndarray:
+    """f32 -> bf16 bit patterns (uint16), round to nearest even; NaN stays NaN."""
+    x, px = _c(x, np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().or_cvt_bf16(px, x.size, out.ctypes.data)
+    return out
+
+
+def bf16_value(b) -> np.ndarray:
+    """Values (f64) of bf16 bit patterns."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def dequant_bf16(w, s, scale2, kind) -> np.ndarray:
+    """The rung's bf16 weights [n, k] (uint16 bit patterns): bf16(f32(E2M1 x ws))."""
+    w, pw = _c(w, np.uint8)
+    s, ps = _c(s, np.uint8)
+    n, k = w.shape[0], w.shape[1] * 2
+    _check_expert(w, s, kind, n, k)
+    out = np.empty((n, k), dtype=np.uint16)
+    _load().or_dequant_bf16(pw, ps, float(np.float32(scale2)), int(kind), n, k, out.ctypes.data)
+    return out
+
+
+def gemm_bf16(a, w):
+    """out[r, c] = sum_k a[r, k] w[c, k] over bf16 bit patterns, in f64; and the magnitude sums."""
+    a, pa = _c(a, np.uint16)
+    w, pw = _c(w, np.uint16)
+    m, k = a.shape
+    n = w.shape[0]
+    if w.shape[1] != k:
+        raise ValueError("a and w must share k")
+    out = np.empty((m, n), dtype=np.float64)
+    absout = np.empty((m, n), dtype=np.float64)
+    _load().or_gemm_bf16(pa, pw, m, n, k, out.ctypes.data, absout.ctypes.data)
+    return out, absout
+
+
+def class_shift_prediction(x, wd) -> np.ndarray:
+    """(U_FP8 / sqrt(3)) * ||x (.) w||_2 per output: x f32 [m, k] (unquantized activations), wd f64
+    [n, k] (dequantized weights).  The RMS of the shift that act-quant rounding errors, uniform in
+    +-U_FP8 relative and independent across k, would cause."""
+    x = np.asarray(x, dtype=np.float64)
+    return U_FP8 / np.sqrt(3.0) * np.sqrt((x * x) @ (np.asarray(wd, dtype=np.float64) ** 2).T)
