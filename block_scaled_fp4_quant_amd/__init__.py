@@ -53,6 +53,12 @@ def lib() -> ctypes.CDLL:
         L.gather_quant_rows.restype = ctypes.c_int
         L.moe_combine.argtypes = [P, I32, I32, P, P, I32, I32, P, P]
         L.moe_combine.restype = ctypes.c_int
+        L.cvt_bf16.argtypes = [P, P, ctypes.c_int64, P]
+        L.cvt_bf16.restype = ctypes.c_int
+        L.fp4_dequant_bf16.argtypes = [P, P, F32, I32, I32, I32, P, P]
+        L.fp4_dequant_bf16.restype = ctypes.c_int
+        L.gemm_bf16.argtypes = [P, P, P, I32, I32, I32, P]
+        L.gemm_bf16.restype = ctypes.c_int
         L.fp4moe_last_error.argtypes = []
         L.fp4moe_last_error.restype = ctypes.c_char_p
         L.fp4moe_version.argtypes = []
@@ -314,4 +320,52 @@ def moe_combine(y, pair_rows, pair_weights=None, out=None, stream=None):
         raise ValueError("out must be [T, n]")
     _check(lib().moe_combine(_ptr(y), y_rows, n, _ptr(pair_rows), _ptr(pair_weights), T, k, _ptr(out),
                              _stream(stream)), "moe_combine")
+    return out
+
+
+# --------------------------------------------------------------------------- the bf16-dequant rung
+
+def cvt_bf16(x, out=None, stream=None):
+    """f32 tensor -> bf16 tensor of the same shape (round to nearest even)."""
+    _dev(x, torch.float32, "x")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    _dev(out, torch.bfloat16, "out")
+    if out.shape != x.shape:
+        raise ValueError("out must have x's shape")
+    _check(lib().cvt_bf16(_ptr(x), _ptr(out), x.numel(), _stream(stream)), "cvt_bf16")
+    return out
+
+
+def fp4_dequant_bf16(w_packed, w_scales, scale2: float, kind: int, out=None, stream=None):
+    """Expert weights u8 [n, k/2] + scales u8 [n, k/gs] -> bf16 [n, k] (the rung's weights)."""
+    _dev(w_packed, torch.uint8, "w_packed", 2)
+    _dev(w_scales, torch.uint8, "w_scales", 2)
+    n, k = w_packed.shape[0], w_packed.shape[1] * 2
+    if w_scales.shape != (n, k // GROUP_SIZE[int(kind)]):
+        raise ValueError("w_scales shape does not match w_packed and kind")
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.bfloat16, device=w_packed.device)
+    _dev(out, torch.bfloat16, "out", 2)
+    if out.shape != (n, k):
+        raise ValueError("out must be [n, k]")
+    _check(lib().fp4_dequant_bf16(_ptr(w_packed), _ptr(w_scales), float(scale2), int(kind), n, k, _ptr(out),
+                                  _stream(stream)), "fp4_dequant_bf16")
+    return out
+
+
+def gemm_bf16(a, w, out=None, stream=None):
+    """a bf16 [m, k], w bf16 [n, k] -> out f32 [m, n] = a w^T (f32 accumulation)."""
+    _dev(a, torch.bfloat16, "a", 2)
+    _dev(w, torch.bfloat16, "w", 2)
+    m, k = a.shape
+    n = w.shape[0]
+    if w.shape[1] != k:
+        raise ValueError("a and w must share k")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=a.device)
+    _dev(out, torch.float32, "out", 2)
+    if out.shape != (m, n):
+        raise ValueError("out must be [m, n]")
+    _check(lib().gemm_bf16(_ptr(a), _ptr(w), _ptr(out), m, n, k, _stream(stream)), "gemm_bf16")
     return out

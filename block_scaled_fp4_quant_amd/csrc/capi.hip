@@ -160,6 +160,39 @@ int moe_combine(const float* y, int32_t y_rows, int32_t n, const int32_t* pair_r
   return launched(fp4moe::launch_combine(y, y_rows, n, pair_rows, pair_weights, tokens, top_k, out, stream), what);
 }
 
+int cvt_bf16(const float* x, uint16_t* out, int64_t count, hipStream_t stream) {
+  if (count < 0) return fail(FP4MOE_EINVAL, "cvt_bf16: count = %lld < 0", (long long)count);
+  if (count == 0) return ok();
+  if (!x || !out) return fail(FP4MOE_EINVAL, "cvt_bf16: NULL buffer with count > 0");
+  return launched(fp4moe::launch_cvt_bf16(x, out, count, stream), "cvt_bf16");
+}
+
+int fp4_dequant_bf16(const uint8_t* w_packed, const uint8_t* w_scales, float scale2, int32_t kind, int32_t n,
+                     int32_t k, uint16_t* out, hipStream_t stream) {
+  const char* what = "fp4_dequant_bf16";
+  if (n < 0) return fail(FP4MOE_EINVAL, "%s: n = %d < 0", what, (int)n);
+  if (int rc = check_k(k, what)) return rc;
+  if (kind != FP4MOE_NVFP4 && kind != FP4MOE_MXFP4)
+    return fail(FP4MOE_EINVAL, "%s: kind = %d is neither 0 (NVFP4) nor 1 (MXFP4)", what, (int)kind);
+  if ((int64_t)n * k * 2 >= kMaxPlaneBytes) return fail(FP4MOE_EINVAL, "%s: n x k bf16 values reach 2^31 bytes", what);
+  if (n == 0) return ok();
+  if (!w_packed || !w_scales || !out) return fail(FP4MOE_EINVAL, "%s: NULL buffer with n > 0", what);
+  if (reinterpret_cast<uintptr_t>(out) & 15) return fail(FP4MOE_EINVAL, "%s: out must be 16-byte aligned", what);
+  if (reinterpret_cast<uintptr_t>(w_packed) & 3) return fail(FP4MOE_EINVAL, "%s: w_packed must be 4-byte aligned", what);
+  return launched(fp4moe::launch_dequant_bf16(w_packed, w_scales, scale2, kind, n, k, out, stream), what);
+}
+
+int gemm_bf16(const uint16_t* a, const uint16_t* w, float* out, int32_t m, int32_t n, int32_t k, hipStream_t stream) {
+  const char* what = "gemm_bf16";
+  if (m < 0 || n <= 0) return fail(FP4MOE_EINVAL, "%s: m = %d must be >= 0 and n = %d > 0", what, (int)m, (int)n);
+  if (k <= 0 || k % 16 != 0) return fail(FP4MOE_EINVAL, "%s: k = %d must be a positive multiple of 16", what, (int)k);
+  if ((int64_t)m * k * 2 >= kMaxPlaneBytes || (int64_t)n * k * 2 >= kMaxPlaneBytes)
+    return fail(FP4MOE_EINVAL, "%s: an operand of 2^31 bytes or more", what);
+  if (m == 0) return ok();
+  if (!a || !w || !out) return fail(FP4MOE_EINVAL, "%s: NULL buffer with m > 0", what);
+  return launched(fp4moe::launch_gemm_bf16(a, w, out, m, n, k, stream), what);
+}
+
 int fp4_expert_gemm(const uint8_t* a_codes, const float* a_scales, const uint8_t* w_packed,
                     const uint8_t* w_scales, float scale2, int32_t kind, float* out, int32_t g,
                     int32_t n, int32_t k, hipStream_t stream) {

@@ -54,6 +54,14 @@ hipError_t launch_gather_rows(const uint8_t* codes, const float* scales, int32_t
 hipError_t launch_combine(const float* y, int32_t y_rows, int32_t n, const int32_t* pair_rows,
                           const float* w, int32_t tokens, int32_t top_k, float* out, hipStream_t stream);
 
+// The bf16-dequant rung (rung.hip): f32 -> bf16, FP4 weights -> bf16 (k % 128 == 0), and a plain
+// bf16 GEMM out = a * w^T with f32 accumulation (k % 16 == 0).
+hipError_t launch_cvt_bf16(const float* x, uint16_t* out, int64_t count, hipStream_t stream);
+hipError_t launch_dequant_bf16(const uint8_t* w, const uint8_t* s, float scale2, int32_t kind, int32_t n,
+                               int32_t k, uint16_t* out, hipStream_t stream);
+hipError_t launch_gemm_bf16(const uint16_t* a, const uint16_t* w, float* out, int32_t m, int32_t n, int32_t k,
+                            hipStream_t stream);
+
 // Row-streaming kernel for few rows per expert (decode): every expert's weights are read once per
 // pass of 32 rows.
 hipError_t launch_gemm_decode(const GemmArgs& a, hipStream_t stream);

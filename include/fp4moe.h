@@ -216,6 +216,39 @@ FP4MOE_API int moe_combine(const float* y, int32_t y_rows, int32_t n, const int3
                            hipStream_t stream);
 
 /*
+ * The bf16-dequant rung -- [GATE: comparison 3, the class shift against the bf16-dequant rung on
+ * the same inputs].  A reference route on unquantized activations and exact weights: cvt_bf16 of
+ * the f32 activations, fp4_dequant_bf16 of the expert, gemm_bf16 of the two.  The native path's
+ * difference from it is the shift caused by quantizing the activations to E4M3, predicted per
+ * output as (2^-4 / sqrt 3) * ||x (.) w||_2.  Not on the hot path.
+ *
+ * cvt_bf16 -- out[i] = bf16(x[i]): round to nearest, ties to even; NaN stays NaN (sign and the top
+ * payload bits kept, quiet bit set).  x: f32 [count]; out: bf16 bit patterns [count].
+ * Errors: EINVAL if count < 0 or a pointer is NULL while count > 0.  count == 0 is a no-op.
+ */
+FP4MOE_API int cvt_bf16(const float* x, uint16_t* out, int64_t count, hipStream_t stream);
+
+/*
+ * fp4_dequant_bf16 -- out[c, j] = bf16(f32(E2M1(W[c, j]) * ws[c, j / gs])) with the GEMM's weight
+ * scale: ws = f32(E4M3(S) * scale2) for NVFP4 (gs 16), 2^(S - 127) for MXFP4 (gs 32, S = 255 NaN);
+ * a NaN result is written as the canonical bf16 NaN 0x7FC0.
+ * w_packed: u8 [n, k/2] (4-byte aligned); w_scales: u8 [n, k/gs]; out: bf16 [n, k] (16-byte aligned).
+ * Errors: EINVAL if n < 0, k <= 0, k % 128 != 0, kind not 0/1, 2*n*k >= 2^31, a pointer is NULL while
+ * n > 0, or an alignment is not met.  n == 0 is a no-op.
+ */
+FP4MOE_API int fp4_dequant_bf16(const uint8_t* w_packed, const uint8_t* w_scales, float scale2, int32_t kind,
+                                int32_t n, int32_t k, uint16_t* out, hipStream_t stream);
+
+/*
+ * gemm_bf16 -- out[r, c] = sum_j a[r, j] * w[c, j]: bf16 operands (exact products), f32 accumulation
+ * in ascending j over 16-wide steps.  a: bf16 [m, k]; w: bf16 [n, k]; out: f32 [m, n].
+ * Errors: EINVAL if m < 0, n <= 0, k <= 0, k % 16 != 0, 2*m*k or 2*n*k >= 2^31, or a pointer is NULL
+ * while m > 0.  m == 0 is a no-op.
+ */
+FP4MOE_API int gemm_bf16(const uint16_t* a, const uint16_t* w, float* out, int32_t m, int32_t n, int32_t k,
+                         hipStream_t stream);
+
+/*
  * fp4moe_set_gemm_schedule -- test and benchmark hook (not part of the method).  The GEMM calls
  * pick a kernel from the host-known rows per expert: a row-streaming kernel (each expert's weights
  * read once per pass of 32 rows; used when total rows <= 32 x experts) or a tiled matrix-core

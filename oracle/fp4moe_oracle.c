@@ -477,7 +477,9 @@ void or_gather_rows(const uint8_t* codes, const float* scales, int64_t a_rows, i
  * path against it].  Readings where the page is silent (it prints the calls, not the kernels):
  *   - f32 -> bf16 rounds to nearest, ties to even; NaN stays NaN (sign and top payload bits kept,
  *     quiet bit set);
- *   - a weight's rung value is the f32 product E2M1 x ws (ws as in the GEMM), rounded to bf16;
+ *   - a weight's rung value is the f32 product E2M1 x ws (ws as in the GEMM), rounded to bf16; a
+ *     NaN scale gives the canonical quiet NaN 0x7FC0 (the sign and payload of a NaN produced by
+ *     arithmetic are not fixed by IEEE 754);
  *   - the bf16 GEMM sums the exact products of the bf16 values (here in f64).
  * ------------------------------------------------------------------------------------------- */
 
@@ -511,7 +513,7 @@ void or_dequant_bf16(const uint8_t* w, const uint8_t* s, float scale2, int kind,
             const unsigned code = (kk & 1) ? (byte >> 4) : (byte & 0x0Fu);
             const float ws = (float)weight_scale(kind, s[c * (k / gs) + kk / gs], scale2);
             const float v = (float)or_e2m1_value(code) * ws;
-            out[c * k + kk] = or_bf16_bits(v);
+            out[c * k + kk] = isnan(v) ? 0x7FC0u : or_bf16_bits(v);
         }
 }
 

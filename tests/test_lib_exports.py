@@ -176,3 +176,19 @@ def test_combine_rejects(lib, y_rows, n, tokens, top_k):
 def test_combine_null_and_noop(lib):
     assert lib.moe_combine(BAD, 8, 16, NULL, NULL, 4, 2, BAD, NULL) == 1
     assert lib.moe_combine(NULL, 0, 16, NULL, NULL, 0, 2, NULL, NULL) == 0
+
+
+def test_rung_rejects(lib):
+    assert lib.cvt_bf16(BAD, BAD, -1, NULL) == 1
+    assert lib.cvt_bf16(NULL, BAD, 4, NULL) == 1
+    assert lib.cvt_bf16(NULL, NULL, 0, NULL) == 0
+    assert lib.fp4_dequant_bf16(BAD, BAD, ctypes.c_float(1.0), 0, 8, 100, BAD, NULL) == 1     # k % 128
+    assert lib.fp4_dequant_bf16(BAD, BAD, ctypes.c_float(1.0), 2, 8, 128, BAD, NULL) == 1     # kind
+    assert lib.fp4_dequant_bf16(BAD, BAD, ctypes.c_float(1.0), 0, 8, 128, ctypes.c_void_p(0x1008), NULL) == 1
+    assert lib.fp4_dequant_bf16(NULL, NULL, ctypes.c_float(1.0), 0, 0, 128, NULL, NULL) == 0
+    assert lib.gemm_bf16(BAD, BAD, BAD, 4, 4, 24, NULL) == 1                                # k % 16
+    assert lib.gemm_bf16(BAD, BAD, BAD, 4, 0, 32, NULL) == 1
+    assert lib.gemm_bf16(NULL, BAD, BAD, 4, 4, 32, NULL) == 1
+    assert lib.gemm_bf16(NULL, NULL, NULL, 0, 4, 32, NULL) == 0
+    for fn in ("cvt_bf16", "fp4_dequant_bf16", "gemm_bf16"):
+        assert fn in declared_functions()
