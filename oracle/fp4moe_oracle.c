@@ -533,3 +533,121 @@ void or_gemm_bf16(const uint16_t* a, const uint16_t* w, int64_t m, int64_t n, in
             abs_out[r * n + c] = mag;
         }
 }
+
+/* ---------------------------------------------------------------------------------------------
+ * W4A4 NVFP4 variant [CHECK: the NVFP4 MMQ W4A4 arms -- E2M1 activations with a two-level scale
+ * (a per-token row scale from the row amax, then a UE4M3 micro-scale per 16-element sub-block of
+ * amax_sub / 6), the sub-block-only quantizer it replaced, the DYNAMIC-RANGE arm (tokens scaled by
+ * decades) and the RESIDUAL-CHANNEL arm (the k loudest channels kept out of the E2M1 path and added
+ * back exactly)].  Lossy: the pages hold it to informational relative errors and two hard
+ * comparisons.  Readings where the pages are silent:
+ *   - E2M1 values are the OCP grid (as for the weights); the micro-scale is an unsigned E4M3 byte;
+ *   - row scale rs = amax_row / 2688 (6 x 448: the largest sub-block then gets micro-scale 448),
+ *     rs = 1 without the row level or for an all-zero row;
+ *   - micro-scale = E4M3 encoding (round to nearest even) of (amax_sub / rs) / 6 clamped to
+ *     [2^-9, 448] -- the smallest and largest UE4M3 values, the clamps the pages speak of -- and 0
+ *     for an all-zero sub-block;
+ *   - code = E2M1 encoding (round to nearest, ties to the even code, saturating at 6) of
+ *     (x / rs) / micro, 0 when the micro-scale decodes to 0; each operation one f32 operation;
+ *   - loudest channels: by the largest |x| over all tokens, ties to the lower index.
+ * ------------------------------------------------------------------------------------------- */
+
+/* E2M1 code of a finite f32 value: nearest grid point, ties to the even code, magnitude capped at 6,
+ * sign bit 3 (kept also when the magnitude rounds to 0). */
+unsigned or_e2m1_encode(float v) {
+    const double a = fabs((double)v);
+    unsigned best = 7;
+    if (a < 6.0) {
+        unsigned lo = 0;
+        while (lo < 7 && or_e2m1_value(lo + 1) <= a) ++lo;      /* value(lo) <= a < value(lo + 1) */
+        const double mid = 0.5 * (or_e2m1_value(lo) + or_e2m1_value(lo + 1));
+        best = a < mid ? lo : (a > mid ? lo + 1 : ((lo & 1u) ? lo + 1 : lo));
+    }
+    return (signbit(v) ? 8u : 0u) | best;
+}
+
+void or_act_quant_fp4(const float* x, int64_t rows, int64_t k, int two_level, uint8_t* codes,
+                      uint8_t* micro, float* row_scale) {
+    for (int64_t r = 0; r < rows; ++r) {
+        const float* xr = x + r * k;
+        float amax = 0.0f;
+        for (int64_t i = 0; i < k; ++i) amax = fmaxf(amax, fabsf(xr[i]));
+        const float rs = (two_level && amax > 0.0f) ? amax / 2688.0f : 1.0f;
+        row_scale[r] = rs;
+        for (int64_t g = 0; g < k / 16; ++g) {
+            float asub = 0.0f;
+            for (int64_t i = 0; i < 16; ++i) asub = fmaxf(asub, fabsf(xr[16 * g + i]));
+            const float t = asub / rs;
+            const float want = t / 6.0f;
+            const unsigned mb = want > 0.0f ? or_e4m3_encode(fminf(fmaxf(want, 0x1p-9f), 448.0f)) & 0x7Fu : 0u;
+            micro[r * (k / 16) + g] = (uint8_t)mb;
+            const float dec = (float)or_e4m3_value(mb);
+            for (int64_t i = 0; i < 16; i += 2) {
+                unsigned c[2];
+                for (int h = 0; h < 2; ++h) {
+                    const float y = xr[16 * g + i + h] / rs;
+                    c[h] = dec > 0.0f ? or_e2m1_encode(y / dec) : 0u;
+                }
+                codes[r * (k / 2) + (16 * g + i) / 2] = (uint8_t)(c[0] | (c[1] << 4));
+            }
+        }
+    }
+}
+
+/* Dequantized W4A4 activations, f64 [rows, k]: rs * micro * E2M1(code). */
+void or_dequant_acts_fp4(const uint8_t* codes, const uint8_t* micro, const float* row_scale, int64_t rows,
+                         int64_t k, double* out) {
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t i = 0; i < k; ++i) {
+            const uint8_t byte = codes[r * (k / 2) + i / 2];
+            const unsigned code = (i & 1) ? (byte >> 4) : (byte & 0x0Fu);
+            out[r * k + i] = (double)row_scale[r] * or_e4m3_value(micro[r * (k / 16) + i / 16]) *
+                             or_e2m1_value(code);
+        }
+}
+
+/* The k_res loudest channels (largest max over tokens of |x|, ties to the lower index), in that
+ * order. */
+void or_loud_channels(const float* x, int64_t rows, int64_t k, int64_t k_res, uint8_t* taken, int32_t* idx) {
+    memset(taken, 0, (size_t)k);
+    for (int64_t j = 0; j < k_res; ++j) {
+        int64_t best = -1;
+        float best_v = -1.0f;
+        for (int64_t c = 0; c < k; ++c) {
+            if (taken[c]) continue;
+            float m = 0.0f;
+            for (int64_t r = 0; r < rows; ++r) m = fmaxf(m, fabsf(x[r * k + c]));
+            if (m > best_v) { best_v = m; best = c; }
+        }
+        taken[best] = 1;
+        idx[j] = (int32_t)best;
+    }
+}
+
+/* W4A4 GEMM in f64 on the quantized operands: out[r, c] = sum_k A(r, k) W(c, k) with A the
+ * dequantized activations above and W = E2M1 x ws (NVFP4, ws = f32(E4M3 x scale2)); plus, when
+ * k_res > 0, the exact contribution of the kept channels: sum_j x[r, idx_j] W(c, idx_j) (those
+ * channels must be zero in the quantized activations).  abs_out: the sum of magnitudes. */
+void or_w4a4_gemm(const uint8_t* a_codes, const uint8_t* a_micro, const float* a_rs, const uint8_t* w,
+                  const uint8_t* s, float scale2, int64_t g, int64_t n, int64_t k, const float* x,
+                  const int32_t* idx, int64_t k_res, double* ad_scratch, double* wd_scratch, double* out,
+                  double* abs_out) {
+    or_dequant_acts_fp4(a_codes, a_micro, a_rs, g, k, ad_scratch);
+    or_dequant_weights(w, s, scale2, OR_NVFP4, n, k, wd_scratch);
+    for (int64_t r = 0; r < g; ++r)
+        for (int64_t c = 0; c < n; ++c) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t i = 0; i < k; ++i) {
+                const double p = ad_scratch[r * k + i] * wd_scratch[c * k + i];
+                acc += p;
+                mag += fabs(p);
+            }
+            for (int64_t j = 0; j < k_res; ++j) {
+                const double p = (double)x[r * k + idx[j]] * wd_scratch[c * k + idx[j]];
+                acc += p;
+                mag += fabs(p);
+            }
+            out[r * n + c] = acc;
+            abs_out[r * n + c] = mag;
+        }
+}

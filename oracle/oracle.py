@@ -87,6 +87,16 @@ def _load():
             lib.or_combine.argtypes = [P, I64, I64, P, P, I64, I64, P, P]
             lib.or_gather_rows.restype = None
             lib.or_gather_rows.argtypes = [P, P, I64, I64, P, I64, P, P]
+            lib.or_e2m1_encode.restype = ctypes.c_uint
+            lib.or_e2m1_encode.argtypes = [ctypes.c_float]
+            lib.or_act_quant_fp4.restype = None
+            lib.or_act_quant_fp4.argtypes = [P, I64, I64, ctypes.c_int, P, P, P]
+            lib.or_dequant_acts_fp4.restype = None
+            lib.or_dequant_acts_fp4.argtypes = [P, P, P, I64, I64, P]
+            lib.or_loud_channels.restype = None
+            lib.or_loud_channels.argtypes = [P, I64, I64, I64, P, P]
+            lib.or_w4a4_gemm.restype = None
+            lib.or_w4a4_gemm.argtypes = [P, P, P, P, P, ctypes.c_float, I64, I64, I64, P, P, I64, P, P, P, P]
             lib.or_cvt_bf16.restype = None
             lib.or_cvt_bf16.argtypes = [P, I64, P]
             lib.or_dequant_bf16.restype = None
@@ -438,3 +448,72 @@ def class_shift_prediction(x, wd) -> np.ndarray:
     +-U_FP8 relative and independent across k, would cause."""
     x = np.asarray(x, dtype=np.float64)
     return U_FP8 / np.sqrt(3.0) * np.sqrt((x * x) @ (np.asarray(wd, dtype=np.float64) ** 2).T)
+
+
+# --------------------------------------------------------------------------- W4A4 NVFP4 variant
+
+def e2m1_encode(v) -> np.ndarray:
+    """E2M1 codes of f32 values (nearest grid point, ties to the even code, magnitude capped at 6)."""
+    lib = _load()
+    v = np.asarray(v, dtype=np.float32)
+    return np.array([lib.or_e2m1_encode(float(t)) for t in v.ravel()], dtype=np.uint8).reshape(v.shape)
+
+
+def act_quant_fp4(x, two_level: bool = True):
+    """W4A4 activations: (codes u8 [rows, k/2] nibble-packed, micro u8 [rows, k/16] UE4M3,
+    row_scale f32 [rows]).  two_level=False is the sub-block-only quantizer (row scale 1)."""
+    x, px = _c(x, np.float32)
+    rows, k = x.shape
+    if k % 16:
+        raise ValueError("k must be a multiple of 16")
+    codes = np.empty((rows, k // 2), dtype=np.uint8)
+    micro = np.empty((rows, k // 16), dtype=np.uint8)
+    rs = np.empty(rows, dtype=np.float32)
+    _load().or_act_quant_fp4(px, rows, k, int(bool(two_level)), codes.ctypes.data, micro.ctypes.data,
+                             rs.ctypes.data)
+    return codes, micro, rs
+
+
+def dequant_acts_fp4(codes, micro, row_scale) -> np.ndarray:
+    codes, pc = _c(codes, np.uint8)
+    micro, pm = _c(micro, np.uint8)
+    row_scale, pr = _c(row_scale, np.float32)
+    rows, k = codes.shape[0], codes.shape[1] * 2
+    out = np.empty((rows, k), dtype=np.float64)
+    _load().or_dequant_acts_fp4(pc, pm, pr, rows, k, out.ctypes.data)
+    return out
+
+
+def loud_channels(x, k_res: int) -> np.ndarray:
+    """Indices of the k_res channels with the largest max |x| over tokens (ties to the lower index)."""
+    x, px = _c(x, np.float32)
+    rows, k = x.shape
+    idx = np.empty(k_res, dtype=np.int32)
+    taken = np.empty(k, dtype=np.uint8)
+    _load().or_loud_channels(px, rows, k, int(k_res), taken.ctypes.data, idx.ctypes.data)
+    return idx
+
+
+def w4a4_gemm(codes, micro, row_scale, w, s, scale2, x=None, idx=None):
+    """f64 W4A4 GEMM on the quantized operands (NVFP4 weights), plus the exact contribution of the
+    kept channels idx of x when given.  Returns (out [g, n], sum of magnitudes)."""
+    codes, pc = _c(codes, np.uint8)
+    micro, pm = _c(micro, np.uint8)
+    row_scale, prs = _c(row_scale, np.float32)
+    w, pw = _c(w, np.uint8)
+    s, ps = _c(s, np.uint8)
+    g, k = codes.shape[0], codes.shape[1] * 2
+    n = w.shape[0]
+    _check_expert(w, s, NVFP4, n, k)
+    k_res = 0 if idx is None else len(idx)
+    px = pidx = None
+    if k_res:
+        x, px = _c(x, np.float32)
+        idx, pidx = _c(idx, np.int32)
+    ad = np.empty((g, k), dtype=np.float64)
+    wd = np.empty((n, k), dtype=np.float64)
+    out = np.empty((g, n), dtype=np.float64)
+    absout = np.empty((g, n), dtype=np.float64)
+    _load().or_w4a4_gemm(pc, pm, prs, pw, ps, float(np.float32(scale2)), g, n, k, px, pidx, k_res,
+                         ad.ctypes.data, wd.ctypes.data, out.ctypes.data, absout.ctypes.data)
+    return out, absout

@@ -359,3 +359,27 @@ def config4_chain() -> ExpertChainWorkload:
     return ExpertChainWorkload("config4 expert layer: gate/up (n=4096, k=7168) -> swiglu limit 7 -> "
                                "down (n=7168, k=2048); 8192 tokens, E=256, Zipf(1.1) top-8",
                                up.x, up.row_ids, up.offsets, route_w, up.kinds, 7.0, up, down, up.logits)
+
+
+# --------------------------------------------------------------------------- W4A4 arms
+W4A4_HOT_CHANNELS = 8
+
+
+def w4a4_case(seed: int, T: int, n: int, k: int, arm: str = "uniform"):
+    """Activations and an NVFP4 expert for the W4A4 arms: x = 0.1 U[0, 1) per element ("uniform");
+    token j additionally scaled by 10^((j mod 7) - 3) ("dyn"); and on top of that 8 fixed channels
+    (977 c + 13) mod k amplified x300 ("res").  Returns (x f32 [T, k], Expert)."""
+    rng = np.random.default_rng([SEED_BASE, 500, seed])
+    x = rng.random((T, k)) * 0.1
+    if arm in ("dyn", "res"):
+        x *= 10.0 ** ((np.arange(T) % 7) - 3)[:, None]
+    if arm == "res":
+        hot = [(c * 977 + 13) % k for c in range(W4A4_HOT_CHANNELS)]
+        x[:, hot] *= 300.0
+    ex = Expert(NVFP4, random_nibbles(rng, n, k), random_scale_codes(rng, NVFP4, n, k),
+                float(GROUPED_SCALE2_CHOICES[1]))
+    return x.astype(np.float32), ex
+
+
+def w4a4_hot_channels(k: int) -> list:
+    return [(c * 977 + 13) % k for c in range(W4A4_HOT_CHANNELS)]
