@@ -59,6 +59,12 @@ def lib() -> ctypes.CDLL:
         L.fp4_dequant_bf16.restype = ctypes.c_int
         L.gemm_bf16.argtypes = [P, P, P, I32, I32, I32, P]
         L.gemm_bf16.restype = ctypes.c_int
+        L.act_quant_fp4.argtypes = [P, P, I32, P, P, P, I32, I32, I32, P]
+        L.act_quant_fp4.restype = ctypes.c_int
+        L.loud_channels.argtypes = [P, I32, I32, I32, P, P]
+        L.loud_channels.restype = ctypes.c_int
+        L.w4a4_gemm.argtypes = [P, P, P, P, P, F32, P, P, I32, P, I32, I32, I32, P]
+        L.w4a4_gemm.restype = ctypes.c_int
         L.fp4moe_last_error.argtypes = []
         L.fp4moe_last_error.restype = ctypes.c_char_p
         L.fp4moe_version.argtypes = []
@@ -368,4 +374,72 @@ def gemm_bf16(a, w, out=None, stream=None):
     if out.shape != (m, n):
         raise ValueError("out must be [m, n]")
     _check(lib().gemm_bf16(_ptr(a), _ptr(w), _ptr(out), m, n, k, _stream(stream)), "gemm_bf16")
+    return out
+
+
+# --------------------------------------------------------------------------- W4A4 NVFP4 variant
+
+def act_quant_fp4(x, two_level: bool = True, skip_channels=None, codes=None, micro=None, row_scale=None,
+                  stream=None):
+    """x f32 [rows, k] -> (codes u8 [rows, k/2], micro u8 [rows, k/16] UE4M3, row_scale f32 [rows]);
+    channels in skip_channels (int32 [n]) count as zero."""
+    _dev(x, torch.float32, "x", 2)
+    rows, k = x.shape
+    n_skip = 0
+    if skip_channels is not None:
+        _dev(skip_channels, torch.int32, "skip_channels", 1)
+        n_skip = skip_channels.shape[0]
+    if codes is None:
+        codes = torch.empty((rows, k // 2), dtype=torch.uint8, device=x.device)
+    if micro is None:
+        micro = torch.empty((rows, k // 16), dtype=torch.uint8, device=x.device)
+    if row_scale is None:
+        row_scale = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _dev(codes, torch.uint8, "codes", 2)
+    _dev(micro, torch.uint8, "micro", 2)
+    _dev(row_scale, torch.float32, "row_scale", 1)
+    if codes.shape != (rows, k // 2) or micro.shape != (rows, k // 16) or row_scale.shape != (rows,):
+        raise ValueError("output shapes do not match x")
+    _check(lib().act_quant_fp4(_ptr(x), _ptr(skip_channels), n_skip, _ptr(codes), _ptr(micro), _ptr(row_scale),
+                               rows, k, int(bool(two_level)), _stream(stream)), "act_quant_fp4")
+    return codes, micro, row_scale
+
+
+def loud_channels(x, k_res: int, idx=None, stream=None):
+    """The k_res channels of x f32 [rows, k] with the largest max |x|, loudest first (int32)."""
+    _dev(x, torch.float32, "x", 2)
+    rows, k = x.shape
+    if idx is None:
+        idx = torch.empty(k_res, dtype=torch.int32, device=x.device)
+    _dev(idx, torch.int32, "idx", 1)
+    if idx.shape != (k_res,):
+        raise ValueError("idx must be [k_res]")
+    _check(lib().loud_channels(_ptr(x), rows, k, int(k_res), _ptr(idx), _stream(stream)), "loud_channels")
+    return idx
+
+
+def w4a4_gemm(codes, micro, row_scale, w_packed, w_scales, scale2: float, x=None, res_idx=None, out=None,
+              stream=None):
+    """W4A4 GEMM with NVFP4 weights -> out f32 [g, n]; res_idx (int32 [k_res]) adds the kept channels of
+    x f32 [g, k] exactly."""
+    _dev(codes, torch.uint8, "codes", 2)
+    _dev(micro, torch.uint8, "micro", 2)
+    _dev(row_scale, torch.float32, "row_scale", 1)
+    _dev(w_packed, torch.uint8, "w_packed", 2)
+    _dev(w_scales, torch.uint8, "w_scales", 2)
+    g, k = codes.shape[0], codes.shape[1] * 2
+    n = w_packed.shape[0]
+    if w_packed.shape != (n, k // 2) or w_scales.shape != (n, k // 16) or micro.shape != (g, k // 16):
+        raise ValueError("operand shapes do not match")
+    k_res = 0
+    if res_idx is not None:
+        _dev(res_idx, torch.int32, "res_idx", 1)
+        _dev(x, torch.float32, "x", 2)
+        k_res = res_idx.shape[0]
+    if out is None:
+        out = torch.empty((g, n), dtype=torch.float32, device=codes.device)
+    _dev(out, torch.float32, "out", 2)
+    _check(lib().w4a4_gemm(_ptr(codes), _ptr(micro), _ptr(row_scale), _ptr(w_packed), _ptr(w_scales),
+                           float(scale2), _ptr(x) if k_res else None, _ptr(res_idx), k_res, _ptr(out), g, n, k,
+                           _stream(stream)), "w4a4_gemm")
     return out

@@ -193,6 +193,54 @@ int gemm_bf16(const uint16_t* a, const uint16_t* w, float* out, int32_t m, int32
   return launched(fp4moe::launch_gemm_bf16(a, w, out, m, n, k, stream), what);
 }
 
+int act_quant_fp4(const float* x, const int32_t* skip_channels, int32_t n_skip, uint8_t* codes, uint8_t* micro,
+                  float* row_scale, int32_t rows, int32_t k, int32_t two_level, hipStream_t stream) {
+  const char* what = "act_quant_fp4";
+  if (rows < 0) return fail(FP4MOE_EINVAL, "%s: rows = %d < 0", what, (int)rows);
+  if (int rc = check_k(k, what)) return rc;
+  if (n_skip < 0 || n_skip > 64) return fail(FP4MOE_EINVAL, "%s: n_skip = %d must be in [0, 64]", what, (int)n_skip);
+  if (two_level != 0 && two_level != 1) return fail(FP4MOE_EINVAL, "%s: two_level must be 0 or 1", what);
+  if ((int64_t)rows * k * 4 >= kMaxPlaneBytes) return fail(FP4MOE_EINVAL, "%s: x reaches 2^31 bytes", what);
+  if (rows == 0) return ok();
+  if (!x || !codes || !micro || !row_scale || (n_skip > 0 && !skip_channels))
+    return fail(FP4MOE_EINVAL, "%s: NULL buffer with rows > 0", what);
+  if ((reinterpret_cast<uintptr_t>(x) & 15) || (reinterpret_cast<uintptr_t>(codes) & 1))
+    return fail(FP4MOE_EINVAL, "%s: x must be 16-byte and codes 2-byte aligned", what);
+  return launched(fp4moe::launch_act_quant_fp4(x, skip_channels, n_skip, rows, k, two_level, codes, micro, row_scale,
+                                               stream),
+                  what);
+}
+
+int loud_channels(const float* x, int32_t rows, int32_t k, int32_t k_res, int32_t* idx, hipStream_t stream) {
+  const char* what = "loud_channels";
+  if (rows < 0) return fail(FP4MOE_EINVAL, "%s: rows = %d < 0", what, (int)rows);
+  if (k < 1 || k > 8192) return fail(FP4MOE_EINVAL, "%s: k = %d must be in [1, 8192]", what, (int)k);
+  if (k_res < 0 || k_res > 64 || k_res > k)
+    return fail(FP4MOE_EINVAL, "%s: k_res = %d must be in [0, min(k, 64)]", what, (int)k_res);
+  if ((int64_t)rows * k * 4 >= kMaxPlaneBytes) return fail(FP4MOE_EINVAL, "%s: x reaches 2^31 bytes", what);
+  if (k_res == 0) return ok();
+  if (!idx || (rows > 0 && !x)) return fail(FP4MOE_EINVAL, "%s: NULL buffer", what);
+  return launched(fp4moe::launch_loud_channels(x, rows, k, k_res, idx, stream), what);
+}
+
+int w4a4_gemm(const uint8_t* a_codes, const uint8_t* a_micro, const float* a_row_scale, const uint8_t* w_packed,
+              const uint8_t* w_scales, float scale2, const float* x, const int32_t* res_idx, int32_t k_res, float* out,
+              int32_t g, int32_t n, int32_t k, hipStream_t stream) {
+  const char* what = "w4a4_gemm";
+  if (g < 0) return fail(FP4MOE_EINVAL, "%s: g = %d < 0", what, (int)g);
+  if (n <= 0) return fail(FP4MOE_EINVAL, "%s: n = %d must be positive", what, (int)n);
+  if (int rc = check_k(k, what)) return rc;
+  if (k_res < 0 || k_res > 64) return fail(FP4MOE_EINVAL, "%s: k_res = %d must be in [0, 64]", what, (int)k_res);
+  if (int rc = check_planes(g, n, k, what)) return rc;
+  if ((int64_t)g * k * 4 >= kMaxPlaneBytes) return fail(FP4MOE_EINVAL, "%s: x reaches 2^31 bytes", what);
+  if (g == 0) return ok();
+  if (!a_codes || !a_micro || !a_row_scale || !w_packed || !w_scales || !out || (k_res > 0 && (!x || !res_idx)))
+    return fail(FP4MOE_EINVAL, "%s: NULL buffer with g > 0", what);
+  return launched(fp4moe::launch_w4a4_gemm(a_codes, a_micro, a_row_scale, w_packed, w_scales, scale2, x, res_idx,
+                                           k_res, out, g, n, k, stream),
+                  what);
+}
+
 int fp4_expert_gemm(const uint8_t* a_codes, const float* a_scales, const uint8_t* w_packed,
                     const uint8_t* w_scales, float scale2, int32_t kind, float* out, int32_t g,
                     int32_t n, int32_t k, hipStream_t stream) {

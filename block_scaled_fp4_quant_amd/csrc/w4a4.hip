@@ -1,0 +1,240 @@
+// w4a4.hip -- the W4A4 NVFP4 variant: E2M1 activations with a two-level scale, the loudest-channel
+// side path, and the FP4 x FP4 GEMM (memra-engine 0.71.0 kernel_check.rs page, the NVFP4 MMQ W4A4
+// arms: a per-token row scale from the row amax, a UE4M3 micro-scale of amax_sub / 6 per 16-element
+// sub-block, E2M1 codes; the sub-block-only quantizer it replaced; the k loudest channels kept out of
+// the E2M1 path and added back exactly).  Lossy by design: E2M1 has 8 magnitudes.
+//
+// Quantizer, per row (f32, each step one IEEE operation):
+//   rs = amax_row / 2688 (6 x 448, so the loudest sub-block gets micro-scale 448), 1 without the row
+//   level or for an all-zero row;  micro = E4M3(clamp((amax_sub / rs) / 6, 2^-9, 448)) rounded to
+//   nearest even, 0 for an all-zero sub-block;  code = E2M1((x / rs) / micro), nearest grid point,
+//   ties to the even code, magnitude capped at 6, 0 when micro is 0.  Kept-out channels count as 0.
+// GEMM: out[r, c] = rs[r] * scale2 * sum_k (E2M1(a) * micro) * (E2M1(w) * E4M3(ws)) + sum over kept
+//   channels j of x[r, j] * (E2M1(w[c, j]) * f32(E4M3(ws) * scale2)).  Both products E2M1 x E4M3 have
+//   at most 5 significant bits, so the bf16 MFMA operands are exact; the row and tensor scales
+//   multiply the f32 sum (exact for power-of-two scale2).
+//
+// Layouts: codes u8 [rows, k/2] (even k in the low nibble), micro u8 [rows, k/16], rs f32 [rows].
+// None of this is tuned: one wavefront per row in the quantizer, one per 32 x 32 output tile in the
+// GEMM, operands dequantized in registers straight from global memory.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace fp4moe {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kW4Threads = 256;
+constexpr int kMaxSkip = 64;
+
+// E2M1 code of a finite f32: the comparisons against the midpoints of the grid
+// {0, .5, 1, 1.5, 2, 3, 4, 6}, each tie going to the even code.
+__device__ __forceinline__ uint32_t e2m1_encode(float q) {
+  const float a = fabsf(q);
+  const uint32_t m = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+  return m | ((f2u(q) >> 28) & 8u);
+}
+
+__device__ __forceinline__ float e2m1_value(uint32_t code) {
+  const uint32_t ef = (code >> 1) & 3u, m = code & 1u;
+  const float mag = ef == 0 ? 0.5f * (float)m : (1.0f + 0.5f * (float)m) * (float)(1u << (ef - 1));
+  return (code & 8u) ? -mag : mag;
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t byte) { return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0); }
+
+__device__ __forceinline__ uint32_t e4m3_encode_pos(float v) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0x7Fu;
+}
+
+// Maximum over each aligned group of 4 lanes.
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, dpp_f32<kDppQuadXor1>(v));
+  return fmaxf(v, dpp_f32<kDppQuadXor2>(v));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = halfwave_max(v);
+  return fmaxf(u2f((uint32_t)__builtin_amdgcn_readlane((int)f2u(v), 0)),
+               u2f((uint32_t)__builtin_amdgcn_readlane((int)f2u(v), 32)));
+}
+
+// One wavefront per row; 256 elements per step (4 per lane, a 16-element sub-block per 4 lanes).
+__global__ __launch_bounds__(kW4Threads) void act_quant_fp4_kernel(const float* __restrict__ x,
+                                                                   const int32_t* __restrict__ skip, int32_t n_skip,
+                                                                   int32_t rows, int32_t k, int32_t two_level,
+                                                                   uint8_t* __restrict__ codes,
+                                                                   uint8_t* __restrict__ micro,
+                                                                   float* __restrict__ row_scale) {
+  __shared__ int32_t s_skip[kMaxSkip];
+  for (int i = threadIdx.x; i < n_skip; i += kW4Threads) s_skip[i] = skip[i];
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * (kW4Threads / 64) + (threadIdx.x >> 6);
+  if (r >= rows) return;                             // uniform per wavefront
+  const float* xr = x + r * k;
+  auto load4 = [&](int c0) {
+    f32x4 v = *reinterpret_cast<const f32x4*>(xr + c0);
+    for (int i = 0; i < n_skip; ++i) {
+      const int d = s_skip[i] - c0;
+      if (d >= 0 && d < 4) v[d] = 0.0f;
+    }
+    return v;
+  };
+  float amax = 0.0f;
+  for (int c0 = 4 * lane; c0 < k; c0 += 256) {
+    const f32x4 v = load4(c0);
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+  }
+  amax = wave_max(amax);
+  const float rs = (two_level && amax > 0.0f) ? amax / 2688.0f : 1.0f;
+  if (lane == 0) row_scale[r] = rs;
+  for (int c0 = 4 * lane; c0 < k; c0 += 256) {
+    const f32x4 v = load4(c0);
+    const float asub = quad_max(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+    const float want = (asub / rs) / 6.0f;
+    const uint32_t mb = want > 0.0f ? e4m3_encode_pos(fminf(fmaxf(want, 0x1p-9f), 448.0f)) : 0u;
+    const float dec = e4m3_value(mb);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t c = dec > 0.0f ? e2m1_encode((v[e] / rs) / dec) : 0u;
+      packed |= c << (4 * e);
+    }
+    reinterpret_cast<uint16_t*>(codes + r * (k / 2))[c0 / 4] = (uint16_t)packed;
+    if ((lane & 3) == 0) micro[r * (k / 16) + c0 / 16] = (uint8_t)mb;
+  }
+}
+
+// One block: the k_res channels with the largest max |x| over rows, ties to the lower index.  Each
+// thread keeps the keys of channels tid + 1024 i (i < 8): high word the order-preserving bits of the
+// (non-negative) column max, low word ~channel.
+constexpr int kLoudThreads = 1024;
+constexpr int kLoudPer = 8;
+
+__global__ __launch_bounds__(kLoudThreads) void loud_channels_kernel(const float* __restrict__ x, int32_t rows,
+                                                                     int32_t k, int32_t k_res,
+                                                                     int32_t* __restrict__ idx) {
+  __shared__ uint64_t s_best[kLoudThreads / 64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint64_t key[kLoudPer];
+#pragma unroll
+  for (int i = 0; i < kLoudPer; ++i) {
+    const int c = threadIdx.x + kLoudThreads * i;
+    float m = 0.0f;
+    if (c < k)
+      for (int32_t r = 0; r < rows; ++r) m = fmaxf(m, fabsf(x[(int64_t)r * k + c]));
+    key[i] = c < k ? (((uint64_t)f2u(m) << 32) | (uint32_t)~c) : 0ull;
+  }
+  for (int j = 0; j < k_res; ++j) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < kLoudPer; ++i) best = best > key[i] ? best : key[i];
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint64_t o = __shfl_xor(best, d, 64);
+      best = best > o ? best : o;
+    }
+    if (lane == 0) s_best[wv] = best;
+    __syncthreads();
+    best = s_best[0];
+    for (int w = 1; w < kLoudThreads / 64; ++w) best = best > s_best[w] ? best : s_best[w];
+    __syncthreads();
+    const int c = (int)~(uint32_t)best;
+#pragma unroll
+    for (int i = 0; i < kLoudPer; ++i)
+      if (c == (int)threadIdx.x + kLoudThreads * i) key[i] = 0ull;
+    if (threadIdx.x == 0) idx[j] = c;
+  }
+}
+
+// 8 E2M1 codes (4 bytes) times a scale, as bf16 (exact: at most 5 significant bits).
+__device__ __forceinline__ bf16x8 fp4x8_scaled_bf16(uint32_t nib, float scale) {
+  bf16x8 out;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = (__bf16)(e2m1_value((nib >> (4 * e)) & 0xFu) * scale);
+  return out;
+}
+
+// out = rs[r] * scale2 * (A W^T) [+ kept channels].  Wavefront (tm, tn): rows 32 tm .., columns
+// 32 tn ...  32x32x16 bf16 MFMA operand layout: lane l supplies row (column) l % 32 and
+// k = 8 (l / 32) .. +8, one 16-element scale group; the result holds column l % 32 and rows
+// 8 (v / 4) + 4 (l / 32) + v % 4.
+__global__ __launch_bounds__(kW4Threads) void w4a4_gemm_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_micro, const float* __restrict__ a_rs,
+    const uint8_t* __restrict__ w, const uint8_t* __restrict__ s, float scale2, const float* __restrict__ x,
+    const int32_t* __restrict__ res_idx, int32_t k_res, float* __restrict__ out, int32_t g, int32_t n, int32_t k,
+    int32_t tiles_n) {
+  const int lane = threadIdx.x & 63;
+  const int64_t tile = (int64_t)blockIdx.x * (kW4Threads / 64) + (threadIdx.x >> 6);
+  const int32_t tm = (int32_t)(tile / tiles_n), tn = (int32_t)(tile % tiles_n);
+  if ((int64_t)tm * 32 >= g) return;                 // uniform per wavefront
+  const rsrc_t rac = make_rsrc(a_codes, (uint32_t)g * (uint32_t)(k / 2));
+  const rsrc_t ram = make_rsrc(a_micro, (uint32_t)g * (uint32_t)(k / 16));
+  const rsrc_t rwc = make_rsrc(w, (uint32_t)n * (uint32_t)(k / 2));
+  const rsrc_t rws = make_rsrc(s, (uint32_t)n * (uint32_t)(k / 16));
+  const int row = tm * 32 + (lane & 31), col = tn * 32 + (lane & 31), half = lane >> 5;
+  const uint32_t oac = row < g ? (uint32_t)row * (uint32_t)(k / 2) + 4u * half : kOffNone;
+  const uint32_t oam = row < g ? (uint32_t)row * (uint32_t)(k / 16) : kOffNone;
+  const uint32_t owc = col < n ? (uint32_t)col * (uint32_t)(k / 2) + 4u * half : kOffNone;
+  const uint32_t ows = col < n ? (uint32_t)col * (uint32_t)(k / 16) : kOffNone;
+  f32x16 acc = {};
+  for (int32_t k0 = 0; k0 < k; k0 += 16) {
+    const uint32_t q = (uint32_t)k0 / 16u;
+    const uint32_t an = buf_load_u32(rac, oac == kOffNone ? kOffNone : oac + 8u * q);
+    const uint32_t am = buf_load_u8(ram, oam == kOffNone ? kOffNone : oam + q);
+    const uint32_t wn = buf_load_u32(rwc, owc == kOffNone ? kOffNone : owc + 8u * q);
+    const uint32_t ws = buf_load_u8(rws, ows == kOffNone ? kOffNone : ows + q);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp4x8_scaled_bf16(an, e4m3_value(am)),
+                                                  fp4x8_scaled_bf16(wn, e4m3_value(ws)), acc, 0, 0, 0);
+  }
+  if (col >= n) return;
+  // the kept channels of this lane's column: W(col, j) = E2M1 x f32(E4M3(ws) x scale2)
+  const float post = scale2;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int r = tm * 32 + 8 * (v / 4) + 4 * half + v % 4;
+    if (r >= g) continue;
+    float o = acc[v] * a_rs[r] * post;
+    for (int j = 0; j < k_res; ++j) {
+      const int32_t c = res_idx[j];
+      if (c < 0 || c >= k) continue;                 // not a channel: no term
+      const uint32_t byte = w[(int64_t)col * (k / 2) + c / 2];
+      const float wv = e2m1_value((c & 1) ? (byte >> 4) : (byte & 0xFu)) *
+                       (e4m3_value(s[(int64_t)col * (k / 16) + c / 16]) * scale2);
+      o = fmaf(x[(int64_t)r * k + c], wv, o);
+    }
+    out[(int64_t)r * n + col] = o;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_act_quant_fp4(const float* x, const int32_t* skip, int32_t n_skip, int32_t rows, int32_t k,
+                                int32_t two_level, uint8_t* codes, uint8_t* micro, float* row_scale,
+                                hipStream_t stream) {
+  const int blocks = (rows + kW4Threads / 64 - 1) / (kW4Threads / 64);
+  hipLaunchKernelGGL(act_quant_fp4_kernel, dim3(blocks), dim3(kW4Threads), 0, stream, x, skip, n_skip, rows, k,
+                     two_level, codes, micro, row_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_loud_channels(const float* x, int32_t rows, int32_t k, int32_t k_res, int32_t* idx,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL(loud_channels_kernel, dim3(1), dim3(kLoudThreads), 0, stream, x, rows, k, k_res, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_w4a4_gemm(const uint8_t* a_codes, const uint8_t* a_micro, const float* a_rs, const uint8_t* w,
+                            const uint8_t* s, float scale2, const float* x, const int32_t* res_idx, int32_t k_res,
+                            float* out, int32_t g, int32_t n, int32_t k, hipStream_t stream) {
+  const int32_t tiles_n = (n + 31) / 32;
+  const int64_t tiles = (int64_t)((g + 31) / 32) * tiles_n;
+  const int64_t blocks = (tiles + kW4Threads / 64 - 1) / (kW4Threads / 64);
+  hipLaunchKernelGGL(w4a4_gemm_kernel, dim3((uint32_t)blocks), dim3(kW4Threads), 0, stream, a_codes, a_micro, a_rs,
+                     w, s, scale2, x, res_idx, k_res, out, g, n, k, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace fp4moe

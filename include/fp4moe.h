@@ -12,6 +12,9 @@
  *           table of weight addresses).
  *   [GATE]  also: the swiglu_limit saturation cell (the clamp math between the gate/up and the down
  *           projection, and its swiglu call with an optional per-row weight).
+ *   [CHECK] also: the NVFP4 MMQ W4A4 arms (E2M1 activations with a per-token row scale and a UE4M3
+ *           micro-scale per 16; the sub-block-only quantizer; the DYNAMIC-RANGE and RESIDUAL-CHANNEL
+ *           arms).
  *   [QWEN]  memra-engine 0.125.0, src/bin/qwen4exp_gpu_gate.rs: the device-router arm (softmax top-k
  *           over router logits; selected ids and their emitted order exact, weights to a few ulp;
  *           ties of duplicates across the cut, all-equal rows, underflow).
@@ -246,6 +249,47 @@ FP4MOE_API int fp4_dequant_bf16(const uint8_t* w_packed, const uint8_t* w_scales
  * while m > 0.  m == 0 is a no-op.
  */
 FP4MOE_API int gemm_bf16(const uint16_t* a, const uint16_t* w, float* out, int32_t m, int32_t n, int32_t k,
+                         hipStream_t stream);
+
+/*
+ * The W4A4 NVFP4 variant -- [CHECK: the NVFP4 MMQ W4A4 arms].  Lossy (E2M1 activations): held to
+ * the pages' relative-error bands and comparisons, not to the FP8 path's bound.
+ *
+ * act_quant_fp4 -- per row r (f32, each step one IEEE operation):
+ *   rs[r] = amax_row / 2688 when two_level = 1 and the row is not all zero, else 1;
+ *   micro[r, g] = E4M3(clamp((amax_g / rs) / 6, 2^-9, 448)), round to nearest even; 0 for a zero group;
+ *   codes[r, j] = E2M1((x[r, j] / rs) / micro): nearest of {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the
+ *   even code, capped at 6, sign in bit 3; 0 when micro is 0.  amax over 16-element groups g.
+ * Channels listed in skip_channels (int32 [n_skip], device, entries outside [0, k) ignored) count as 0.
+ * x: f32 [rows, k] (16-byte aligned); codes: u8 [rows, k/2] (even j in the low nibble, 2-byte
+ * aligned); micro: u8 [rows, k/16]; row_scale: f32 [rows].
+ * Errors: EINVAL if rows < 0, k <= 0, k % 128 != 0, n_skip outside [0, 64], two_level not 0/1,
+ * 4*rows*k >= 2^31, an alignment is not met, or a required pointer is NULL while rows > 0.
+ */
+FP4MOE_API int act_quant_fp4(const float* x, const int32_t* skip_channels, int32_t n_skip, uint8_t* codes,
+                             uint8_t* micro, float* row_scale, int32_t rows, int32_t k, int32_t two_level,
+                             hipStream_t stream);
+
+/*
+ * loud_channels -- idx[j], j < k_res: the channels with the largest max over rows of |x[r, c]|, the
+ * loudest first, ties to the lower channel.  x: f32 [rows, k]; idx: int32 [k_res] (device).
+ * Errors: EINVAL if rows < 0, k outside [1, 8192], k_res outside [0, min(k, 64)], 4*rows*k >= 2^31,
+ * or a required pointer is NULL.  k_res == 0 is a no-op.
+ */
+FP4MOE_API int loud_channels(const float* x, int32_t rows, int32_t k, int32_t k_res, int32_t* idx,
+                             hipStream_t stream);
+
+/*
+ * w4a4_gemm -- out[r, c] = rs[r] * scale2 * sum_j (E2M1(a[r, j]) * micro[r, j/16]) * (E2M1(w[c, j]) *
+ * E4M3(S[c, j/16])), f32 accumulation of exact products, plus, for the k_res kept channels res_idx[i],
+ * x[r, res_idx[i]] * E2M1(w[c, res_idx[i]]) * f32(E4M3(S) * scale2) (x f32 [g, k]; those channels
+ * should be the ones act_quant_fp4 skipped).  NVFP4 weights as in fp4_expert_gemm.  out: f32 [g, n].
+ * Errors: EINVAL if g < 0, n <= 0, k <= 0, k % 128 != 0, k_res outside [0, 64], a plane reaches 2^31
+ * bytes, or a required pointer is NULL while g > 0.  g == 0 is a no-op.
+ */
+FP4MOE_API int w4a4_gemm(const uint8_t* a_codes, const uint8_t* a_micro, const float* a_row_scale,
+                         const uint8_t* w_packed, const uint8_t* w_scales, float scale2, const float* x,
+                         const int32_t* res_idx, int32_t k_res, float* out, int32_t g, int32_t n, int32_t k,
                          hipStream_t stream);
 
 /*

@@ -192,3 +192,21 @@ def test_rung_rejects(lib):
     assert lib.gemm_bf16(NULL, NULL, NULL, 0, 4, 32, NULL) == 0
     for fn in ("cvt_bf16", "fp4_dequant_bf16", "gemm_bf16"):
         assert fn in declared_functions()
+
+
+def test_w4a4_rejects(lib):
+    assert lib.act_quant_fp4(BAD, NULL, 0, BAD, BAD, BAD, 4, 100, 1, NULL) == 1          # k % 128
+    assert lib.act_quant_fp4(BAD, NULL, 65, BAD, BAD, BAD, 4, 128, 1, NULL) == 1         # n_skip
+    assert lib.act_quant_fp4(BAD, NULL, 2, BAD, BAD, BAD, 4, 128, 1, NULL) == 1          # skip NULL
+    assert lib.act_quant_fp4(BAD, NULL, 0, BAD, BAD, BAD, 4, 128, 2, NULL) == 1          # two_level
+    assert lib.act_quant_fp4(NULL, NULL, 0, NULL, NULL, NULL, 0, 128, 1, NULL) == 0
+    assert lib.loud_channels(BAD, 4, 8193, 1, BAD, NULL) == 1
+    assert lib.loud_channels(BAD, 4, 16, 17, BAD, NULL) == 1
+    assert lib.loud_channels(BAD, 4, 128, 65, BAD, NULL) == 1
+    assert lib.loud_channels(NULL, 4, 128, 0, NULL, NULL) == 0
+    assert lib.w4a4_gemm(BAD, BAD, BAD, BAD, BAD, ctypes.c_float(1.0), NULL, NULL, 0, BAD, 4, 8, 100, NULL) == 1
+    assert lib.w4a4_gemm(BAD, BAD, BAD, BAD, BAD, ctypes.c_float(1.0), NULL, NULL, 4, BAD, 4, 8, 128, NULL) == 1
+    assert lib.w4a4_gemm(BAD, BAD, BAD, BAD, BAD, ctypes.c_float(1.0), NULL, NULL, 65, BAD, 4, 8, 128, NULL) == 1
+    assert lib.w4a4_gemm(NULL, NULL, NULL, NULL, NULL, ctypes.c_float(1.0), NULL, NULL, 0, NULL, 0, 8, 128, NULL) == 0
+    for fn in ("act_quant_fp4", "loud_channels", "w4a4_gemm"):
+        assert fn in declared_functions()
