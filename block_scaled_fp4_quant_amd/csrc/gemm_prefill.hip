@@ -6,14 +6,18 @@
 // grouped GEMM section).  Here the work is a dense contraction, so the kernel is built around the
 // matrix cores.
 //
-// Arithmetic (bf16 MFMA 32x32x16, every operand exact):
+// Arithmetic (f16 or bf16 MFMA 32x32x16, every operand exact):
 //   A: E4M3 activation byte times its power-of-two row scale as[r, block], converted once per
 //      workgroup into LDS with the hardware scaled conversion (the scale only moves the exponent,
-//      so the bf16 value is exact).  Folding `as` into A removes any per-block partial sums.
-//   B: NVFP4 nibble -> f32 (hardware FP4 conversion), times the E4M3 weight scale decoded to f32
-//      (<= 6 significant bits: exact), packed to bf16 (exact).  scale2 multiplies the final f32 sum
-//      (exact for power-of-two scale2, otherwise within one f32 rounding of the per-group weight
-//      scale).  Products of these bf16 values are exact in f32.
+//      so the value is exact).  Folding `as` into A removes any per-block partial sums.
+//   B (NVFP4, f16 route): nibble -> f16 (hardware FP4 conversion), times the E4M3 weight scale as
+//      f16 with packed multiplies (at most 5 significant bits: exact).  Half the conversion work of
+//      the bf16 route.  f16 holds E4M3 x 2^t exactly for 2^-15 <= 2^t <= 2^7, so a tile takes this
+//      route only when every activation block scale of its rows lies there (real activations:
+//      2^-9 .. 2^3); otherwise:
+//   B (NVFP4, bf16 route): nibble -> f32, times the E4M3 weight scale in f32, packed to bf16.
+//   Either way scale2 multiplies the final f32 sum (exact for power-of-two scale2, otherwise within
+//   one f32 rounding of the per-group weight scale); products of the operands are exact in f32.
 //   MXFP4: nibble -> bf16 with the E8M0 scale applied by the hardware conversion (a pure exponent:
 //      exact).  The block-scaled FP8 x FP4 MFMA is not used: it aligns its products to the largest
 //      one before summing and drops the low bits of the others (measured: 448 + 2^-6 -> 448), which
@@ -52,6 +56,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kBM = 128;                     // rows per tile
+static_assert(kThreads == 2 * kBM, "the f16 operand check gives each row two threads");
 constexpr int kMT = kBM / 32;                // 4 MFMA row tiles (32 rows) per wavefront
 constexpr int kNT = 2;                       // 2 MFMA column tiles (32 columns) per wavefront
 constexpr int kWaveCols = 32 * kNT;          // 64
@@ -63,6 +68,13 @@ constexpr int kADepth = 1;                   // register sets in the activation 
 constexpr int kUnroll = 2;                   // blocks per loop iteration (a multiple of both depths and of the 2 LDS stages)
 constexpr int kNV = 0;
 constexpr int kMX = 1;
+constexpr int kNV16 = 2;                     // NVFP4 on f16 operands (tiles whose activation scales allow it)
+
+__host__ __device__ constexpr bool is_nv(int kind) { return kind != kMX; }
+
+// Operand type of the MFMAs: bf16, or f16 for kNV16.
+template <int KIND> struct OpT { typedef bf16x8 T; };
+template <> struct OpT<kNV16> { typedef h16x8 T; };
 
 struct Stage {
   uint8_t a[kBM * kARow];                    // bf16 activations (as folded), [row][128 k]
@@ -87,8 +99,11 @@ __device__ __forceinline__ void lds_barrier() {
 
 // 32x32x16 bf16 MFMA.  Lane l holds A row l%32 (B column l%32) for k = 8*(l/32) .. +8; the f32
 // result holds column l%32, rows 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.
-__device__ __forceinline__ f32x16 mfma32x32x16_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32x32x16(h16x8 a, h16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // The k order inside a 128-wide block.  Both operands use the same order, so the sum is the same
@@ -140,7 +155,7 @@ __device__ __forceinline__ void w_load(const Rsrc& r, const uint32_t (&wo)[kNT],
   }
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) {
-    if constexpr (KIND == kNV) {
+    if constexpr (is_nv(KIND)) {
       d.s[nt] = buf_load_u32(r.s, valid ? so[nt] + (uint32_t)b * 8u : kOffNone);
     } else {
       d.s[nt] = buf_load_u16(r.s, valid ? so[nt] + (uint32_t)b * 4u : kOffNone);
@@ -148,35 +163,49 @@ __device__ __forceinline__ void w_load(const Rsrc& r, const uint32_t (&wo)[kNT],
   }
 }
 
-// Row i of the staged rows (16 activation bytes): converted to bf16 with the power-of-two row
-// scale folded in (exact: the scale only moves the exponent) and written to the LDS stage.  The two
-// 16-byte halves are written in an order that puts the 8 lanes of a row on distinct banks.
+// Row i of the staged rows (16 activation bytes): converted to bf16 (f16 for kNV16) with the
+// power-of-two row scale folded in (exact: the scale only moves the exponent, and kNV16 tiles keep
+// every scaled value inside f16's exact range) and written to the LDS stage.  The two 16-byte halves
+// are written in an order that puts the 8 lanes of a row on distinct banks.
+template <int KIND>
 __device__ __forceinline__ void stage_store_q(Stage& st, const StageRegs& d, int i) {
   const int tid = threadIdx.x, c = tid & 7, row = (tid >> 3) + 32 * i;
-  u32x4 lo, hi;
+  // lanes c >= 4 write their upper half first: the code dwords are swapped before conversion
+  const bool swap = (c >> 2) & 1;
+  const uint32_t src[4] = {swap ? d.a[i][2] : d.a[i][0], swap ? d.a[i][3] : d.a[i][1],
+                           swap ? d.a[i][0] : d.a[i][2], swap ? d.a[i][1] : d.a[i][3]};
+  u32x4 first, second;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d.a[i][w], d.as[i], false);
-    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d.a[i][w], d.as[i], true);
-    if (w < 2) {
-      lo[2 * w] = __builtin_bit_cast(uint32_t, p0);
-      lo[2 * w + 1] = __builtin_bit_cast(uint32_t, p1);
+    uint32_t p0, p1;
+    if constexpr (KIND == kNV16) {
+      p0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src[w], d.as[i], false));
+      p1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src[w], d.as[i], true));
     } else {
-      hi[2 * (w - 2)] = __builtin_bit_cast(uint32_t, p0);
-      hi[2 * (w - 2) + 1] = __builtin_bit_cast(uint32_t, p1);
+      p0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src[w], d.as[i], false));
+      p1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src[w], d.as[i], true));
+    }
+    if (w < 2) {
+      first[2 * w] = p0;
+      first[2 * w + 1] = p1;
+    } else {
+      second[2 * (w - 2)] = p0;
+      second[2 * (w - 2) + 1] = p1;
     }
   }
   uint8_t* dst = st.a + row * kARow + 32 * c;
-  const bool swap = (c >> 2) & 1;
-  *reinterpret_cast<u32x4*>(dst + (swap ? 16 : 0)) = swap ? hi : lo;
-  *reinterpret_cast<u32x4*>(dst + (swap ? 0 : 16)) = swap ? lo : hi;
+  *reinterpret_cast<u32x4*>(dst + (swap ? 16 : 0)) = first;
+  *reinterpret_cast<u32x4*>(dst + (swap ? 0 : 16)) = second;
 }
 
 // Eight nibbles (k = 8 of one column) of step s, dequantized to bf16.
 template <int KIND, int S>
-__device__ __forceinline__ bf16x8 dequant_step(const WRegs& w, int nt) {
+__device__ __forceinline__ typename OpT<KIND>::T dequant_step(const WRegs& w, int nt) {
   const uint32_t q = w.w[nt][S >> 2][S & 3];
-  if constexpr (KIND == kNV) {
+  if constexpr (KIND == kNV16) {
+    // E2M1 -> f16 (exact), times the E4M3 group scale as f16 (exact; at most 5 significant bits)
+    return e2m1x8_scaled_f16(q, (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)w.s[nt], S >> 1));
+  } else if constexpr (KIND == kNV) {
     // E2M1 -> f32 (exact), times the E4M3 group scale (<= 6 significant bits: exact), -> bf16 (exact)
     const float sv = __builtin_amdgcn_cvt_f32_fp8((int)w.s[nt], S >> 1);
     const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q, 1.0f, 0);
@@ -199,15 +228,18 @@ __device__ __forceinline__ bf16x8 dequant_step(const WRegs& w, int nt) {
   }
 }
 
-__device__ __forceinline__ bf16x8 lds_a(const Stage& st, int mt, int s) {
+template <int KIND>
+__device__ __forceinline__ typename OpT<KIND>::T lds_a(const Stage& st, int mt, int s) {
   const int lane = threadIdx.x & 63;
-  return *reinterpret_cast<const bf16x8*>(st.a + (32 * mt + (lane & 31)) * kARow + 128 * (lane >> 5) + 16 * s);
+  return *reinterpret_cast<const typename OpT<KIND>::T*>(st.a + (32 * mt + (lane & 31)) * kARow +
+                                                         128 * (lane >> 5) + 16 * s);
 }
 
 // Fragments of the step the MFMAs consume next.
+template <int KIND>
 struct Frags {
-  bf16x8 a[kMT];
-  bf16x8 b[kNT];
+  typename OpT<KIND>::T a[kMT];
+  typename OpT<KIND>::T b[kNT];
 };
 
 // One 128-wide k block.  Step s issues its MFMAs while the operands of step s+1 are prepared
@@ -218,18 +250,18 @@ template <int KIND, int NMT>
 __device__ __forceinline__ void run_block(const Stage& cur, Stage& nxt, const WRegs& w, const WRegs& wn,
                                           StageRegs& store_src, StageRegs& load_dst, const Rsrc& r,
                                           const AOffs& ao, int b, int nblk, WRegs& wload,
-                                          const uint32_t (&wo)[kNT], const uint32_t (&so)[kNT], Frags& f,
+                                          const uint32_t (&wo)[kNT], const uint32_t (&so)[kNT], Frags<KIND>& f,
                                           f32x16 (&acc)[kMT][kNT]) {
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) {
-    Frags g;
+    Frags<KIND> g;
     if (s == kSteps - 1) {
       __builtin_amdgcn_sched_barrier(0);
       lds_barrier();                         // next stage complete; this stage fully read
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) g.a[mt] = (s + 1 < kSteps) ? lds_a(cur, mt, s + 1) : lds_a(nxt, mt, 0);
+    for (int mt = 0; mt < NMT; ++mt) g.a[mt] = (s + 1 < kSteps) ? lds_a<KIND>(cur, mt, s + 1) : lds_a<KIND>(nxt, mt, 0);
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
       switch (s) {
@@ -243,11 +275,11 @@ __device__ __forceinline__ void run_block(const Stage& cur, Stage& nxt, const WR
         default: g.b[nt] = dequant_step<KIND, 0>(wn, nt); break;
       }
     }
-    if (s < 4) stage_store_q(nxt, store_src, s);
+    if (s < 4) stage_store_q<KIND>(nxt, store_src, s);
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = mfma32x32x16_bf16(f.a[mt], f.b[nt], acc[mt][nt]);
+      for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = mfma32x32x16(f.a[mt], f.b[nt], acc[mt][nt]);
     if (s == 4) {
       __builtin_amdgcn_sched_barrier(0);
       stage_load(r, ao, b + 1 + kADepth, nblk, load_dst);
@@ -271,7 +303,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
   const int tid = threadIdx.x, lane = tid & 63, c32 = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int k = p.k, nblk = k >> 7;
-  constexpr int GS = (KIND == kNV) ? 16 : 32;
+  constexpr int GS = is_nv(KIND) ? 16 : 32;
 
   Rsrc r;
   r.w = make_rsrc(ex.w, (uint32_t)p.n * (uint32_t)(k / 2));
@@ -292,7 +324,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
   for (int nt = 0; nt < kNT; ++nt) {
     const int col = n0 + wave * kWaveCols + 32 * nt + c32;
     wo[nt] = col < p.n ? (uint32_t)col * (uint32_t)(k / 2) + 32u * h : kOffNone;
-    so[nt] = col < p.n ? (uint32_t)col * (uint32_t)(k / GS) + (KIND == kNV ? 4u : 2u) * h : kOffNone;
+    so[nt] = col < p.n ? (uint32_t)col * (uint32_t)(k / GS) + (is_nv(KIND) ? 4u : 2u) * h : kOffNone;
   }
 
   f32x16 acc[kMT][kNT];
@@ -320,16 +352,16 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) stage_store_q(st[0], sr[0], q);
+  for (int q = 0; q < 4; ++q) stage_store_q<KIND>(st[0], sr[0], q);
   __builtin_amdgcn_sched_barrier(0);
   stage_load(r, ao, kADepth, nblk, sr[0]);
   __builtin_amdgcn_sched_barrier(0);
   w_load<KIND>(r, wo, so, kWDepth - 1, nblk, wr[kWDepth - 1]);
   __builtin_amdgcn_sched_barrier(0);
   lds_barrier();
-  Frags f;
+  Frags<KIND> f;
 #pragma unroll
-  for (int mt = 0; mt < NMT; ++mt) f.a[mt] = lds_a(st[0], mt, 0);
+  for (int mt = 0; mt < NMT; ++mt) f.a[mt] = lds_a<KIND>(st[0], mt, 0);
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) f.b[nt] = dequant_step<KIND, 0>(wr[0], nt);
 
@@ -347,7 +379,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
     }
   }
 
-  const float post = (KIND == kNV) ? ex.scale2 : 1.0f;
+  const float post = is_nv(KIND) ? ex.scale2 : 1.0f;
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
@@ -363,6 +395,37 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
         }
       }
     }
+}
+
+// f16 holds E4M3 x 2^t exactly for every code when 2^-15 <= 2^t <= 2^7 (the smallest code step
+// 2^-9 stays >= f16's 2^-24, and 448 x 2^7 < 65504).  A tile takes the f16 route when the scale of
+// every 128-wide activation block of its rows lies in that range (or is 0: rows not loaded).  Real
+// activations have block scales of 2^-9 .. 2^3; all-zero or tiny blocks fall back to bf16.
+__device__ __forceinline__ bool f16_operands_exact(const GemmArgs& p, int m0, int mrows) {
+  // two threads per row (kThreads = 2 x kBM): thread half h reads blocks 8j + 4h .. +4 with 16-byte
+  // loads, all issued before the first test (past the row's end the buffer reads 0, which passes)
+  const int nblk = p.k >> 7, row = threadIdx.x >> 1, h = threadIdx.x & 1;
+  const int ar = row < mrows ? act_row(p, m0 + row) : -1;
+  const rsrc_t r = make_rsrc(p.a_scales, (uint32_t)p.a_rows * (uint32_t)nblk * 4u);
+  const uint32_t base = ar >= 0 ? (uint32_t)ar * (uint32_t)nblk * 4u : kOffNone;
+  bool ok = true;
+  for (int b0 = 4 * h; b0 < nblk; b0 += 32) {
+    f32x4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = b0 + 8 * j;
+      v[j] = __builtin_bit_cast(f32x4, buf_load_x4(r, base != kOffNone && b < nblk ? base + 4u * b : kOffNone));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // blocks past the row's end read the next row's scales: harmless, the test only gets stricter
+        const float x = v[j][e];
+        ok &= x == 0.0f || (x >= 0x1p-15f && x <= 128.0f);
+      }
+  }
+  return __builtin_amdgcn_readfirstlane(__syncthreads_and(ok)) != 0;
 }
 
 __global__ __launch_bounds__(kThreads, 2) void gemm_prefill_kernel(GemmArgs p, int ntn) {
@@ -429,8 +492,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill_kernel(GemmArgs p, i
   // are computed.
   const int nmt = (mrows + 31) >> 5;
   if (ex.kind == kNV) {
-    if (nmt <= 2) {
-      run_tile<kNV, 2>(p, ex, m0, mrows, n0, st);
+    if (f16_operands_exact(p, m0, mrows)) {
+      if (nmt <= 2) {
+        run_tile<kNV16, 2>(p, ex, m0, mrows, n0, st);
+      } else {
+        run_tile<kNV16, 4>(p, ex, m0, mrows, n0, st);
+      }
     } else {
       run_tile<kNV, 4>(p, ex, m0, mrows, n0, st);
     }
