@@ -253,3 +253,19 @@ def test_config4_sampled(orc, config4_dev):
         cols = np.concatenate([cols, (np.arange(lo, hi)[:64] * 37) % gd.n])
     worst = grouped_check(gd, orc, out, (rows, cols))
     print(f"config4 worst err / (2^-24 sum|p|) over {rows.size} samples = {worst:.2f}")
+
+
+@pytest.mark.parametrize("factor", [1.0, 1e-5, 3e5])
+def test_tiles_outside_the_f16_range(orc, schedule, factor):
+    # The tiled kernel feeds NVFP4 tiles to f16 MFMAs only when every activation block scale of the
+    # tile lies in [2^-15, 2^7]; a few rows scaled by 1e-5 (scales near 2^-18) or 3e5 (near 2^10)
+    # send their tiles to the bf16 route while the other tiles stay on f16.  Every tile must meet
+    # the same bound.
+    wl = workloads.grouped_random(77, 400, 4, 2, 96, 512, kinds=[NV] * 4)
+    wl.x[::37] *= np.float32(factor)
+    gd = GroupedDevice(wl)
+    _, scales, out = gd.step()
+    s = scales.cpu().numpy()
+    if factor != 1.0:
+        assert ((s < 2.0 ** -15) | (s > 2.0 ** 7)).any()
+    grouped_check(gd, orc, out)
