@@ -34,8 +34,9 @@
 // the LDS reads and weight dequantization of step s+1 are issued, and the conversion of the next
 // block's activations into the other LDS stage is spread over the first four steps.  One barrier
 // per block.  Two workgroups share a compute unit (256 registers per lane, 139 KB of LDS), so each
-// SIMD interleaves two independent wavefronts.  An expert's last row slice computes only 64 rows
-// when it holds no more, which keeps the padding of the skewed per-expert row counts small.
+// SIMD interleaves two independent wavefronts.  On the f16 route an expert's last row slice
+// computes only its occupied 32-row MFMA tiles (32, 64 or 96 rows), which keeps the padding of the
+// skewed per-expert row counts small; the bf16 route computes whole slices.
 // Activations are staged with 8 lanes per row, so each 16-byte load instruction touches 8 cache
 // lines.
 //
@@ -493,8 +494,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill_kernel(GemmArgs p, i
   const int nmt = (mrows + 31) >> 5;
   if (ex.kind == kNV) {
     if (f16_operands_exact(p, m0, mrows)) {
-      if (nmt <= 2) {
+      if (nmt == 1) {
+        run_tile<kNV16, 1>(p, ex, m0, mrows, n0, st);
+      } else if (nmt == 2) {
         run_tile<kNV16, 2>(p, ex, m0, mrows, n0, st);
+      } else if (nmt == 3) {
+        run_tile<kNV16, 3>(p, ex, m0, mrows, n0, st);
       } else {
         run_tile<kNV16, 4>(p, ex, m0, mrows, n0, st);
       }
