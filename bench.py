@@ -128,10 +128,11 @@ def main():
     # before the rate settles; the default warm-up covers that so the timed steps see the steady
     # state.
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="config3", choices=["config3", "config4", "chain4"],
+    ap.add_argument("--workload", default="config3", choices=["config3", "config4", "chain4", "w4a4"],
                     help="config3: grouped decode GEMM; config4: grouped prefill GEMM; chain4: the "
                          "whole prefill expert layer from router logits (top-k, packing, gate/up GEMM, "
-                         "swiglu+quant, down GEMM, combine)")
+                         "swiglu+quant, down GEMM, combine); w4a4: the W4A4 variant on one NVFP4 "
+                         "expert of the prefill shape, beside the FP8 path on the same inputs")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 disables it)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -155,6 +156,8 @@ def main():
 
     if args.workload == "chain4":
         return run_chain(args, torch, fp4, dev)
+    if args.workload == "w4a4":
+        return run_w4a4(args, torch, fp4, dev)
 
     t0 = time.perf_counter()
     wl = workloads.config3() if args.workload == "config3" else workloads.config4()
@@ -348,6 +351,62 @@ def run_chain(args, torch, fp4, dev):
                    "swiglu_quant_gbs": round(sw_gbs, 1), "combine_gbs": round(cb_gbs, 1)},
         "roofline": {"bound": "mfma", "achieved": round(tf_up, 1), "peak": MFMA_PEAK_TFLOPS["f16"],
                      "unit": "TFLOP/s", "frac": round(tf_up / MFMA_PEAK_TFLOPS["f16"], 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def run_w4a4(args, torch, fp4, dev):
+    """The W4A4 variant: act_quant_fp4 (two-level) + w4a4_gemm on one NVFP4 expert of the prefill
+    gate/up shape (n = 4096, k = 7168) over 8192 tokens of 0.1 U[0, 1) activations, timed beside
+    act_quant_fp8 + fp4_expert_gemm on the same activations and weights."""
+    T, n, k = 8192, 4096, 7168
+    x_np, ex = workloads.w4a4_case(7, T, n, k, "uniform")
+    x = torch.from_numpy(x_np).to(dev)
+    w = torch.from_numpy(ex.w).to(dev)
+    sc = torch.from_numpy(ex.s).to(dev)
+    codes4 = torch.empty((T, k // 2), dtype=torch.uint8, device=dev)
+    micro = torch.empty((T, k // 16), dtype=torch.uint8, device=dev)
+    rs = torch.empty(T, dtype=torch.float32, device=dev)
+    codes8 = torch.empty((T, k), dtype=torch.uint8, device=dev)
+    scales8 = torch.empty((T, k // 128), dtype=torch.float32, device=dev)
+    out = torch.empty((T, n), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    legs = {
+        "act_quant_fp4": lambda: fp4.act_quant_fp4(x, True, None, codes4, micro, rs, stream=stream),
+        "w4a4_gemm": lambda: fp4.w4a4_gemm(codes4, micro, rs, w, sc, ex.scale2, out=out, stream=stream),
+        "act_quant_fp8": lambda: fp4.act_quant_fp8(x, codes8, scales8, stream=stream),
+        "fp4_expert_gemm": lambda: fp4.fp4_expert_gemm(codes8, scales8, w, sc, ex.scale2, workloads.NVFP4, out=out,
+                                                       stream=stream),
+    }
+    for _ in range(args.warmup):
+        for f in legs.values():
+            f()
+    torch.cuda.synchronize()
+    K = args.steps
+    us = {}
+    for name, f in legs.items():
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+        ev[0].record(stream)
+        for i in range(K):
+            f()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        us[name] = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(K)])) * 1e3
+    flops = 2.0 * T * n * k
+    tf = flops / (us["w4a4_gemm"] * 1e-6) / 1e12
+    tf8 = flops / (us["fp4_expert_gemm"] * 1e-6) / 1e12
+    log("  " + ", ".join(f"{nm} {u:.1f} us" for nm, u in us.items()))
+    log(f"W4A4 GEMM {tf:.1f} TFLOP/s; FP8 x FP4 GEMM on the same shape {tf8:.1f} TFLOP/s")
+    step_ms = (us["act_quant_fp4"] + us["w4a4_gemm"]) / 1e3
+    result = {
+        "metric": METRIC, "value": round(tf, 4), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp4xfp4->f32", "data": "synthetic",
+        "config": {"workload": "w4a4: one NVFP4 expert n=4096 k=7168, 8192 tokens of 0.1 U[0,1), two-level E2M1",
+                   "us": {nm: round(u, 2) for nm, u in us.items()}, "fp8_path_tflops": round(tf8, 1)},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_PEAK_TFLOPS["f16"],
+                     "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_TFLOPS["f16"], 4), "traffic": None},
         "cpu_baseline": None,
     }
     print(json.dumps(result), flush=True)

@@ -236,8 +236,23 @@ int w4a4_gemm(const uint8_t* a_codes, const uint8_t* a_micro, const float* a_row
   if (g == 0) return ok();
   if (!a_codes || !a_micro || !a_row_scale || !w_packed || !w_scales || !out || (k_res > 0 && (!x || !res_idx)))
     return fail(FP4MOE_EINVAL, "%s: NULL buffer with g > 0", what);
-  return launched(fp4moe::launch_w4a4_gemm(a_codes, a_micro, a_row_scale, w_packed, w_scales, scale2, x, res_idx,
-                                           k_res, out, g, n, k, stream),
+  fp4moe::GemmArgs a{};
+  a.a_codes = a_codes;
+  a.a_micro = a_micro;
+  a.a_row_scale = a_row_scale;
+  a.a_rows = g;
+  a.num_experts = 1;
+  a.total_rows = g;
+  a.w = w_packed;
+  a.s = w_scales;
+  a.scale2 = scale2;
+  a.kind = FP4MOE_NVFP4;
+  a.out = out;
+  a.n = n;
+  a.k = k;
+  if (int rc = launched(fp4moe::launch_gemm_prefill(a, stream), what)) return rc;
+  if (k_res == 0) return ok();
+  return launched(fp4moe::launch_w4a4_residual(x, res_idx, k_res, w_packed, w_scales, scale2, out, g, n, k, stream),
                   what);
 }
 

@@ -70,12 +70,14 @@ constexpr int kUnroll = 2;                   // blocks per loop iteration (a mul
 constexpr int kNV = 0;
 constexpr int kMX = 1;
 constexpr int kNV16 = 2;                     // NVFP4 on f16 operands (tiles whose activation scales allow it)
+constexpr int kW4 = 3;                       // NVFP4 weights x W4A4 activations (E2M1 x UE4M3), f16 operands
 
 __host__ __device__ constexpr bool is_nv(int kind) { return kind != kMX; }
 
 // Operand type of the MFMAs: bf16, or f16 for kNV16.
 template <int KIND> struct OpT { typedef bf16x8 T; };
 template <> struct OpT<kNV16> { typedef h16x8 T; };
+template <> struct OpT<kW4> { typedef h16x8 T; };
 
 struct Stage {
   uint8_t a[kBM * kARow];                    // bf16 activations (as folded), [row][128 k]
@@ -136,8 +138,21 @@ struct Rsrc {
   rsrc_t w, s, a, as;
 };
 
+template <int KIND>
 __device__ __forceinline__ void stage_load(const Rsrc& r, const AOffs& o, int b, int nblk, StageRegs& d) {
   const bool valid = b < nblk;
+  if constexpr (KIND == kW4) {
+    // W4A4: 8 nibble bytes (16 elements, one micro-scale group) and that group's micro-scale byte
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint2 v = buf_load_x2(r.a, valid && o.a[i] != kOffNone ? o.a[i] + (uint32_t)b * 64u : kOffNone);
+      d.a[i] = u32x4{v.x, v.y, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      d.as[i] = u2f(buf_load_u8(r.as, valid && o.as[i] != kOffNone ? o.as[i] + (uint32_t)b * 8u : kOffNone));
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) d.a[i] = buf_load_x4(r.a, valid ? o.a[i] + (uint32_t)b * 128u : kOffNone);
 #pragma unroll
@@ -171,6 +186,17 @@ __device__ __forceinline__ void w_load(const Rsrc& r, const uint32_t (&wo)[kNT],
 template <int KIND>
 __device__ __forceinline__ void stage_store_q(Stage& st, const StageRegs& d, int i) {
   const int tid = threadIdx.x, c = tid & 7, row = (tid >> 3) + 32 * i;
+  if constexpr (KIND == kW4) {
+    // 16 E2M1 values times their UE4M3 micro-scale as f16 (at most 5 significant bits: exact)
+    const _Float16 ms = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)f2u(d.as[i]), 0);
+    const bool swap = (c >> 2) & 1;
+    const h16x8 first = e2m1x8_scaled_f16(swap ? d.a[i][1] : d.a[i][0], ms);
+    const h16x8 second = e2m1x8_scaled_f16(swap ? d.a[i][0] : d.a[i][1], ms);
+    uint8_t* dst = st.a + row * kARow + 32 * c;
+    *reinterpret_cast<h16x8*>(dst + (swap ? 16 : 0)) = first;
+    *reinterpret_cast<h16x8*>(dst + (swap ? 0 : 16)) = second;
+    return;
+  }
   // lanes c >= 4 write their upper half first: the code dwords are swapped before conversion
   const bool swap = (c >> 2) & 1;
   const uint32_t src[4] = {swap ? d.a[i][2] : d.a[i][0], swap ? d.a[i][3] : d.a[i][1],
@@ -203,7 +229,7 @@ __device__ __forceinline__ void stage_store_q(Stage& st, const StageRegs& d, int
 template <int KIND, int S>
 __device__ __forceinline__ typename OpT<KIND>::T dequant_step(const WRegs& w, int nt) {
   const uint32_t q = w.w[nt][S >> 2][S & 3];
-  if constexpr (KIND == kNV16) {
+  if constexpr (KIND == kNV16 || KIND == kW4) {
     // E2M1 -> f16 (exact), times the E4M3 group scale as f16 (exact; at most 5 significant bits)
     return e2m1x8_scaled_f16(q, (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)w.s[nt], S >> 1));
   } else if constexpr (KIND == kNV) {
@@ -283,7 +309,7 @@ __device__ __forceinline__ void run_block(const Stage& cur, Stage& nxt, const WR
       for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = mfma32x32x16(f.a[mt], f.b[nt], acc[mt][nt]);
     if (s == 4) {
       __builtin_amdgcn_sched_barrier(0);
-      stage_load(r, ao, b + 1 + kADepth, nblk, load_dst);
+      stage_load<KIND>(r, ao, b + 1 + kADepth, nblk, load_dst);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (s == kSteps - 1) {
@@ -309,16 +335,26 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
   Rsrc r;
   r.w = make_rsrc(ex.w, (uint32_t)p.n * (uint32_t)(k / 2));
   r.s = make_rsrc(ex.s, (uint32_t)p.n * (uint32_t)(k / GS));
-  r.a = make_rsrc(p.a_codes, (uint32_t)p.a_rows * (uint32_t)k);
-  r.as = make_rsrc(p.a_scales, (uint32_t)p.a_rows * (uint32_t)nblk * 4u);
+  if constexpr (KIND == kW4) {
+    r.a = make_rsrc(p.a_codes, (uint32_t)p.a_rows * (uint32_t)(k / 2));
+    r.as = make_rsrc(p.a_micro, (uint32_t)p.a_rows * (uint32_t)(k / 16));
+  } else {
+    r.a = make_rsrc(p.a_codes, (uint32_t)p.a_rows * (uint32_t)k);
+    r.as = make_rsrc(p.a_scales, (uint32_t)p.a_rows * (uint32_t)nblk * 4u);
+  }
 
   AOffs ao;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = (tid >> 3) + 32 * i;
     const int ar = row < mrows ? act_row(p, m0 + row) : -1;
-    ao.a[i] = ar >= 0 ? (uint32_t)ar * (uint32_t)k + 16u * (tid & 7) : kOffNone;
-    ao.as[i] = ar >= 0 ? (uint32_t)ar * (uint32_t)nblk * 4u : kOffNone;
+    if constexpr (KIND == kW4) {
+      ao.a[i] = ar >= 0 ? (uint32_t)ar * (uint32_t)(k / 2) + 8u * (tid & 7) : kOffNone;
+      ao.as[i] = ar >= 0 ? (uint32_t)ar * (uint32_t)(k / 16) + (uint32_t)(tid & 7) : kOffNone;
+    } else {
+      ao.a[i] = ar >= 0 ? (uint32_t)ar * (uint32_t)k + 16u * (tid & 7) : kOffNone;
+      ao.as[i] = ar >= 0 ? (uint32_t)ar * (uint32_t)nblk * 4u : kOffNone;
+    }
   }
   uint32_t wo[kNT], so[kNT];
 #pragma unroll
@@ -340,11 +376,11 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
   // then the weights of block b+kWDepth).  Loads past the last block return zeros.
   StageRegs sr[kADepth];
   WRegs wr[kWDepth];
-  stage_load(r, ao, 0, nblk, sr[0]);
+  stage_load<KIND>(r, ao, 0, nblk, sr[0]);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 1; j < kADepth; ++j) {
-    stage_load(r, ao, j, nblk, sr[j]);
+    stage_load<KIND>(r, ao, j, nblk, sr[j]);
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
@@ -355,7 +391,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
 #pragma unroll
   for (int q = 0; q < 4; ++q) stage_store_q<KIND>(st[0], sr[0], q);
   __builtin_amdgcn_sched_barrier(0);
-  stage_load(r, ao, kADepth, nblk, sr[0]);
+  stage_load<KIND>(r, ao, kADepth, nblk, sr[0]);
   __builtin_amdgcn_sched_barrier(0);
   w_load<KIND>(r, wo, so, kWDepth - 1, nblk, wr[kWDepth - 1]);
   __builtin_amdgcn_sched_barrier(0);
@@ -388,11 +424,13 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
       const int row = 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3);
       if (row < mrows) {
         const int prow = m0 + row;
-        const bool bad = act_row(p, prow) < 0;
+        const int arow = act_row(p, prow);
+        const bool bad = arow < 0;
+        const float rsc = (KIND == kW4 && !bad) ? p.a_row_scale[arow] : 1.0f;
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
           const int col = n0 + wave * kWaveCols + 32 * nt + c32;
-          if (col < p.n) p.out[(size_t)prow * p.n + col] = bad ? __builtin_nanf("") : acc[mt][nt][v] * post;
+          if (col < p.n) p.out[(size_t)prow * p.n + col] = bad ? __builtin_nanf("") : acc[mt][nt][v] * (post * rsc);
         }
       }
     }
@@ -492,7 +530,25 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill_kernel(GemmArgs p, i
   // The last slice of an expert may hold fewer than 128 rows: only its occupied 32-row MFMA tiles
   // are computed.
   const int nmt = (mrows + 31) >> 5;
-  if (ex.kind == kNV) {
+  if (p.a_micro) {
+    // W4A4 activations: always exact in f16; NVFP4 weights only (other kinds give NaN below)
+    if (ex.kind == kNV) {
+      if (nmt == 1) {
+        run_tile<kW4, 1>(p, ex, m0, mrows, n0, st);
+      } else if (nmt == 2) {
+        run_tile<kW4, 2>(p, ex, m0, mrows, n0, st);
+      } else if (nmt == 3) {
+        run_tile<kW4, 3>(p, ex, m0, mrows, n0, st);
+      } else {
+        run_tile<kW4, 4>(p, ex, m0, mrows, n0, st);
+      }
+    } else {
+      for (int i = threadIdx.x; i < mrows * kBN; i += kThreads) {
+        const int rr = m0 + i / kBN, col = n0 + i % kBN;
+        if (col < p.n) p.out[(size_t)rr * p.n + col] = __builtin_nanf("");
+      }
+    }
+  } else if (ex.kind == kNV) {
     if (f16_operands_exact(p, m0, mrows)) {
       if (nmt == 1) {
         run_tile<kNV16, 1>(p, ex, m0, mrows, n0, st);

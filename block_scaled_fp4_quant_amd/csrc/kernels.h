@@ -28,6 +28,10 @@ struct GemmArgs {
   float* out;
   int32_t n;
   int32_t k;
+  // W4A4 activations (tiled kernel only): a_codes are E2M1 nibbles [a_rows, k/2] with UE4M3
+  // micro-scales a_micro [a_rows, k/16] and row scales a_row_scale [a_rows]; a_scales is unused.
+  const uint8_t* a_micro;
+  const float* a_row_scale;
 };
 
 hipError_t launch_act_quant(const float* x, uint8_t* codes, float* scales, int64_t ngroups,
@@ -63,16 +67,16 @@ hipError_t launch_gemm_bf16(const uint16_t* a, const uint16_t* w, float* out, in
                             hipStream_t stream);
 
 // The W4A4 NVFP4 variant (w4a4.hip): the two-level E2M1 activation quantizer (k % 128 == 0, at most
-// 64 kept-out channels), the loudest-channel selection (k <= 8192, one block), and the FP4 x FP4 GEMM
-// with the kept channels added exactly.
+// 64 kept-out channels), the loudest-channel selection (k <= 8192, one block), and the exact addition
+// of the kept channels after the GEMM (the GEMM itself is launch_gemm_prefill with a_micro set).
 hipError_t launch_act_quant_fp4(const float* x, const int32_t* skip, int32_t n_skip, int32_t rows, int32_t k,
                                 int32_t two_level, uint8_t* codes, uint8_t* micro, float* row_scale,
                                 hipStream_t stream);
 hipError_t launch_loud_channels(const float* x, int32_t rows, int32_t k, int32_t k_res, int32_t* idx,
                                 hipStream_t stream);
-hipError_t launch_w4a4_gemm(const uint8_t* a_codes, const uint8_t* a_micro, const float* a_rs, const uint8_t* w,
-                            const uint8_t* s, float scale2, const float* x, const int32_t* res_idx, int32_t k_res,
-                            float* out, int32_t g, int32_t n, int32_t k, hipStream_t stream);
+hipError_t launch_w4a4_residual(const float* x, const int32_t* res_idx, int32_t k_res, const uint8_t* w,
+                                const uint8_t* s, float scale2, float* out, int32_t g, int32_t n, int32_t k,
+                                hipStream_t stream);
 
 // Row-streaming kernel for few rows per expert (decode): every expert's weights are read once per
 // pass of 32 rows.

@@ -10,20 +10,19 @@
 //   nearest even, 0 for an all-zero sub-block;  code = E2M1((x / rs) / micro), nearest grid point,
 //   ties to the even code, magnitude capped at 6, 0 when micro is 0.  Kept-out channels count as 0.
 // GEMM: out[r, c] = rs[r] * scale2 * sum_k (E2M1(a) * micro) * (E2M1(w) * E4M3(ws)) + sum over kept
-//   channels j of x[r, j] * (E2M1(w[c, j]) * f32(E4M3(ws) * scale2)).  Both products E2M1 x E4M3 have
-//   at most 5 significant bits, so the bf16 MFMA operands are exact; the row and tensor scales
-//   multiply the f32 sum (exact for power-of-two scale2).
+//   channels j of x[r, j] * (E2M1(w[c, j]) * f32(E4M3(ws) * scale2)).  The first term runs on the
+//   tiled matrix-core kernel of the FP8 path (gemm_prefill.hip) with W4A4 activation staging: both
+//   products E2M1 x E4M3 have at most 5 significant bits, so its f16 operands are exact, and the row
+//   and tensor scales multiply the f32 sum (exact for power-of-two scale2).  The kept channels are
+//   added by w4a4_residual_kernel.
 //
 // Layouts: codes u8 [rows, k/2] (even k in the low nibble), micro u8 [rows, k/16], rs f32 [rows].
-// None of this is tuned: one wavefront per row in the quantizer, one per 32 x 32 output tile in the
-// GEMM, operands dequantized in registers straight from global memory.
+// The quantizer takes one wavefront per row; the channel selection one block.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace fp4moe {
 namespace {
-
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kW4Threads = 256;
 constexpr int kMaxSkip = 64;
@@ -149,64 +148,28 @@ __global__ __launch_bounds__(kLoudThreads) void loud_channels_kernel(const float
   }
 }
 
-// 8 E2M1 codes (4 bytes) times a scale, as bf16 (exact: at most 5 significant bits).
-__device__ __forceinline__ bf16x8 fp4x8_scaled_bf16(uint32_t nib, float scale) {
-  bf16x8 out;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) out[e] = (__bf16)(e2m1_value((nib >> (4 * e)) & 0xFu) * scale);
-  return out;
-}
-
-// out = rs[r] * scale2 * (A W^T) [+ kept channels].  Wavefront (tm, tn): rows 32 tm .., columns
-// 32 tn ...  32x32x16 bf16 MFMA operand layout: lane l supplies row (column) l % 32 and
-// k = 8 (l / 32) .. +8, one 16-element scale group; the result holds column l % 32 and rows
-// 8 (v / 4) + 4 (l / 32) + v % 4.
-__global__ __launch_bounds__(kW4Threads) void w4a4_gemm_kernel(
-    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_micro, const float* __restrict__ a_rs,
-    const uint8_t* __restrict__ w, const uint8_t* __restrict__ s, float scale2, const float* __restrict__ x,
-    const int32_t* __restrict__ res_idx, int32_t k_res, float* __restrict__ out, int32_t g, int32_t n, int32_t k,
-    int32_t tiles_n) {
-  const int lane = threadIdx.x & 63;
-  const int64_t tile = (int64_t)blockIdx.x * (kW4Threads / 64) + (threadIdx.x >> 6);
-  const int32_t tm = (int32_t)(tile / tiles_n), tn = (int32_t)(tile % tiles_n);
-  if ((int64_t)tm * 32 >= g) return;                 // uniform per wavefront
-  const rsrc_t rac = make_rsrc(a_codes, (uint32_t)g * (uint32_t)(k / 2));
-  const rsrc_t ram = make_rsrc(a_micro, (uint32_t)g * (uint32_t)(k / 16));
-  const rsrc_t rwc = make_rsrc(w, (uint32_t)n * (uint32_t)(k / 2));
-  const rsrc_t rws = make_rsrc(s, (uint32_t)n * (uint32_t)(k / 16));
-  const int row = tm * 32 + (lane & 31), col = tn * 32 + (lane & 31), half = lane >> 5;
-  const uint32_t oac = row < g ? (uint32_t)row * (uint32_t)(k / 2) + 4u * half : kOffNone;
-  const uint32_t oam = row < g ? (uint32_t)row * (uint32_t)(k / 16) : kOffNone;
-  const uint32_t owc = col < n ? (uint32_t)col * (uint32_t)(k / 2) + 4u * half : kOffNone;
-  const uint32_t ows = col < n ? (uint32_t)col * (uint32_t)(k / 16) : kOffNone;
-  f32x16 acc = {};
-  for (int32_t k0 = 0; k0 < k; k0 += 16) {
-    const uint32_t q = (uint32_t)k0 / 16u;
-    const uint32_t an = buf_load_u32(rac, oac == kOffNone ? kOffNone : oac + 8u * q);
-    const uint32_t am = buf_load_u8(ram, oam == kOffNone ? kOffNone : oam + q);
-    const uint32_t wn = buf_load_u32(rwc, owc == kOffNone ? kOffNone : owc + 8u * q);
-    const uint32_t ws = buf_load_u8(rws, ows == kOffNone ? kOffNone : ows + q);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp4x8_scaled_bf16(an, e4m3_value(am)),
-                                                  fp4x8_scaled_bf16(wn, e4m3_value(ws)), acc, 0, 0, 0);
+// The kept channels, added to the W4A4 GEMM's output: out[r, c] += sum_j x[r, j] * W(c, j) over the
+// channel list, W = E2M1 x f32(E4M3(ws) x scale2), one f32 FMA per term in list order.  One thread
+// per output; channel indices outside [0, k) add nothing.
+__global__ __launch_bounds__(kW4Threads) void w4a4_residual_kernel(const float* __restrict__ x,
+                                                                   const int32_t* __restrict__ res_idx,
+                                                                   int32_t k_res, const uint8_t* __restrict__ w,
+                                                                   const uint8_t* __restrict__ s, float scale2,
+                                                                   float* __restrict__ out, int32_t g, int32_t n,
+                                                                   int32_t k) {
+  const int64_t i = (int64_t)blockIdx.x * kW4Threads + threadIdx.x;
+  if (i >= (int64_t)g * n) return;
+  const int64_t r = i / n, col = i - r * n;
+  float o = out[i];
+  for (int j = 0; j < k_res; ++j) {
+    const int32_t c = res_idx[j];
+    if (c < 0 || c >= k) continue;
+    const uint32_t byte = w[col * (k / 2) + c / 2];
+    const float wv = e2m1_value((c & 1) ? (byte >> 4) : (byte & 0xFu)) *
+                     (e4m3_value(s[col * (k / 16) + c / 16]) * scale2);
+    o = fmaf(x[r * k + c], wv, o);
   }
-  if (col >= n) return;
-  // the kept channels of this lane's column: W(col, j) = E2M1 x f32(E4M3(ws) x scale2)
-  const float post = scale2;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int r = tm * 32 + 8 * (v / 4) + 4 * half + v % 4;
-    if (r >= g) continue;
-    float o = acc[v] * a_rs[r] * post;
-    for (int j = 0; j < k_res; ++j) {
-      const int32_t c = res_idx[j];
-      if (c < 0 || c >= k) continue;                 // not a channel: no term
-      const uint32_t byte = w[(int64_t)col * (k / 2) + c / 2];
-      const float wv = e2m1_value((c & 1) ? (byte >> 4) : (byte & 0xFu)) *
-                       (e4m3_value(s[(int64_t)col * (k / 16) + c / 16]) * scale2);
-      o = fmaf(x[(int64_t)r * k + c], wv, o);
-    }
-    out[(int64_t)r * n + col] = o;
-  }
+  out[i] = o;
 }
 
 }  // namespace
@@ -226,14 +189,12 @@ hipError_t launch_loud_channels(const float* x, int32_t rows, int32_t k, int32_t
   return hipGetLastError();
 }
 
-hipError_t launch_w4a4_gemm(const uint8_t* a_codes, const uint8_t* a_micro, const float* a_rs, const uint8_t* w,
-                            const uint8_t* s, float scale2, const float* x, const int32_t* res_idx, int32_t k_res,
-                            float* out, int32_t g, int32_t n, int32_t k, hipStream_t stream) {
-  const int32_t tiles_n = (n + 31) / 32;
-  const int64_t tiles = (int64_t)((g + 31) / 32) * tiles_n;
-  const int64_t blocks = (tiles + kW4Threads / 64 - 1) / (kW4Threads / 64);
-  hipLaunchKernelGGL(w4a4_gemm_kernel, dim3((uint32_t)blocks), dim3(kW4Threads), 0, stream, a_codes, a_micro, a_rs,
-                     w, s, scale2, x, res_idx, k_res, out, g, n, k, tiles_n);
+hipError_t launch_w4a4_residual(const float* x, const int32_t* res_idx, int32_t k_res, const uint8_t* w,
+                                const uint8_t* s, float scale2, float* out, int32_t g, int32_t n, int32_t k,
+                                hipStream_t stream) {
+  const int64_t items = (int64_t)g * n;
+  hipLaunchKernelGGL(w4a4_residual_kernel, dim3((uint32_t)((items + kW4Threads - 1) / kW4Threads)), dim3(kW4Threads),
+                     0, stream, x, res_idx, k_res, w, s, scale2, out, g, n, k);
   return hipGetLastError();
 }
 
