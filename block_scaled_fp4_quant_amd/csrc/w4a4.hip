@@ -17,7 +17,8 @@
 //   added by w4a4_residual_kernel.
 //
 // Layouts: codes u8 [rows, k/2] (even k in the low nibble), micro u8 [rows, k/16], rs f32 [rows].
-// The quantizer takes one wavefront per row; the channel selection one block.
+// The quantizer takes one block per row with the row in registers (k <= 8192; one wavefront per row
+// and two passes above that); the channel selection one block.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -106,6 +107,65 @@ __global__ __launch_bounds__(kW4Threads) void act_quant_fp4_kernel(const float* 
   }
 }
 
+// One block per row with the row held in registers (k <= 8192): thread t owns the 16-byte pieces
+// t + 256 j of the row, so every quad of threads owns one 16-element sub-block.  One read of x.
+constexpr int kRowPieces = 8;                        // 16-byte pieces per thread: k <= 256 x 8 x 4
+
+template <int NP>
+__global__ __launch_bounds__(kW4Threads) void act_quant_fp4_row_kernel(const float* __restrict__ x,
+                                                                       const int32_t* __restrict__ skip,
+                                                                       int32_t n_skip, int32_t rows, int32_t k,
+                                                                       int32_t two_level, uint8_t* __restrict__ codes,
+                                                                       uint8_t* __restrict__ micro,
+                                                                       float* __restrict__ row_scale) {
+  __shared__ int32_t s_skip[kMaxSkip];
+  __shared__ float s_max[kW4Threads / 64];
+  for (int i = threadIdx.x; i < n_skip; i += kW4Threads) s_skip[i] = skip[i];
+  __syncthreads();
+  const int64_t r = blockIdx.x;
+  const float* xr = x + r * k;
+  const int npieces = k / 4;
+  f32x4 v[NP];
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int piece = threadIdx.x + kW4Threads * j;
+    v[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (piece < npieces) {
+      v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(xr) + piece);
+      for (int i = 0; i < n_skip; ++i) {
+        const int d = s_skip[i] - 4 * piece;
+        if (d >= 0 && d < 4) v[j][d] = 0.0f;
+      }
+    }
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[j][0]), fabsf(v[j][1])), fmaxf(fabsf(v[j][2]), fabsf(v[j][3]))));
+  }
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+  const float rs = (two_level && amax > 0.0f) ? amax / 2688.0f : 1.0f;
+  if (threadIdx.x == 0) row_scale[r] = rs;
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int piece = threadIdx.x + kW4Threads * j;
+    // uniform per quad: a sub-block is 4 pieces and npieces is a multiple of 4
+    const float asub = quad_max(fmaxf(fmaxf(fabsf(v[j][0]), fabsf(v[j][1])), fmaxf(fabsf(v[j][2]), fabsf(v[j][3]))));
+    if (piece >= npieces) continue;
+    const float want = (asub / rs) / 6.0f;
+    const uint32_t mb = want > 0.0f ? e4m3_encode_pos(fminf(fmaxf(want, 0x1p-9f), 448.0f)) : 0u;
+    const float dec = e4m3_value(mb);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t c = dec > 0.0f ? e2m1_encode((v[j][e] / rs) / dec) : 0u;
+      packed |= c << (4 * e);
+    }
+    reinterpret_cast<uint16_t*>(codes + r * (k / 2))[piece] = (uint16_t)packed;
+    if ((threadIdx.x & 3) == 0) micro[r * (k / 16) + piece / 4] = (uint8_t)mb;
+  }
+}
+
 // One block: the k_res channels with the largest max |x| over rows, ties to the lower index.  Each
 // thread keeps the keys of channels tid + 1024 i (i < 8): high word the order-preserving bits of the
 // (non-negative) column max, low word ~channel.
@@ -177,6 +237,18 @@ __global__ __launch_bounds__(kW4Threads) void w4a4_residual_kernel(const float* 
 hipError_t launch_act_quant_fp4(const float* x, const int32_t* skip, int32_t n_skip, int32_t rows, int32_t k,
                                 int32_t two_level, uint8_t* codes, uint8_t* micro, float* row_scale,
                                 hipStream_t stream) {
+  const int per_thread = (k / 4 + kW4Threads - 1) / kW4Threads;
+  if (per_thread <= kRowPieces) {
+#define FP4MOE_AQ4(NP)                                                                                        \
+  hipLaunchKernelGGL(act_quant_fp4_row_kernel<NP>, dim3(rows), dim3(kW4Threads), 0, stream, x, skip, n_skip, rows, \
+                     k, two_level, codes, micro, row_scale)
+    if (per_thread <= 1) FP4MOE_AQ4(1);
+    else if (per_thread <= 2) FP4MOE_AQ4(2);
+    else if (per_thread <= 4) FP4MOE_AQ4(4);
+    else FP4MOE_AQ4(8);
+#undef FP4MOE_AQ4
+    return hipGetLastError();
+  }
   const int blocks = (rows + kW4Threads / 64 - 1) / (kW4Threads / 64);
   hipLaunchKernelGGL(act_quant_fp4_kernel, dim3(blocks), dim3(kW4Threads), 0, stream, x, skip, n_skip, rows, k,
                      two_level, codes, micro, row_scale);

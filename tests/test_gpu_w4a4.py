@@ -29,7 +29,8 @@ def gpu_w4a4(x, ex, two_level=True, k_res=0):
 
 
 @pytest.mark.parametrize("arm,T,k", [("uniform", 16, 1024), ("dyn", 33, 512), ("res", 128, 1024),
-                                     ("uniform", 1, 128), ("dyn", 7, 7168)])
+                                     ("uniform", 1, 128), ("dyn", 7, 7168), ("res", 9, 2048),
+                                     ("dyn", 3, 8320)])           # k > 8192: the two-pass kernel
 @pytest.mark.parametrize("two_level", [True, False])
 def test_quantizer_bit_exact(orc, arm, T, k, two_level):
     x, ex = workloads.w4a4_case(10 + T, T, 64, k, arm)
