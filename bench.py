@@ -133,6 +133,10 @@ def main():
                          "whole prefill expert layer from router logits (top-k, packing, gate/up GEMM, "
                          "swiglu+quant, down GEMM, combine); w4a4: the W4A4 variant on one NVFP4 "
                          "expert of the prefill shape, beside the FP8 path on the same inputs")
+    ap.add_argument("--gate-up", default="fused", choices=["fused", "unfused"],
+                    help="chain4 only: the gate/up GEMM with the activation and its quantization in "
+                         "its epilogue (fused), or the GEMM writing f32 gate/up values followed by "
+                         "swiglu_quant_fp8 (unfused)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 disables it)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -297,15 +301,24 @@ def run_chain(args, torch, fp4, dev):
     y = torch.empty((R, Hd), dtype=torch.float32, device=dev)
     out = torch.empty((T, Hd), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
-    names = ["route_topk", "route_pack", "act_quant", "gate/up GEMM", "swiglu+quant", "down GEMM", "combine"]
+    fused = args.gate_up == "fused"
+    if fused:
+        names = ["route_topk", "route_pack", "act_quant", "gate/up GEMM+swiglu+quant", "down GEMM", "combine"]
+    else:
+        names = ["route_topk", "route_pack", "act_quant", "gate/up GEMM", "swiglu+quant", "down GEMM", "combine"]
 
     def launches():
         yield lambda: fp4.route_softmax_topk(logits, top, ids=ids, weights=tw, stream=stream)
         yield lambda: fp4.route_pack(ids, E, tw, offsets, row_ids, pair_rows, rw, ws, stream=stream)
         yield lambda: fp4.act_quant_fp8(x, codes, scales, stream=stream)
-        yield lambda: fp4.fp4_grouped_gemm(codes, scales, row_ids, offsets, up[2], up[3], kinds, up[4],
-                                           2 * I, out=gu, stream=stream)
-        yield lambda: fp4.swiglu_quant_fp8(gu, ch.limit, row_weights=rw, codes=hc, scales=hs, stream=stream)
+        if fused:
+            yield lambda: fp4.fp4_grouped_gemm_swiglu_quant(codes, scales, row_ids, offsets, up[2], up[3], kinds,
+                                                            up[4], I, ch.limit, row_weights=rw, h_codes=hc,
+                                                            h_scales=hs, stream=stream)
+        else:
+            yield lambda: fp4.fp4_grouped_gemm(codes, scales, row_ids, offsets, up[2], up[3], kinds, up[4],
+                                               2 * I, out=gu, stream=stream)
+            yield lambda: fp4.swiglu_quant_fp8(gu, ch.limit, row_weights=rw, codes=hc, scales=hs, stream=stream)
         yield lambda: fp4.fp4_grouped_gemm(hc, hs, None, offsets, dn[2], dn[3], kinds, dn[4], Hd, out=y,
                                            stream=stream)
         yield lambda: fp4.moe_combine(y, pair_rows, out=out, stream=stream)
@@ -329,17 +342,20 @@ def run_chain(args, torch, fp4, dev):
     wall = time.perf_counter() - wall0
     step_ms = ev[0][0].elapsed_time(ev[K - 1][L]) / K
     part = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev])) for j in range(L)]
+    us = dict(zip(names, part))
     f_up, f_dn = 2.0 * R * Hd * 2 * I, 2.0 * R * I * Hd
     sw_bytes = R * I * (8 + 1) + R * (I // 128) * 4 + R * 4
     cb_bytes = R * Hd * 4 + T * Hd * 4 + T * top * 4
     log(f"timed {K} steps: wall {wall * 1e3 / K:.3f} ms/step, events {step_ms:.3f} ms/step")
     log("  " + ", ".join(f"{n} {p * 1e3:.1f} us" for n, p in zip(names, part)))
-    tf_up = f_up / (part[3] * 1e-3) / 1e12
-    sw_gbs = sw_bytes / (part[4] * 1e-3) / 1e9
-    cb_gbs = cb_bytes / (part[6] * 1e-3) / 1e9
-    log(f"gate/up {tf_up:.1f} TFLOP/s, down {f_dn / (part[5] * 1e-3) / 1e12:.1f} TFLOP/s, swiglu+quant "
-        f"{sw_gbs:.0f} GB/s ({sw_gbs / HBM_PEAK_GBS:.1%} of 8 TB/s), combine {cb_gbs:.0f} GB/s "
-        f"({cb_gbs / HBM_PEAK_GBS:.1%})")
+    t_up = us["gate/up GEMM+swiglu+quant" if fused else "gate/up GEMM"]
+    tf_up = f_up / (t_up * 1e-3) / 1e12
+    sw_gbs = None if fused else sw_bytes / (us["swiglu+quant"] * 1e-3) / 1e9
+    cb_gbs = cb_bytes / (us["combine"] * 1e-3) / 1e9
+    log(f"gate/up{' (fused with swiglu+quant)' if fused else ''} {tf_up:.1f} TFLOP/s, down "
+        f"{f_dn / (us['down GEMM'] * 1e-3) / 1e12:.1f} TFLOP/s, "
+        + ("" if fused else f"swiglu+quant {sw_gbs:.0f} GB/s ({sw_gbs / HBM_PEAK_GBS:.1%} of 8 TB/s), ")
+        + f"combine {cb_gbs:.0f} GB/s ({cb_gbs / HBM_PEAK_GBS:.1%})")
     value = (f_up + f_dn) / (step_ms * 1e-3) / 1e12
     result = {
         "metric": METRIC, "value": round(value, 4), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
@@ -347,8 +363,8 @@ def run_chain(args, torch, fp4, dev):
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8xfp4->f32", "data": "synthetic",
         "config": {"workload": ch.name, "tokens": int(T), "experts": int(E), "top_k": top,
                    "routed_rows": int(R), "hidden": int(Hd), "inter": int(I),
-                   "us": {n: round(p * 1e3, 2) for n, p in zip(names, part)},
-                   "swiglu_quant_gbs": round(sw_gbs, 1), "combine_gbs": round(cb_gbs, 1)},
+                   "gate_up": args.gate_up, "us": {n: round(p * 1e3, 2) for n, p in zip(names, part)},
+                   "swiglu_quant_gbs": None if fused else round(sw_gbs, 1), "combine_gbs": round(cb_gbs, 1)},
         "roofline": {"bound": "mfma", "achieved": round(tf_up, 1), "peak": MFMA_PEAK_TFLOPS["f16"],
                      "unit": "TFLOP/s", "frac": round(tf_up / MFMA_PEAK_TFLOPS["f16"], 4), "traffic": None},
         "cpu_baseline": None,

@@ -43,6 +43,9 @@ def lib() -> ctypes.CDLL:
         L.fp4_expert_gemm.restype = ctypes.c_int
         L.fp4_grouped_gemm.argtypes = [P, P, I32, P, P, I32, I32, P, P, P, P, P, I32, I32, P]
         L.fp4_grouped_gemm.restype = ctypes.c_int
+        L.fp4_grouped_gemm_swiglu_quant.argtypes = [P, P, I32, P, P, I32, I32, P, P, P, P, I32, I32, P, F32,
+                                                    P, P, P, P]
+        L.fp4_grouped_gemm_swiglu_quant.restype = ctypes.c_int
         L.route_softmax_topk.argtypes = [P, I32, I32, I32, I32, P, P, P]
         L.route_softmax_topk.restype = ctypes.c_int
         L.route_pack_workspace_size.argtypes = [I32, I32]
@@ -221,6 +224,58 @@ def fp4_grouped_gemm(a_codes, a_scales, row_ids, offsets, w_ptrs, s_ptrs, kinds,
                                   _ptr(scale2), _ptr(out), int(n), k, _stream(stream)),
            "fp4_grouped_gemm")
     return out
+
+
+def fp4_grouped_gemm_swiglu_quant(a_codes, a_scales, row_ids, offsets, w_ptrs, s_ptrs, kinds, scale2,
+                                  inter: int, limit: float, row_weights=None, h_codes=None, h_scales=None,
+                                  h_out=None, stream=None):
+    """The gate/up projection fused with the expert activation and its FP8 quantization: the
+    arguments of fp4_grouped_gemm (expert planes [2*inter, k/2], gate columns first) plus those of
+    swiglu_quant_fp8 -> (h_codes u8 [R, inter], h_scales f32 [R, inter/128]), R = len(row_ids)
+    (or h_codes' rows when row_ids is None).  h_out (f32 [R, inter]) receives h when given."""
+    _dev(a_codes, torch.uint8, "a_codes", 2)
+    _dev(a_scales, torch.float32, "a_scales", 2)
+    _dev(offsets, torch.int32, "offsets", 1)
+    _dev(w_ptrs, torch.int64, "w_ptrs", 1)
+    _dev(s_ptrs, torch.int64, "s_ptrs", 1)
+    _dev(kinds, torch.int32, "kinds", 1)
+    _dev(scale2, torch.float32, "scale2", 1)
+    a_rows, k = a_codes.shape
+    E = offsets.shape[0] - 1
+    if not (w_ptrs.shape[0] == s_ptrs.shape[0] == kinds.shape[0] == scale2.shape[0] == E):
+        raise ValueError("per-expert tables must all have num_experts entries")
+    inter = int(inter)
+    if inter <= 0 or inter % 128:
+        raise ValueError("inter must be a positive multiple of 128")
+    if row_ids is not None:
+        _dev(row_ids, torch.int32, "row_ids", 1)
+        R = row_ids.shape[0]
+    elif h_codes is not None:
+        R = h_codes.shape[0]
+    else:
+        raise ValueError("give row_ids or h_codes so that the number of packed rows is known")
+    if h_codes is None:
+        h_codes = torch.empty((R, inter), dtype=torch.uint8, device=a_codes.device)
+    if h_scales is None:
+        h_scales = torch.empty((R, inter // 128), dtype=torch.float32, device=a_codes.device)
+    _dev(h_codes, torch.uint8, "h_codes", 2)
+    _dev(h_scales, torch.float32, "h_scales", 2)
+    if h_codes.shape != (R, inter) or h_scales.shape != (R, inter // 128):
+        raise ValueError("h_codes/h_scales shapes must be [R, inter] and [R, inter/128]")
+    if row_weights is not None:
+        _dev(row_weights, torch.float32, "row_weights", 1)
+        if row_weights.shape != (R,):
+            raise ValueError("row_weights must be [R]")
+    if h_out is not None:
+        _dev(h_out, torch.float32, "h_out", 2)
+        if h_out.shape != (R, inter):
+            raise ValueError("h_out must be [R, inter]")
+    _check(lib().fp4_grouped_gemm_swiglu_quant(_ptr(a_codes), _ptr(a_scales), a_rows, _ptr(row_ids), _ptr(offsets),
+                                               E, R, _ptr(w_ptrs), _ptr(s_ptrs), _ptr(kinds), _ptr(scale2), inter,
+                                               k, _ptr(row_weights), float(limit), _ptr(h_codes), _ptr(h_scales),
+                                               _ptr(h_out), _stream(stream)),
+           "fp4_grouped_gemm_swiglu_quant")
+    return h_codes, h_scales
 
 
 # --------------------------------------------------------------------------- routing

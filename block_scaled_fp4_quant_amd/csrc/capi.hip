@@ -321,6 +321,52 @@ int fp4_grouped_gemm(const uint8_t* a_codes, const float* a_scales, int32_t a_ro
   return launched(launch_gemm(a, total_rows, num_experts, stream), "fp4_grouped_gemm");
 }
 
+int fp4_grouped_gemm_swiglu_quant(const uint8_t* a_codes, const float* a_scales, int32_t a_rows,
+                                  const int32_t* row_ids, const int32_t* offsets, int32_t num_experts,
+                                  int32_t total_rows, const uint64_t* w_ptrs, const uint64_t* s_ptrs,
+                                  const int32_t* kinds, const float* scale2, int32_t inter, int32_t k,
+                                  const float* row_weights, float limit, uint8_t* h_codes, float* h_scales,
+                                  float* h_out, hipStream_t stream) {
+  const char* what = "fp4_grouped_gemm_swiglu_quant";
+  if (a_rows < 0 || total_rows < 0)
+    return fail(FP4MOE_EINVAL, "%s: a_rows = %d, total_rows = %d must be >= 0", what, (int)a_rows, (int)total_rows);
+  if (num_experts <= 0) return fail(FP4MOE_EINVAL, "%s: num_experts = %d must be positive", what, (int)num_experts);
+  if (inter <= 0 || inter % 128 != 0 || inter > (1 << 29))
+    return fail(FP4MOE_EINVAL, "%s: inter = %d must be a positive multiple of 128 up to 2^29", what, (int)inter);
+  if (int rc = check_k(k, what)) return rc;
+  if (!(limit > 0.0f)) return fail(FP4MOE_EINVAL, "%s: limit must be > 0", what);
+  if (!row_ids && a_rows < total_rows)
+    return fail(FP4MOE_EINVAL, "%s: row_ids is NULL but a_rows = %d < total_rows = %d", what, (int)a_rows,
+                (int)total_rows);
+  if (total_rows == 0) return ok();
+  if (!a_codes || !a_scales || !offsets || !w_ptrs || !s_ptrs || !kinds || !scale2 || !h_codes || !h_scales)
+    return fail(FP4MOE_EINVAL, "%s: NULL buffer with total_rows > 0", what);
+  if ((reinterpret_cast<uintptr_t>(h_codes) | reinterpret_cast<uintptr_t>(h_out)) & 15)
+    return fail(FP4MOE_EINVAL, "%s: h_codes and h_out must be 16-byte aligned", what);
+  if (int rc = check_planes(a_rows, 2 * inter, k, what)) return rc;
+  fp4moe::GemmArgs a{};
+  a.a_codes = a_codes;
+  a.a_scales = a_scales;
+  a.row_ids = row_ids;
+  a.a_rows = a_rows;
+  a.offsets = offsets;
+  a.num_experts = num_experts;
+  a.total_rows = total_rows;
+  a.w_ptrs = w_ptrs;
+  a.s_ptrs = s_ptrs;
+  a.kinds = kinds;
+  a.scale2s = scale2;
+  a.n = 2 * inter;
+  a.k = k;
+  a.swiglu_inter = inter;
+  a.swiglu_limit = limit;
+  a.swiglu_row_w = row_weights;
+  a.h_codes = h_codes;
+  a.h_scales = h_scales;
+  a.h_out = h_out;
+  return launched(fp4moe::launch_gemm_prefill(a, stream), what);
+}
+
 int fp4moe_set_gemm_schedule(int32_t schedule) {
   if (schedule < FP4MOE_SCHEDULE_AUTO || schedule > FP4MOE_SCHEDULE_TILED)
     return fail(FP4MOE_EINVAL, "fp4moe_set_gemm_schedule: schedule = %d is not 0, 1 or 2", (int)schedule);

@@ -56,6 +56,15 @@ __device__ __forceinline__ float pow2_recip(float s) {
   return u2f((254u - (f2u(s) >> 23)) << 23);
 }
 
+// The expert activation between the gate/up and the down projection (swiglu with limit), in the
+// order of the f32 operations both of its kernels use: min/clamp, expf, one correctly rounded
+// division, then gate * sigmoid * up * weight.
+__device__ __forceinline__ float swiglu_one(float g, float u, float limit, float w) {
+  g = fminf(g, limit);
+  u = fminf(fmaxf(u, -limit), limit);
+  return g * (1.0f / (1.0f + expf(-g))) * u * w;
+}
+
 // --------------------------------------------------------------------------- cross-lane maximum
 // DPP controls (gfx9 encoding): quad permutations and row (16-lane) mirrors.
 constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]

@@ -324,7 +324,90 @@ __device__ __forceinline__ void run_block(const Stage& cur, Stage& nxt, const WR
   }
 }
 
-// One 128 x 256 output tile: packed rows [m0, m0 + mrows) of expert `ex`, columns [n0, n0 + 256).
+// Fused with the activation (swiglu_inter > 0), a tile covers the h columns [n0, n0 + 128), n0 = 128 q:
+// wavefront w computes gate columns n0 + 32 w .. +31 in its first MFMA column tile and the matching
+// up columns inter + n0 + 32 w .. +31 in its second, so that every lane holds each gate value next to
+// its up value.  Otherwise wavefront w computes columns n0 + 64 w .. +63.
+__device__ __forceinline__ int tile_col(const GemmArgs& p, int n0, int wave, int nt) {
+  return p.swiglu_inter ? (nt ? p.swiglu_inter : 0) + n0 + 32 * wave : n0 + kWaveCols * wave + 32 * nt;
+}
+
+// The fused activation epilogue of one tile (gate/up projection -> h = swiglu -> FP8 codes of h).  The
+// tile's 128 h columns of a row are exactly one act-quant group.  swiglu multiplies by the row weight
+// last, so every lane first forms t = swiglu with weight 1 from its gate/up pairs and stores t in LDS
+// (over the activation stages, which the main loop no longer needs), letting the accumulators die as
+// they are consumed.  Two threads then take a row, 64 values each: h = t * w, the row's amax (the
+// halves exchange theirs through LDS) and the codes, written as contiguous 16-byte stores.  f32
+// rounding is monotone, so max |t * w| = max |t| * |w| exactly; with the unfused route's operations
+// in its order everywhere else, codes, scales and h are bit-identical to the grouped GEMM followed by
+// swiglu_quant_fp8.  A packed row whose activation row is invalid gets what the unfused route gives
+// the grouped GEMM's NaN output: the activation of NaN gate and up values, in every column.
+constexpr int kHPitch = 128 + 4;                           // floats per row of the t exchange
+template <int NMT>
+__device__ __forceinline__ void swiglu_epilogue(const GemmArgs& p, int m0, int mrows, int n0, float post,
+                                                f32x16 (&acc)[kMT][kNT], Stage (&st)[2]) {
+  static_assert(kNT == 2 && kWaves == 4, "a wavefront holds 32 gate and 32 up columns");
+  static_assert(kThreads == 2 * kBM, "two threads quantize each row");
+  static_assert(sizeof(Stage) * 2 >= (kBM * kHPitch + 2 * kBM) * sizeof(float), "exchange space");
+  const int tid = threadIdx.x, lane = tid & 63, c32 = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int inter = p.swiglu_inter;
+  const float limit = p.swiglu_limit;
+  float* tx = reinterpret_cast<float*>(&st[0]);            // [128 rows][kHPitch] t
+  float* hmax = tx + kBM * kHPitch;                        // [2 halves][128 rows] max |t|
+  __syncthreads();                                         // every wavefront is done with the stages
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3);
+      tx[row * kHPitch + 32 * wave + c32] = swiglu_one(acc[mt][0][v] * post, acc[mt][1][v] * post, limit, 1.0f);
+    }
+  __syncthreads();
+  const int row = tid & (kBM - 1), half = tid / kBM;
+  f32x4 t[16];
+  float m = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    t[j] = *reinterpret_cast<const f32x4*>(tx + row * kHPitch + 64 * half + 4 * j);
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(t[j][0]), fabsf(t[j][1])), fmaxf(fabsf(t[j][2]), fabsf(t[j][3]))));
+  }
+  hmax[half * kBM + row] = m;
+  __syncthreads();
+  if (row < mrows) {
+    const int prow = m0 + row;
+    const float w = p.swiglu_row_w ? p.swiglu_row_w[prow] : 1.0f;
+    const bool bad = act_row(p, prow) < 0;
+    const float hbad = swiglu_one(__builtin_nanf(""), __builtin_nanf(""), limit, w);
+    const float tmax = fmaxf(hmax[row], hmax[kBM + row]);
+    const float amax = fmaxf(bad ? fabsf(hbad) : tmax * fabsf(w), 1e-4f);
+    const float sc = pow2_ceil_pos(amax * u2f(0x3B124925u));   // 1/448 rounded once to f32
+    const float rcp = pow2_recip(sc);                      // h * rcp == h / sc exactly (sc = 2^e)
+    const size_t at = (size_t)prow * inter + n0 + 64 * half;
+    uint32_t packed[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      f32x4 hv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hv[e] = bad ? hbad : t[j][e] * w;
+      const float a0 = fminf(fmaxf(hv[0] * rcp, -448.f), 448.f);
+      const float a1 = fminf(fmaxf(hv[1] * rcp, -448.f), 448.f);
+      const float a2 = fminf(fmaxf(hv[2] * rcp, -448.f), 448.f);
+      const float a3 = fminf(fmaxf(hv[3] * rcp, -448.f), 448.f);
+      const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+      packed[j] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, pk, true);
+      if (p.h_out) *reinterpret_cast<f32x4*>(p.h_out + at + 4 * j) = hv;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      reinterpret_cast<u32x4*>(p.h_codes + at)[j] =
+          u32x4{packed[4 * j], packed[4 * j + 1], packed[4 * j + 2], packed[4 * j + 3]};
+    if (half == 0) p.h_scales[(size_t)prow * (inter / 128) + n0 / 128] = sc;
+  }
+}
+
+// One 128 x 256 output tile: packed rows [m0, m0 + mrows) of expert `ex`, columns [n0, n0 + 256)
+// (fused with the activation: the gate and up columns of the h columns [n0, n0 + 128)).
 template <int KIND, int NMT>
 __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex, int m0, int mrows, int n0, Stage (&st)[2]) {
   const int tid = threadIdx.x, lane = tid & 63, c32 = lane & 31, h = lane >> 5;
@@ -359,7 +442,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
   uint32_t wo[kNT], so[kNT];
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) {
-    const int col = n0 + wave * kWaveCols + 32 * nt + c32;
+    const int col = tile_col(p, n0, wave, nt) + c32;
     wo[nt] = col < p.n ? (uint32_t)col * (uint32_t)(k / 2) + 32u * h : kOffNone;
     so[nt] = col < p.n ? (uint32_t)col * (uint32_t)(k / GS) + (is_nv(KIND) ? 4u : 2u) * h : kOffNone;
   }
@@ -417,23 +500,27 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
   }
 
   const float post = is_nv(KIND) ? ex.scale2 : 1.0f;
+  if (p.swiglu_inter) {
+    swiglu_epilogue<NMT>(p, m0, mrows, n0, post, acc, st);
+  } else {
 #pragma unroll
-  for (int mt = 0; mt < NMT; ++mt)
+    for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3);
-      if (row < mrows) {
-        const int prow = m0 + row;
-        const int arow = act_row(p, prow);
-        const bool bad = arow < 0;
-        const float rsc = (KIND == kW4 && !bad) ? p.a_row_scale[arow] : 1.0f;
+      for (int v = 0; v < 16; ++v) {
+        const int row = 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (row < mrows) {
+          const int prow = m0 + row;
+          const int arow = act_row(p, prow);
+          const bool bad = arow < 0;
+          const float rsc = (KIND == kW4 && !bad) ? p.a_row_scale[arow] : 1.0f;
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-          const int col = n0 + wave * kWaveCols + 32 * nt + c32;
-          if (col < p.n) p.out[(size_t)prow * p.n + col] = bad ? __builtin_nanf("") : acc[mt][nt][v] * (post * rsc);
+          for (int nt = 0; nt < kNT; ++nt) {
+            const int col = tile_col(p, n0, wave, nt) + c32;
+            if (col < p.n) p.out[(size_t)prow * p.n + col] = bad ? __builtin_nanf("") : acc[mt][nt][v] * (post * rsc);
+          }
         }
       }
-    }
+  }
 }
 
 // f16 holds E4M3 x 2^t exactly for every code when 2^-15 <= 2^t <= 2^7 (the smallest code step
@@ -465,6 +552,26 @@ __device__ __forceinline__ bool f16_operands_exact(const GemmArgs& p, int m0, in
       }
   }
   return __builtin_amdgcn_readfirstlane(__syncthreads_and(ok)) != 0;
+}
+
+// A tile whose weight format the kernel does not take: NaN outputs (fused with the activation: the
+// activation of NaN gate and up values).
+__device__ __forceinline__ void nan_tile(const GemmArgs& p, int m0, int mrows, int n0, Stage (&st)[2]) {
+  if (p.swiglu_inter) {
+    f32x16 nacc[kMT][kNT];
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) nacc[mt][nt][v] = __builtin_nanf("");
+    swiglu_epilogue<kMT>(p, m0, mrows, n0, 1.0f, nacc, st);
+    return;
+  }
+  for (int i = threadIdx.x; i < mrows * kBN; i += kThreads) {
+    const int rr = m0 + i / kBN, col = n0 + i % kBN;
+    if (col < p.n) p.out[(size_t)rr * p.n + col] = __builtin_nanf("");
+  }
 }
 
 __global__ __launch_bounds__(kThreads, 2) void gemm_prefill_kernel(GemmArgs p, int ntn) {
@@ -526,7 +633,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill_kernel(GemmArgs p, i
   } else {
     ex = ExpertView{p.w, p.s, p.scale2, p.kind};
   }
-  const int n0 = nt * kBN;
+  const int n0 = nt * (p.swiglu_inter ? 128 : kBN);
   // The last slice of an expert may hold fewer than 128 rows: only its occupied 32-row MFMA tiles
   // are computed.
   const int nmt = (mrows + 31) >> 5;
@@ -543,10 +650,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill_kernel(GemmArgs p, i
         run_tile<kW4, 4>(p, ex, m0, mrows, n0, st);
       }
     } else {
-      for (int i = threadIdx.x; i < mrows * kBN; i += kThreads) {
-        const int rr = m0 + i / kBN, col = n0 + i % kBN;
-        if (col < p.n) p.out[(size_t)rr * p.n + col] = __builtin_nanf("");
-      }
+      nan_tile(p, m0, mrows, n0, st);
     }
   } else if (ex.kind == kNV) {
     if (f16_operands_exact(p, m0, mrows)) {
@@ -565,17 +669,14 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill_kernel(GemmArgs p, i
   } else if (ex.kind == kMX) {
     run_tile<kMX, 4>(p, ex, m0, mrows, n0, st);
   } else {
-    for (int i = threadIdx.x; i < mrows * kBN; i += kThreads) {
-      const int rr = m0 + i / kBN, col = n0 + i % kBN;
-      if (col < p.n) p.out[(size_t)rr * p.n + col] = __builtin_nanf("");
-    }
+    nan_tile(p, m0, mrows, n0, st);
   }
 }
 
 }  // namespace
 
 hipError_t launch_gemm_prefill(const GemmArgs& a, hipStream_t stream) {
-  const int ntn = (a.n + kBN - 1) / kBN;
+  const int ntn = a.swiglu_inter ? a.swiglu_inter / 128 : (a.n + kBN - 1) / kBN;
   const int E = a.offsets ? a.num_experts : 1;
   const int64_t slices = ((int64_t)a.total_rows + kBM - 1) / kBM + E;
   const int64_t blocks = slices * ntn;

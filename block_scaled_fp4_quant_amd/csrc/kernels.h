@@ -32,6 +32,16 @@ struct GemmArgs {
   // micro-scales a_micro [a_rows, k/16] and row scales a_row_scale [a_rows]; a_scales is unused.
   const uint8_t* a_micro;
   const float* a_row_scale;
+  // Gate/up projection fused with the expert activation and its FP8 quantization (tiled kernel
+  // only; swiglu_inter > 0): columns [0, inter) are the gate, [inter, 2 inter) the up projection,
+  // and instead of `out` the kernel writes h_codes [rows, inter], h_scales [rows, inter/128] and, when
+  // given, h_out [rows, inter] for h = swiglu(gate, up, swiglu_limit) * swiglu_row_w[row].
+  int32_t swiglu_inter;
+  float swiglu_limit;
+  const float* swiglu_row_w;
+  uint8_t* h_codes;
+  float* h_scales;
+  float* h_out;
 };
 
 hipError_t launch_act_quant(const float* x, uint8_t* codes, float* scales, int64_t ngroups,

@@ -25,12 +25,6 @@ constexpr int kSqThreads = 256;
 constexpr int kSqUnroll = 4;                             // groups per half wave per iteration
 constexpr int kSqGroupsPerBlock = (kSqThreads / 32) * kSqUnroll;
 
-__device__ __forceinline__ float swiglu_one(float g, float u, float limit, float w) {
-  g = fminf(g, limit);
-  u = fminf(fmaxf(u, -limit), limit);
-  return g * (1.0f / (1.0f + expf(-g))) * u * w;
-}
-
 __global__ __launch_bounds__(kSqThreads) void swiglu_quant_kernel(const float* __restrict__ gu,
                                                                   const float* __restrict__ weights,
                                                                   float limit, uint8_t* __restrict__ codes,

@@ -135,6 +135,32 @@ FP4MOE_API int swiglu_quant_fp8(const float* gu, const float* row_weights, float
                                 hipStream_t stream);
 
 /*
+ * fp4_grouped_gemm_swiglu_quant -- [CHECK: f16g grouped GEMM; GATE: the swiglu_limit saturation cell,
+ * then quant_rows].  The gate/up projection of the routed rows with the expert activation and its
+ * FP8 quantization applied before anything is written: the result is bit-identical to
+ *   gu = fp4_grouped_gemm(..., n = 2*inter, ...)   (the tiled schedule)
+ *   swiglu_quant_fp8(gu, row_weights, limit, h_codes, h_scales, h_out, total_rows, inter)
+ * without the f32 [total_rows, 2*inter] intermediate.  Expert planes are [2*inter, k/2] (gate columns
+ * first, then up), as for fp4_grouped_gemm with n = 2*inter.  A packed row whose row_ids entry is
+ * out of range, or whose expert has a kind other than 0/1, enters the activation as NaN gate and up
+ * values, exactly as the unfused route's NaN GEMM output would.
+ * Arguments as for fp4_grouped_gemm and swiglu_quant_fp8:
+ * row_weights: f32 [total_rows] or NULL (per packed row);  limit: [host] f32 > 0 (+Inf: no clamp).
+ * h_codes:     u8  [total_rows, inter], 16-byte aligned, written.
+ * h_scales:    f32 [total_rows, inter/128], written.
+ * h_out:       f32 [total_rows, inter], 16-byte aligned, or NULL: receives h when given.
+ * Errors: EINVAL on the conditions of fp4_grouped_gemm (with n = 2*inter), inter not a positive
+ * multiple of 128 up to 2^29, limit not > 0, or a misaligned h_codes/h_out.  total_rows == 0 is a
+ * no-op.
+ */
+FP4MOE_API int fp4_grouped_gemm_swiglu_quant(const uint8_t* a_codes, const float* a_scales, int32_t a_rows,
+                                  const int32_t* row_ids, const int32_t* offsets, int32_t num_experts,
+                                  int32_t total_rows, const uint64_t* w_ptrs, const uint64_t* s_ptrs,
+                                  const int32_t* kinds, const float* scale2, int32_t inter, int32_t k,
+                                  const float* row_weights, float limit, uint8_t* h_codes, float* h_scales,
+                                  float* h_out, hipStream_t stream);
+
+/*
  * route_softmax_topk -- [QWEN: the device-router arm].  For every token t, the top_k experts by
  * router logit, best first, and their softmax weights:
  *   ranking: a larger logit first; equal logits (+0 equal to -0) by the lower expert id; NaN below

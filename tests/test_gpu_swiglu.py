@@ -171,3 +171,88 @@ def test_expert_chain_saturation_cell(orc, kind):
     gate, up = gu[:, :I], gu[:, I:]
     assert np.sum(gate > ch.limit) > 0, "the gate clamp never engaged"
     assert np.sum(np.abs(up) > ch.limit) > 0, "the up clamp never engaged"
+
+
+# --------------------------------------------------------------------------- fused gate/up + activation
+
+def run_fused_vs_unfused(ch, limit=None, row_ids=None, kinds=None, weighted=True, x=None):
+    """fp4_grouped_gemm_swiglu_quant against the unfused route it replaces (the tiled grouped GEMM,
+    then swiglu_quant_fp8) on the same inputs: codes, scales and h must agree bit for bit, and every
+    output element must be written (the outputs start poisoned, with two different poisons)."""
+    d = require_gpu()
+    limit = ch.limit if limit is None else limit
+    xd = dev(ch.x if x is None else x, d)
+    rid = dev(ch.row_ids if row_ids is None else row_ids, d)
+    offsets = dev(ch.offsets, d)
+    kd = dev(ch.kinds if kinds is None else np.asarray(kinds, dtype=np.int32), d)
+    rw = dev(ch.route_w, d) if weighted else None
+    up = _upload_bank(ch.up, d)
+    R, I = ch.R, ch.inter
+    codes_x, scales_x = fp4.act_quant_fp8(xd)
+    fp4.set_gemm_schedule(fp4.SCHEDULE_TILED)
+    try:
+        gu = fp4.fp4_grouped_gemm(codes_x, scales_x, rid, offsets, up[2], up[3], kd, up[4], 2 * I)
+    finally:
+        fp4.set_gemm_schedule(fp4.SCHEDULE_AUTO)
+    h_ref = torch.empty((R, I), dtype=torch.float32, device=d)
+    c_ref, s_ref = fp4.swiglu_quant_fp8(gu, limit, row_weights=rw, h_out=h_ref)
+    outs = []
+    for poison, with_h in ((0xA5, True), (0x5A, False)):
+        hc = torch.full((R, I), poison, dtype=torch.uint8, device=d)
+        hs = torch.full((R, I // 128), float(poison), dtype=torch.float32, device=d)
+        h = torch.full((R, I), float(poison), dtype=torch.float32, device=d) if with_h else None
+        fp4.fp4_grouped_gemm_swiglu_quant(codes_x, scales_x, rid, offsets, up[2], up[3], kd, up[4], I, limit,
+                                          row_weights=rw, h_codes=hc, h_scales=hs, h_out=h)
+        outs.append((hc, hs, h))
+    torch.cuda.synchronize()
+    i32 = torch.int32
+    for hc, hs, h in outs:
+        assert torch.equal(hc, c_ref), first_byte_diff(hc.cpu().numpy(), c_ref.cpu().numpy(), h_ref.cpu().numpy())
+        assert torch.equal(hs.view(i32), s_ref.view(i32)), "scales differ from the unfused route"
+        if h is not None:
+            assert torch.equal(h.view(i32), h_ref.view(i32)), "h differs from the unfused route"
+    return gu.cpu().numpy(), outs[0][2].cpu().numpy(), c_ref.cpu().numpy(), s_ref.cpu().numpy()
+
+
+@pytest.mark.parametrize("seed,T,E,top,hidden,inter,x_scale", [(1, 40, 8, 2, 512, 256, 1.0),
+                                                               (2, 96, 6, 3, 384, 384, 2.0),
+                                                               (3, 600, 4, 2, 256, 128, 1.0),
+                                                               (4, 700, 8, 2, 1024, 512, 1.0),
+                                                               (5, 9, 3, 1, 128, 1024, 0.5)])
+def test_fused_gate_up_matches_the_unfused_route(orc, seed, T, E, top, hidden, inter, x_scale):
+    kinds = [NV if e % 3 else MX for e in range(E)]
+    ch = workloads.expert_chain(seed, T, E, top, hidden, inter, kinds=kinds, x_scale=x_scale)
+    gu, h, codes, scales = run_fused_vs_unfused(ch, weighted=seed % 2 == 1)
+    if seed == 1:
+        # anchored to the oracle as well: h within the f32 bound of the exact activation of the same gate/up
+        # values, and the codes its act-quant
+        check_h(h, orc.swiglu(gu, inter, ch.limit, ch.route_w), "fused h")
+        rc, rs = orc.act_quant(h)
+        assert np.array_equal(codes, rc) and np.array_equal(scales, rs)
+
+
+@pytest.mark.parametrize("limit", [7.0, float("inf")])
+def test_fused_gate_up_saturation(limit):
+    ch = workloads.expert_chain(58, 70, 3, 2, 512, 256, kinds=[NV, MX, NV], x_scale=50.0)
+    gu, _, _, _ = run_fused_vs_unfused(ch, limit=limit)
+    if limit == 7.0:
+        assert np.sum(gu[:, :256] > 7.0) > 0 and np.sum(np.abs(gu[:, 256:]) > 7.0) > 0
+
+
+@pytest.mark.parametrize("factor", [1e-5, 3e5])
+def test_fused_gate_up_outside_the_f16_range(factor):
+    # rows scaled so that some NVFP4 tiles take the bf16 operand route, the others the f16 one
+    ch = workloads.expert_chain(59, 300, 4, 2, 512, 256, kinds=[NV] * 4)
+    x = ch.x.copy()
+    x[::29] *= np.float32(factor)
+    run_fused_vs_unfused(ch, x=x)
+
+
+def test_fused_gate_up_invalid_rows_and_kinds():
+    # packed rows whose activation row is out of range, and an expert of an unknown format, enter the
+    # activation as NaN gate/up values in both routes
+    ch = workloads.expert_chain(60, 120, 5, 2, 256, 256, kinds=[NV, MX, NV, NV, MX])
+    rid = ch.row_ids.copy()
+    rid[::17] = -1
+    rid[5::23] = len(ch.x) + 3
+    run_fused_vs_unfused(ch, row_ids=rid, kinds=[NV, MX, 7, NV, MX])

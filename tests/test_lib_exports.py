@@ -31,7 +31,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for fn in ("act_quant_fp8", "swiglu_quant_fp8", "fp4_expert_gemm", "fp4_grouped_gemm",
-               "fp4moe_last_error", "fp4moe_version"):
+               "fp4_grouped_gemm_swiglu_quant", "fp4moe_last_error", "fp4moe_version"):
         assert fn in names
 
 
@@ -101,6 +101,25 @@ def test_grouped_gemm_null_and_noop(lib):
     assert lib.fp4_grouped_gemm(BAD, BAD, 8, BAD, NULL, 4, 8, BAD, BAD, BAD, BAD, BAD, 16, 128, NULL) == 1
     assert lib.fp4_grouped_gemm(NULL, NULL, 0, NULL, NULL, 4, 0, NULL, NULL, NULL, NULL, NULL,
                                 16, 128, NULL) == 0
+
+
+@pytest.mark.parametrize("a_rows,E,R,inter,k,limit", [
+    (-1, 4, 8, 128, 128, 1.0), (8, 0, 8, 128, 128, 1.0), (8, 4, 8, 0, 128, 1.0), (8, 4, 8, 192, 128, 1.0),
+    (8, 4, 8, 128, 96, 1.0), (8, 4, 8, 128, 128, 0.0), (8, 4, 8, 128, 128, float("nan")),
+    (1 << 20, 4, 8, 128, 4096, 1.0)])
+def test_fused_gate_up_rejects(lib, a_rows, E, R, inter, k, limit):
+    assert lib.fp4_grouped_gemm_swiglu_quant(BAD, BAD, a_rows, BAD, BAD, E, R, BAD, BAD, BAD, BAD, inter, k, NULL,
+                                             limit, BAD, BAD, NULL, NULL) == 1
+    assert "fp4_grouped_gemm_swiglu_quant" in lib.fp4moe_last_error().decode()
+
+
+def test_fused_gate_up_null_alignment_and_noop(lib):
+    f = lib.fp4_grouped_gemm_swiglu_quant
+    assert f(BAD, BAD, 8, BAD, BAD, 4, 8, BAD, BAD, BAD, BAD, 128, 128, NULL, 1.0, NULL, BAD, NULL, NULL) == 1
+    assert f(BAD, BAD, 8, BAD, BAD, 4, 8, BAD, BAD, BAD, BAD, 128, 128, NULL, 1.0, ctypes.c_void_p(0x1008), BAD, NULL, NULL) == 1
+    assert "aligned" in lib.fp4moe_last_error().decode()
+    assert f(NULL, NULL, 0, NULL, NULL, 4, 0, NULL, NULL, NULL, NULL, 128, 128, NULL, 1.0, NULL, NULL, NULL,
+             NULL) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
