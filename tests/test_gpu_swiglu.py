@@ -211,7 +211,7 @@ def run_fused_vs_unfused(ch, limit=None, row_ids=None, kinds=None, weighted=True
         assert torch.equal(hs.view(i32), s_ref.view(i32)), "scales differ from the unfused route"
         if h is not None:
             assert torch.equal(h.view(i32), h_ref.view(i32)), "h differs from the unfused route"
-    return gu.cpu().numpy(), outs[0][2].cpu().numpy(), c_ref.cpu().numpy(), s_ref.cpu().numpy()
+    return gu, outs[0][2], c_ref, s_ref
 
 
 @pytest.mark.parametrize("seed,T,E,top,hidden,inter,x_scale", [(1, 40, 8, 2, 512, 256, 1.0),
@@ -222,7 +222,7 @@ def run_fused_vs_unfused(ch, limit=None, row_ids=None, kinds=None, weighted=True
 def test_fused_gate_up_matches_the_unfused_route(orc, seed, T, E, top, hidden, inter, x_scale):
     kinds = [NV if e % 3 else MX for e in range(E)]
     ch = workloads.expert_chain(seed, T, E, top, hidden, inter, kinds=kinds, x_scale=x_scale)
-    gu, h, codes, scales = run_fused_vs_unfused(ch, weighted=seed % 2 == 1)
+    gu, h, codes, scales = (t.cpu().numpy() for t in run_fused_vs_unfused(ch, weighted=seed % 2 == 1))
     if seed == 1:
         # anchored to the oracle as well: h within the f32 bound of the exact activation of the same gate/up
         # values, and the codes its act-quant
@@ -234,7 +234,7 @@ def test_fused_gate_up_matches_the_unfused_route(orc, seed, T, E, top, hidden, i
 @pytest.mark.parametrize("limit", [7.0, float("inf")])
 def test_fused_gate_up_saturation(limit):
     ch = workloads.expert_chain(58, 70, 3, 2, 512, 256, kinds=[NV, MX, NV], x_scale=50.0)
-    gu, _, _, _ = run_fused_vs_unfused(ch, limit=limit)
+    gu = run_fused_vs_unfused(ch, limit=limit)[0].cpu().numpy()
     if limit == 7.0:
         assert np.sum(gu[:, :256] > 7.0) > 0 and np.sum(np.abs(gu[:, 256:]) > 7.0) > 0
 
@@ -256,3 +256,13 @@ def test_fused_gate_up_invalid_rows_and_kinds():
     rid[::17] = -1
     rid[5::23] = len(ch.x) + 3
     run_fused_vs_unfused(ch, row_ids=rid, kinds=[NV, MX, 7, NV, MX])
+
+
+def test_config4_fused_gate_up_full_size():
+    # the prefill layer's gate/up projection at full size (8192 tokens, top-8, 256 experts, n = 4096,
+    # k = 7168, limit 7, routing-weighted rows), in the launch the chain benchmark times: bit-identical
+    # to the unfused route over all 65536 x 2048 outputs
+    ch = workloads.config4_chain()
+    gu, h, codes, _ = run_fused_vs_unfused(ch)
+    assert gu.shape == (ch.R, 2 * ch.inter) and codes.shape == (ch.R, ch.inter)
+    assert torch.isfinite(h).all()
