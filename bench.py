@@ -51,16 +51,16 @@ def sources_sha(workload: str) -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str):
-    """HBM bytes per GEMM launch measured with rocprofv3 counters for this exact kernel source, or
-    None when no measurement matches the current source."""
+def recorded_traffic(workload: str, layout: str):
+    """HBM bytes per GEMM launch measured with rocprofv3 counters for this exact kernel source and
+    weight layout, or None when no measurement matches."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
     ent = rec.get(workload)
-    if not ent or ent.get("gemm_sources_sha") != sources_sha(workload):
+    if not ent or ent.get("gemm_sources_sha") != sources_sha(workload) or ent.get("layout", "plain") != layout:
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -137,6 +137,10 @@ def main():
                     help="chain4 only: the gate/up GEMM with the activation and its quantization in "
                          "its epilogue (fused), or the GEMM writing f32 gate/up values followed by "
                          "swiglu_quant_fp8 (unfused)")
+    ap.add_argument("--layout", default="swizzled", choices=["swizzled", "plain"],
+                    help="config3/config4: expert planes in the swizzled layout (fp4_weight_swizzle, "
+                         "run once at load time before the timed region) or as the plain [n, k/2] and "
+                         "[n, k/gs] planes")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 disables it)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -176,6 +180,8 @@ def main():
     s_bank = torch.from_numpy(wl.s_bank).to(dev)
     w_ptrs = torch.from_numpy((w_bank.data_ptr() + wl.w_off).astype(np.int64)).to(dev)
     s_ptrs = torch.from_numpy((s_bank.data_ptr() + wl.s_off).astype(np.int64)).to(dev)
+    if args.layout == "swizzled":
+        w_bank, s_bank, w_ptrs, s_ptrs, kinds = swizzle_bank(wl, torch, fp4, dev, w_bank, s_bank)
     T, k = wl.x.shape
     codes = torch.empty((T, k), dtype=torch.uint8, device=dev)
     scales = torch.empty((T, k // 128), dtype=torch.float32, device=dev)
@@ -217,7 +223,7 @@ def main():
     ws_bytes = alg["weights"]
     gemm_s = gemm_ms * 1e-3
     achieved_gbs = alg["total"] / gemm_s / 1e9
-    traffic = recorded_traffic(args.workload)
+    traffic = recorded_traffic(args.workload, args.layout)
     if args.workload == "config3":
         value = ws_bytes / (step_ms * 1e-3) / 1e12
         unit = "TB/s"
@@ -241,6 +247,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8xfp4->f32", "data": "synthetic",
         "config": {"workload": wl.name, "tokens": int(T), "experts": int(wl.E), "top_k": 8,
                    "routed_rows": int(wl.R), "k": int(wl.k), "n": int(wl.n),
+                   "weight_layout": args.layout,
                    "weight_stream_bytes": int(ws_bytes), "gemm_us": round(gemm_ms * 1e3, 2),
                    "act_quant_us": round(aq_ms * 1e3, 2)},
         "roofline": roofline,
@@ -260,6 +267,28 @@ def main():
             result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
             log(f"cpu_baseline: {result['cpu_baseline']}")
     print(json.dumps(result), flush=True)
+
+
+def swizzle_bank(wl, torch, fp4, dev, w_bank, s_bank):
+    """Every expert's planes rewritten by fp4_weight_swizzle into new banks (load-time work, before
+    any timing); returns the banks, their address tables and the kinds with the layout flag."""
+    sizes = [fp4.swizzled_plane_bytes(int(kd), wl.n, wl.k) for kd in wl.kinds]
+    w_off = np.concatenate([[0], np.cumsum([a for a, _ in sizes])]).astype(np.int64)
+    s_off = np.concatenate([[0], np.cumsum([(b + 255) // 256 * 256 for _, b in sizes])]).astype(np.int64)
+    w_swz = torch.empty(int(w_off[-1]), dtype=torch.uint8, device=dev)
+    s_swz = torch.empty(int(s_off[-1]), dtype=torch.uint8, device=dev)
+    gs = {workloads.NVFP4: 16, workloads.MXFP4: 32}
+    for e, kd in enumerate(wl.kinds):
+        kd = int(kd)
+        wp = w_bank[int(wl.w_off[e]):int(wl.w_off[e]) + wl.n * wl.k // 2].view(wl.n, wl.k // 2)
+        sp = s_bank[int(wl.s_off[e]):int(wl.s_off[e]) + wl.n * wl.k // gs[kd]].view(wl.n, wl.k // gs[kd])
+        fp4.fp4_weight_swizzle(wp, sp, kd, w_out=w_swz[int(w_off[e]):int(w_off[e + 1])],
+                               s_out=s_swz[int(s_off[e]):int(s_off[e]) + sizes[e][1]])
+    torch.cuda.synchronize()
+    w_ptrs = torch.from_numpy((w_swz.data_ptr() + w_off[:-1]).astype(np.int64)).to(dev)
+    s_ptrs = torch.from_numpy((s_swz.data_ptr() + s_off[:-1]).astype(np.int64)).to(dev)
+    kinds = torch.from_numpy((wl.kinds | fp4.SWIZZLED).astype(np.int32)).to(dev)
+    return w_swz, s_swz, w_ptrs, s_ptrs, kinds
 
 
 def upload_bank(gw, torch, dev):

@@ -15,6 +15,7 @@ import torch
 
 NVFP4 = 0
 MXFP4 = 1
+SWIZZLED = 2          # layout flag OR'ed into a kind: planes written by fp4_weight_swizzle
 GROUP_SIZE = {NVFP4: 16, MXFP4: 32}
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -74,6 +75,13 @@ def lib() -> ctypes.CDLL:
         L.fp4moe_version.restype = ctypes.c_char_p
         L.fp4moe_set_gemm_schedule.argtypes = [I32]
         L.fp4moe_set_gemm_schedule.restype = ctypes.c_int
+        L.fp4_swizzled_weight_bytes.restype = ctypes.c_size_t
+        L.fp4_swizzled_weight_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
+        L.fp4_swizzled_scale_bytes.restype = ctypes.c_size_t
+        L.fp4_swizzled_scale_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+        L.fp4_weight_swizzle.restype = ctypes.c_int
+        L.fp4_weight_swizzle.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -164,21 +172,67 @@ def swiglu_quant_fp8(gu: torch.Tensor, limit: float, row_weights=None, codes=Non
     return codes, scales
 
 
-def fp4_expert_gemm(a_codes, a_scales, w_packed, w_scales, scale2: float, kind: int, out=None,
-                    stream=None):
-    """One expert: a_codes u8 [g, k], a_scales f32 [g, k/128], w_packed u8 [n, k/2],
-    w_scales u8 [n, k/gs] -> out f32 [g, n]."""
-    _dev(a_codes, torch.uint8, "a_codes", 2)
-    _dev(a_scales, torch.float32, "a_scales", 2)
+def swizzled_plane_bytes(kind: int, n: int, k: int):
+    """(nibble bytes, scale bytes) of one expert's swizzled planes."""
+    L = lib()
+    wb, sb = L.fp4_swizzled_weight_bytes(int(n), int(k)), L.fp4_swizzled_scale_bytes(int(kind), int(n), int(k))
+    if wb == 0 or sb == 0:
+        raise ValueError(f"no swizzled layout for kind={kind} n={n} k={k}")
+    return int(wb), int(sb)
+
+
+def fp4_weight_swizzle(w_packed, w_scales, kind: int, w_out=None, s_out=None, stream=None):
+    """One expert's plain planes (w_packed u8 [n, k/2], w_scales u8 [n, k/gs]) -> the swizzled
+    planes (u8 1-D tensors) that the GEMMs read with kind | SWIZZLED."""
     _dev(w_packed, torch.uint8, "w_packed", 2)
     _dev(w_scales, torch.uint8, "w_scales", 2)
-    g, k = a_codes.shape
-    n = w_packed.shape[0]
     if kind not in GROUP_SIZE:
         raise ValueError(f"kind must be 0 (NVFP4) or 1 (MXFP4), got {kind}")
-    if a_scales.shape != (g, k // 128) or w_packed.shape != (n, k // 2) \
-            or w_scales.shape != (n, k // GROUP_SIZE[kind]):
-        raise ValueError("operand shapes do not match")
+    n, k = w_packed.shape[0], 2 * w_packed.shape[1]
+    if w_scales.shape != (n, k // GROUP_SIZE[kind]):
+        raise ValueError("w_scales shape does not match w_packed")
+    wb, sb = swizzled_plane_bytes(kind, n, k)
+    if w_out is None:
+        w_out = torch.empty(wb, dtype=torch.uint8, device=w_packed.device)
+    if s_out is None:
+        s_out = torch.empty(sb, dtype=torch.uint8, device=w_packed.device)
+    _dev(w_out, torch.uint8, "w_out")
+    _dev(s_out, torch.uint8, "s_out")
+    if w_out.numel() != wb or s_out.numel() != sb:
+        raise ValueError(f"swizzled planes must hold {wb} and {sb} bytes")
+    _check(lib().fp4_weight_swizzle(_ptr(w_packed), _ptr(w_scales), int(kind), n, k, _ptr(w_out), _ptr(s_out),
+                                    _stream(stream)), "fp4_weight_swizzle")
+    return w_out, s_out
+
+
+def fp4_expert_gemm(a_codes, a_scales, w_packed, w_scales, scale2: float, kind: int, out=None,
+                    stream=None, n=None):
+    """One expert: a_codes u8 [g, k], a_scales f32 [g, k/128], w_packed u8 [n, k/2],
+    w_scales u8 [n, k/gs] -> out f32 [g, n].  With kind | SWIZZLED the planes are the 1-D
+    tensors of fp4_weight_swizzle and n must be given."""
+    _dev(a_codes, torch.uint8, "a_codes", 2)
+    _dev(a_scales, torch.float32, "a_scales", 2)
+    g, k = a_codes.shape
+    base = kind & ~SWIZZLED if isinstance(kind, int) and kind >= 0 else kind
+    if base not in GROUP_SIZE or kind > (MXFP4 | SWIZZLED):
+        raise ValueError(f"kind must be 0/1 (NVFP4/MXFP4), or 2/3 for swizzled planes, got {kind}")
+    if kind & SWIZZLED:
+        _dev(w_packed, torch.uint8, "w_packed", 1)
+        _dev(w_scales, torch.uint8, "w_scales", 1)
+        if n is None:
+            raise ValueError("n must be given with swizzled planes")
+        n = int(n)
+        if (w_packed.numel(), w_scales.numel()) != swizzled_plane_bytes(base, n, k):
+            raise ValueError("swizzled plane sizes do not match n and k")
+        if a_scales.shape != (g, k // 128):
+            raise ValueError("operand shapes do not match")
+    else:
+        _dev(w_packed, torch.uint8, "w_packed", 2)
+        _dev(w_scales, torch.uint8, "w_scales", 2)
+        n = w_packed.shape[0]
+        if a_scales.shape != (g, k // 128) or w_packed.shape != (n, k // 2) \
+                or w_scales.shape != (n, k // GROUP_SIZE[kind]):
+            raise ValueError("operand shapes do not match")
     if out is None:
         out = torch.empty((g, n), dtype=torch.float32, device=a_codes.device)
     _dev(out, torch.float32, "out", 2)

@@ -43,10 +43,13 @@ int check_planes(int64_t a_rows, int32_t n, int32_t k, const char* what) {
   if (a_rows * (int64_t)k >= kMaxPlaneBytes)
     return fail(FP4MOE_EINVAL, "%s: activation plane of %lld x %d bytes exceeds 2^31", what,
                 (long long)a_rows, (int)k);
-  if ((int64_t)n * (k / 2) >= kMaxPlaneBytes)
+  // the swizzled planes round n up to a multiple of 16 columns
+  if ((int64_t)(n + 15) / 16 * 16 * (k / 2) >= kMaxPlaneBytes)
     return fail(FP4MOE_EINVAL, "%s: weight plane of %d x %d bytes exceeds 2^31", what, (int)n, (int)(k / 2));
   return FP4MOE_OK;
 }
+
+bool is_gemm_kind(int32_t kind) { return kind >= 0 && kind <= (FP4MOE_MXFP4 | FP4MOE_SWIZZLED); }
 
 // GEMM schedule: row-streaming (decode) kernel for at most 32 rows per expert on average, tiled
 // (prefill) kernel otherwise.  Both compute the same definition; the choice only changes the
@@ -262,8 +265,8 @@ int fp4_expert_gemm(const uint8_t* a_codes, const float* a_scales, const uint8_t
   if (g < 0) return fail(FP4MOE_EINVAL, "fp4_expert_gemm: g = %d < 0", (int)g);
   if (n <= 0) return fail(FP4MOE_EINVAL, "fp4_expert_gemm: n = %d must be positive", (int)n);
   if (int rc = check_k(k, "fp4_expert_gemm")) return rc;
-  if (kind != FP4MOE_NVFP4 && kind != FP4MOE_MXFP4)
-    return fail(FP4MOE_EINVAL, "fp4_expert_gemm: kind = %d is neither 0 (NVFP4) nor 1 (MXFP4)", (int)kind);
+  if (!is_gemm_kind(kind))
+    return fail(FP4MOE_EINVAL, "fp4_expert_gemm: kind = %d is not 0/1 (NVFP4/MXFP4) or 2/3 (swizzled)", (int)kind);
   if (g == 0) return ok();
   if (!a_codes || !a_scales || !w_packed || !w_scales || !out)
     return fail(FP4MOE_EINVAL, "fp4_expert_gemm: NULL buffer with g > 0");
@@ -365,6 +368,31 @@ int fp4_grouped_gemm_swiglu_quant(const uint8_t* a_codes, const float* a_scales,
   a.h_scales = h_scales;
   a.h_out = h_out;
   return launched(fp4moe::launch_gemm_prefill(a, stream), what);
+}
+
+size_t fp4_swizzled_weight_bytes(int32_t n, int32_t k) {
+  if (n <= 0 || k <= 0 || k % 128 != 0) return 0;
+  return (size_t)fp4moe::swizzled_weight_bytes(n, k);
+}
+
+size_t fp4_swizzled_scale_bytes(int32_t kind, int32_t n, int32_t k) {
+  if (n <= 0 || k <= 0 || k % 128 != 0 || (kind != FP4MOE_NVFP4 && kind != FP4MOE_MXFP4)) return 0;
+  return (size_t)fp4moe::swizzled_scale_bytes(kind, n, k);
+}
+
+int fp4_weight_swizzle(const uint8_t* w_packed, const uint8_t* w_scales, int32_t kind, int32_t n, int32_t k,
+                       uint8_t* w_swz, uint8_t* s_swz, hipStream_t stream) {
+  const char* what = "fp4_weight_swizzle";
+  if (n <= 0) return fail(FP4MOE_EINVAL, "%s: n = %d must be positive", what, (int)n);
+  if (int rc = check_k(k, what)) return rc;
+  if (kind != FP4MOE_NVFP4 && kind != FP4MOE_MXFP4)
+    return fail(FP4MOE_EINVAL, "%s: kind = %d is neither 0 (NVFP4) nor 1 (MXFP4)", what, (int)kind);
+  if (int rc = check_planes(0, n, k, what)) return rc;
+  if (!w_packed || !w_scales || !w_swz || !s_swz) return fail(FP4MOE_EINVAL, "%s: NULL buffer", what);
+  if ((reinterpret_cast<uintptr_t>(w_packed) | reinterpret_cast<uintptr_t>(w_swz) |
+       reinterpret_cast<uintptr_t>(s_swz)) & 15)
+    return fail(FP4MOE_EINVAL, "%s: w_packed, w_swz and s_swz must be 16-byte aligned", what);
+  return launched(fp4moe::launch_weight_swizzle(w_packed, w_scales, kind, n, k, w_swz, s_swz, stream), what);
 }
 
 int fp4moe_set_gemm_schedule(int32_t schedule) {

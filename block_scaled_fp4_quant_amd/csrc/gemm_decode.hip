@@ -56,6 +56,7 @@ constexpr int kARow = kChunkK + 16;          // padded LDS row of activation cod
 constexpr int kSCol = 40;                    // padded LDS column of one chunk's weight scales
 constexpr int kNV = 0;
 constexpr int kMX = 1;
+constexpr int kSwizzled = 2;                 // kind flag: planes in the swizzled layout
 
 struct Stage {
   uint8_t a[kRows * kARow];                  // activation codes, [row][512 (+16 pad)]
@@ -85,18 +86,22 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Per-thread staging registers of one chunk, and their global byte offsets for chunk 0.
+// Per-thread staging registers of one chunk, and their global byte offsets for chunk 0.  With
+// swizzled weight planes (SWZ) the weight scales are not staged: each lane loads its own.
+template <int KIND>
+constexpr int kStagedScales = KIND == kNV ? 2 : 1;
+
 template <int KIND>
 struct StageRegs {
   u32x4 a[4];                                 // activation codes: 4 x 16 bytes
-  u32x4 s[KIND == kNV ? 2 : 1];               // weight scales: 16 bytes per column half (NV) / column (MX)
+  u32x4 s[kStagedScales<KIND>];               // weight scales: 16 bytes per column half (NV) / column (MX)
   float as;                                   // one activation scale (threads < 128)
 };
 
 template <int KIND>
 struct StageOffsets {
   uint32_t a[4];                              // row * k + 16 * part, or kOffNone
-  uint32_t s[KIND == kNV ? 2 : 1];            // column * k/gs + 16 * half, or kOffNone
+  uint32_t s[kStagedScales<KIND>];            // column * k/gs + 16 * half, or kOffNone
   uint32_t as;                                // (row * nblk + blk) * 4, or kOffNone
 };
 
@@ -104,20 +109,22 @@ struct Rsrc {
   rsrc_t w, s, a, as;
 };
 
-template <int KIND>
+template <int KIND, bool SWZ>
 __device__ __forceinline__ void stage_load(const Rsrc& r, const StageOffsets<KIND>& o, int c, bool valid,
                                            StageRegs<KIND>& d) {
   const uint32_t uc = (uint32_t)c;
 #pragma unroll
   for (int j = 0; j < 4; ++j) d.a[j] = buf_load_x4(r.a, valid ? o.a[j] + uc * kChunkK : kOffNone);
+  if constexpr (!SWZ) {
 #pragma unroll
-  for (int h = 0; h < (KIND == kNV ? 2 : 1); ++h)
-    d.s[h] = buf_load_x4(r.s, valid ? o.s[h] + uc * (KIND == kNV ? 32u : 16u) : kOffNone);
+    for (int h = 0; h < kStagedScales<KIND>; ++h)
+      d.s[h] = buf_load_x4(r.s, valid ? o.s[h] + uc * (KIND == kNV ? 32u : 16u) : kOffNone);
+  }
   d.as = u2f(buf_load_u32(r.as, valid ? o.as + uc * (uint32_t)(kBlk * 4) : kOffNone));
 }
 
 // Store one chunk's staged data into an LDS stage.
-template <int KIND>
+template <int KIND, bool SWZ>
 __device__ __forceinline__ void stage_store(Stage& st, const StageRegs<KIND>& d) {
   const int tid = threadIdx.x;
 #pragma unroll
@@ -126,7 +133,9 @@ __device__ __forceinline__ void stage_store(Stage& st, const StageRegs<KIND>& d)
     *reinterpret_cast<u32x4*>(st.a + row * kARow + part * 16) = d.a[j];
   }
   if (tid < kRows * kBlk) st.as[(tid & 3) * kRows + (tid >> 2)] = d.as;
-  if constexpr (KIND == kNV) {
+  if constexpr (SWZ) {
+    return;
+  } else if constexpr (KIND == kNV) {
     // The thread holds 16 bytes of one column = blocks {2h, 2h+1} x 4 ushort scale pairs (lane
     // groups g = 0..3).  For each g, the two pairs become one dword at [col][8g + 4h], so the
     // reader lane (column, g) finds the pairs of blocks 0..3 in 8 contiguous bytes.
@@ -196,8 +205,8 @@ __device__ __forceinline__ void compute_block_nv(const Stage& st, int bq, const 
 // scale applied by the conversion, a pure exponent) and the same per-block partial tile as NVFP4.
 // bf16 rather than f16 because an E8M0 scale can lie outside the f16 range.
 template <int MT>
-__device__ __forceinline__ void compute_block_mx(const Stage& st, int bq, int wave, const u32x4 (&wq)[kCT],
-                                                 f32x4 (&acc)[MT][kCT]) {
+__device__ __forceinline__ void compute_block_mx(const Stage& st, int bq, const uint32_t (&sb)[kCT],
+                                                 const u32x4 (&wq)[kCT], f32x4 (&acc)[MT][kCT]) {
   const int lane = threadIdx.x & 63, c16 = lane & 15, g = lane >> 4;
   f32x4 part[MT][kCT];
 #pragma unroll
@@ -211,12 +220,11 @@ __device__ __forceinline__ void compute_block_mx(const Stage& st, int bq, int wa
     aq[mt][0] = *reinterpret_cast<const u32x4*>(ap);
     aq[mt][1] = *reinterpret_cast<const u32x4*>(ap + 16);
   }
-  // The lane's k = 32g .. +32 of the block is one MXFP4 group: E8M0 byte 4*bq + g of the column's
-  // chunk scales, used as the exponent field of the conversion's scale operand.
+  // The lane's k = 32g .. +32 of the block is one MXFP4 group: its E8M0 byte sb[ct], used as the
+  // exponent field of the conversion's scale operand.
   float sv[kCT];
 #pragma unroll
-  for (int ct = 0; ct < kCT; ++ct)
-    sv[ct] = u2f((uint32_t)st.s[(wave * kWaveCols + 16 * ct + c16) * kSCol + 4 * bq + g] << 23);
+  for (int ct = 0; ct < kCT; ++ct) sv[ct] = u2f((sb[ct] & 0xFFu) << 23);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     bf16x8 af[MT];
@@ -239,18 +247,41 @@ __device__ __forceinline__ void compute_block_mx(const Stage& st, int bq, int wa
   }
 }
 
+// Scale registers of one 4-block chunk for one lane and column tile, with swizzled planes: the
+// NVFP4 scale pairs of blocks 0..3 (8 bytes) or the MXFP4 bytes of blocks 0..3 (4 bytes).
+template <int KIND> struct ChunkScale { typedef uint2 T; };
+template <> struct ChunkScale<kMX> { typedef uint32_t T; };
+
+template <int KIND>
+__device__ __forceinline__ typename ChunkScale<KIND>::T scale_load(rsrc_t r, uint32_t off) {
+  if constexpr (KIND == kNV) return buf_load_x2(r, off);
+  else return buf_load_u32(r, off);
+}
+
 // One pass over the packed rows [m0, mend) (at most 32) for the 256 columns starting at n0.
-template <int MT, int KIND>
+// SWZ: the expert's planes are in the swizzled layout (fp4_weight_swizzle): a weight load of the
+// wavefront reads 1 KB of consecutive bytes, and each lane loads the weight scales of its pieces
+// for a whole chunk directly into registers, one chunk ahead, instead of staging them in LDS.
+template <int MT, int KIND, bool SWZ>
 __device__ void run_pass(const GemmArgs& p, const ExpertView& ex, int n0, int m0, int mend, Stage (&st)[2]) {
   const int tid = threadIdx.x, lane = tid & 63, c16 = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int k = p.k, nblk = k >> 7;
   const int nch = (nblk + kBlk - 1) / kBlk;
   constexpr int GS = (KIND == kNV) ? 16 : 32;
+  // Bytes of one block of one lane piece row in the weight plane, of one chunk in the scale plane.
+  constexpr uint32_t kWB = SWZ ? 1024u : 64u;
+  constexpr uint32_t kSQ = KIND == kNV ? 512u : 256u;
 
   Rsrc r;
-  r.w = make_rsrc(ex.w, (uint32_t)p.n * (uint32_t)(k / 2));
-  r.s = make_rsrc(ex.s, (uint32_t)p.n * (uint32_t)(k / GS));
+  if constexpr (SWZ) {
+    const uint32_t n16 = (uint32_t)(p.n + 15) >> 4;
+    r.w = make_rsrc(ex.w, n16 * 16u * (uint32_t)(k / 2));
+    r.s = make_rsrc(ex.s, n16 * (uint32_t)nch * kSQ);
+  } else {
+    r.w = make_rsrc(ex.w, (uint32_t)p.n * (uint32_t)(k / 2));
+    r.s = make_rsrc(ex.s, (uint32_t)p.n * (uint32_t)(k / GS));
+  }
   r.a = make_rsrc(p.a_codes, (uint32_t)p.a_rows * (uint32_t)k);
   r.as = make_rsrc(p.a_scales, (uint32_t)p.a_rows * (uint32_t)nblk * 4u);
 
@@ -271,18 +302,27 @@ __device__ void run_pass(const GemmArgs& p, const ExpertView& ex, int n0, int m0
     const int ar = (tid < kRows * kBlk && row < MT * 16 && prow < mend) ? act_row(p, prow) : -1;
     so.as = ar >= 0 ? ((uint32_t)ar * (uint32_t)nblk + blk) * 4u : kOffNone;
   }
+  if constexpr (!SWZ) {
 #pragma unroll
-  for (int h = 0; h < (KIND == kNV ? 2 : 1); ++h) {
-    const int q = tid + kThreads * h;
-    const int col = KIND == kNV ? (q >> 1) : q, half = KIND == kNV ? (q & 1) : 0;
-    so.s[h] = (n0 + col < p.n) ? (uint32_t)(n0 + col) * (uint32_t)(k / GS) + 16u * half : kOffNone;
+    for (int h = 0; h < kStagedScales<KIND>; ++h) {
+      const int q = tid + kThreads * h;
+      const int col = KIND == kNV ? (q >> 1) : q, half = KIND == kNV ? (q & 1) : 0;
+      so.s[h] = (n0 + col < p.n) ? (uint32_t)(n0 + col) * (uint32_t)(k / GS) + 16u * half : kOffNone;
+    }
   }
-  // Weight stream offsets of this wavefront's 4 column tiles.
-  uint32_t wo[kCT];
+  // Weight stream offsets of this wavefront's 4 column tiles (and, swizzled, of their scales).
+  uint32_t wo[kCT], sco[kCT];
 #pragma unroll
   for (int ct = 0; ct < kCT; ++ct) {
     const int col = n0 + wave * kWaveCols + 16 * ct + c16;
-    wo[ct] = col < p.n ? (uint32_t)col * (uint32_t)(k / 2) + 16u * g : kOffNone;
+    if constexpr (SWZ) {
+      const uint32_t t = (uint32_t)col >> 4, piece = (uint32_t)(16 * g + c16);
+      wo[ct] = col < p.n ? t * (uint32_t)nblk * 1024u + 16u * piece : kOffNone;
+      sco[ct] = col < p.n ? t * (uint32_t)nch * kSQ + piece * (kSQ / 64u) : kOffNone;
+    } else {
+      wo[ct] = col < p.n ? (uint32_t)col * (uint32_t)(k / 2) + 16u * g : kOffNone;
+      sco[ct] = kOffNone;
+    }
   }
 
   f32x4 acc[MT][kCT];
@@ -291,38 +331,51 @@ __device__ void run_pass(const GemmArgs& p, const ExpertView& ex, int n0, int m0
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct) acc[mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Prologue: chunk 0 staged into LDS stage 0, chunk 1 loaded into the staging registers, then the
-  // weight ring for the blocks of chunk 0 -- the same order of outstanding loads as at the top of
-  // every loop iteration (staged chunk first, then 4 blocks of weights), so that the compiler's
-  // wait counts, merged over the loop entry and the back edge, stay exact.  Every group of loads is
-  // pinned where it is written (sched_barrier): the machine scheduler would otherwise sink loads
-  // toward their first use.  All loads are issued on every path (out-of-range ones return zero
-  // without touching memory).
+  // Prologue: chunk 0 staged into LDS stage 0, chunk 1 loaded into the staging registers, then
+  // (swizzled) the weight scales of chunk 0 and the weight ring for the blocks of chunk 0 -- the
+  // same order of outstanding loads as at the top of every loop iteration (staged chunk first, then
+  // scales, then 4 blocks of weights), so that the compiler's wait counts, merged over the loop
+  // entry and the back edge, stay exact.  Every group of loads is pinned where it is written
+  // (sched_barrier): the machine scheduler would otherwise sink loads toward their first use.  All
+  // loads are issued on every path (out-of-range ones return zero without touching memory).
   StageRegs<KIND> sr;
-  stage_load<KIND>(r, so, 0, true, sr);
+  stage_load<KIND, SWZ>(r, so, 0, true, sr);
   __builtin_amdgcn_sched_barrier(0);
-  stage_store<KIND>(st[0], sr);
-  stage_load<KIND>(r, so, 1, 1 < nch, sr);
+  stage_store<KIND, SWZ>(st[0], sr);
+  stage_load<KIND, SWZ>(r, so, 1, 1 < nch, sr);
   __builtin_amdgcn_sched_barrier(0);
+  typename ChunkScale<KIND>::T scn[kCT], scc[kCT];   // next chunk's / this chunk's scales (SWZ)
+  if constexpr (SWZ) {
+#pragma unroll
+    for (int ct = 0; ct < kCT; ++ct) scn[ct] = scale_load<KIND>(r.s, sco[ct]);
+  }
   u32x4 wq[kBlk][kCT];
 #pragma unroll
   for (int j = 0; j < kBlk; j += 2) {
 #pragma unroll
     for (int ct = 0; ct < kCT; ++ct) {
-      wq[j][ct] = buf_load_x4(r.w, j < nblk ? wo[ct] + (uint32_t)j * 64u : kOffNone);
-      wq[j + 1][ct] = buf_load_x4(r.w, j + 1 < nblk ? wo[ct] + (uint32_t)(j + 1) * 64u : kOffNone);
+      wq[j][ct] = buf_load_x4(r.w, j < nblk ? wo[ct] + (uint32_t)j * kWB : kOffNone);
+      wq[j + 1][ct] = buf_load_x4(r.w, j + 1 < nblk ? wo[ct] + (uint32_t)(j + 1) * kWB : kOffNone);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 
   for (int c = 0; c < nch; ++c) {
     lds_barrier();                           // stage c&1 complete; stage (c+1)&1 no longer read
-    stage_store<KIND>(st[(c + 1) & 1], sr);  // chunk c+1 (zeros past the end)
-    stage_load<KIND>(r, so, c + 2, c + 2 < nch, sr);
+    stage_store<KIND, SWZ>(st[(c + 1) & 1], sr);  // chunk c+1 (zeros past the end)
+    stage_load<KIND, SWZ>(r, so, c + 2, c + 2 < nch, sr);
     __builtin_amdgcn_sched_barrier(0);
     const Stage& cur = st[c & 1];
     uint2 scp[kCT];                          // NVFP4 scale pairs of blocks 0..3 of this chunk
-    if constexpr (KIND == kNV) {
+    uint32_t mxs[kCT];                       // MXFP4 scale bytes of blocks 0..3 of this chunk
+    if constexpr (SWZ) {
+#pragma unroll
+      for (int ct = 0; ct < kCT; ++ct) {
+        scc[ct] = scn[ct];
+        if constexpr (KIND == kNV) scp[ct] = scc[ct];
+        else mxs[ct] = scc[ct];
+      }
+    } else if constexpr (KIND == kNV) {
 #pragma unroll
       for (int ct = 0; ct < kCT; ++ct)
         scp[ct] = *reinterpret_cast<const uint2*>(cur.s + (wave * kWaveCols + 16 * ct + c16) * kSCol + 8 * g);
@@ -337,17 +390,30 @@ __device__ void run_pass(const GemmArgs& p, const ExpertView& ex, int n0, int m0
           for (int ct = 0; ct < kCT; ++ct) sc[ct] = (bq < 2 ? scp[ct].x : scp[ct].y) >> (16 * (bq & 1));
           compute_block_nv<MT>(cur, bq, wq[bq], sc, acc);
         } else {
-          compute_block_mx<MT>(cur, bq, wave, wq[bq], acc);
+          uint32_t sb[kCT];
+#pragma unroll
+          for (int ct = 0; ct < kCT; ++ct)
+            sb[ct] = SWZ ? mxs[ct] >> (8 * bq)
+                         : (uint32_t)cur.s[(wave * kWaveCols + 16 * ct + c16) * kSCol + 4 * bq + g];
+          compute_block_mx<MT>(cur, bq, sb, wq[bq], acc);
         }
       }
       // Refill the ring two blocks at a time: the two 64-byte halves of each column's 128-byte
-      // line are requested back to back, so the line is fetched from HBM once.
+      // line are requested back to back, so the line is fetched from HBM once.  Swizzled: the
+      // next chunk's scales go first.
       if (bq & 1) {
         const int bn = b + kBlk;
+        if constexpr (SWZ) {
+          if (bq == 1) {
+#pragma unroll
+            for (int ct = 0; ct < kCT; ++ct)
+              scn[ct] = scale_load<KIND>(r.s, c + 1 < nch ? sco[ct] + (uint32_t)(c + 1) * kSQ : kOffNone);
+          }
+        }
 #pragma unroll
         for (int ct = 0; ct < kCT; ++ct) {
-          wq[bq - 1][ct] = buf_load_x4(r.w, bn - 1 < nblk ? wo[ct] + (uint32_t)(bn - 1) * 64u : kOffNone);
-          wq[bq][ct] = buf_load_x4(r.w, bn < nblk ? wo[ct] + (uint32_t)bn * 64u : kOffNone);
+          wq[bq - 1][ct] = buf_load_x4(r.w, bn - 1 < nblk ? wo[ct] + (uint32_t)(bn - 1) * kWB : kOffNone);
+          wq[bq][ct] = buf_load_x4(r.w, bn < nblk ? wo[ct] + (uint32_t)bn * kWB : kOffNone);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -372,13 +438,13 @@ __device__ void run_pass(const GemmArgs& p, const ExpertView& ex, int n0, int m0
     }
 }
 
-template <int KIND>
+template <int KIND, bool SWZ>
 __device__ void run_expert(const GemmArgs& p, const ExpertView& ex, int n0, Stage (&st)[2]) {
   for (int m0 = ex.rb; m0 < ex.re; m0 += kRows) {
     const int mend = min(m0 + kRows, ex.re);
     if (m0 > ex.rb) lds_barrier();           // the previous pass may still be reading the stages
-    if (mend - m0 > 16) run_pass<2, KIND>(p, ex, n0, m0, mend, st);
-    else run_pass<1, KIND>(p, ex, n0, m0, mend, st);
+    if (mend - m0 > 16) run_pass<2, KIND, SWZ>(p, ex, n0, m0, mend, st);
+    else run_pass<1, KIND, SWZ>(p, ex, n0, m0, mend, st);
   }
 }
 
@@ -406,10 +472,15 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_decode_kernel(GemmArgs p, in
   }
   if (ex.rb >= ex.re) return;
   const int n0 = nt * kTileN;
+  // kinds 0/1: plain planes; 2/3: the same formats in the swizzled layout
   if (ex.kind == kNV) {
-    run_expert<kNV>(p, ex, n0, st);
+    run_expert<kNV, false>(p, ex, n0, st);
   } else if (ex.kind == kMX) {
-    run_expert<kMX>(p, ex, n0, st);
+    run_expert<kMX, false>(p, ex, n0, st);
+  } else if (ex.kind == (kNV | kSwizzled)) {
+    run_expert<kNV, true>(p, ex, n0, st);
+  } else if (ex.kind == (kMX | kSwizzled)) {
+    run_expert<kMX, true>(p, ex, n0, st);
   } else {
     for (int i = threadIdx.x; i < (ex.re - ex.rb) * kTileN; i += kThreads) {
       const int r = ex.rb + i / kTileN, col = n0 + i % kTileN;

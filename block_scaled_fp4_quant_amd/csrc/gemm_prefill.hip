@@ -71,6 +71,7 @@ constexpr int kNV = 0;
 constexpr int kMX = 1;
 constexpr int kNV16 = 2;                     // NVFP4 on f16 operands (tiles whose activation scales allow it)
 constexpr int kW4 = 3;                       // NVFP4 weights x W4A4 activations (E2M1 x UE4M3), f16 operands
+constexpr int kSwizzled = 2;                 // flag in an expert's kind: planes in the swizzled layout
 
 __host__ __device__ constexpr bool is_nv(int kind) { return kind != kMX; }
 
@@ -159,19 +160,32 @@ __device__ __forceinline__ void stage_load(const Rsrc& r, const AOffs& o, int b,
   for (int i = 0; i < 4; ++i) d.as[i] = u2f(buf_load_u32(r.as, valid ? o.as[i] + (uint32_t)b * 4u : kOffNone));
 }
 
-template <int KIND>
+// SWZ: planes in the swizzled layout (fp4_weight_swizzle).  The lane's 32 bytes are then the lane
+// pieces 2h and 2h+1 of its column (256 bytes apart), and their scale bytes sit in those pieces'
+// rows of the 4-block chunk: (b/4) * chunk bytes + (b%4) * bytes per block, the second piece 16 rows
+// further.  wo/so are the block-0 offsets of piece 2h.
+template <int KIND, bool SWZ>
 __device__ __forceinline__ void w_load(const Rsrc& r, const uint32_t (&wo)[kNT], const uint32_t (&so)[kNT],
                                        int b, int nblk, WRegs& d) {
   const bool valid = b < nblk;
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) {
-    const uint32_t o = valid ? wo[nt] + (uint32_t)b * 64u : kOffNone;
+    const uint32_t o = valid ? wo[nt] + (uint32_t)b * (SWZ ? 1024u : 64u) : kOffNone;
     d.w[nt][0] = buf_load_x4(r.w, o);
-    d.w[nt][1] = buf_load_x4(r.w, o + 16u);
+    d.w[nt][1] = buf_load_x4(r.w, o + (SWZ ? 256u : 16u));
   }
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) {
-    if constexpr (is_nv(KIND)) {
+    if constexpr (SWZ) {
+      const uint32_t ub = (uint32_t)b;
+      if constexpr (is_nv(KIND)) {
+        const uint32_t o = valid ? so[nt] + (ub >> 2) * 512u + (ub & 3u) * 2u : kOffNone;
+        d.s[nt] = buf_load_u16(r.s, o) | (buf_load_u16(r.s, o + 128u) << 16);
+      } else {
+        const uint32_t o = valid ? so[nt] + (ub >> 2) * 256u + (ub & 3u) : kOffNone;
+        d.s[nt] = buf_load_u8(r.s, o) | (buf_load_u8(r.s, o + 64u) << 8);
+      }
+    } else if constexpr (is_nv(KIND)) {
       d.s[nt] = buf_load_u32(r.s, valid ? so[nt] + (uint32_t)b * 8u : kOffNone);
     } else {
       d.s[nt] = buf_load_u16(r.s, valid ? so[nt] + (uint32_t)b * 4u : kOffNone);
@@ -273,7 +287,7 @@ struct Frags {
 // (LDS reads, 2 weight dequantizations); steps 0-3 also convert and store the next block's
 // activations, step 4 issues the loads of the block after, and before step 7 the workgroup meets
 // at the barrier that publishes the next stage.  Step 7 prepares step 0 of the next block.
-template <int KIND, int NMT>
+template <int KIND, int NMT, bool SWZ>
 __device__ __forceinline__ void run_block(const Stage& cur, Stage& nxt, const WRegs& w, const WRegs& wn,
                                           StageRegs& store_src, StageRegs& load_dst, const Rsrc& r,
                                           const AOffs& ao, int b, int nblk, WRegs& wload,
@@ -314,7 +328,7 @@ __device__ __forceinline__ void run_block(const Stage& cur, Stage& nxt, const WR
     }
     if (s == kSteps - 1) {
       __builtin_amdgcn_sched_barrier(0);
-      w_load<KIND>(r, wo, so, b + kWDepth, nblk, wload);
+      w_load<KIND, SWZ>(r, wo, so, b + kWDepth, nblk, wload);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -408,16 +422,22 @@ __device__ __forceinline__ void swiglu_epilogue(const GemmArgs& p, int m0, int m
 
 // One 128 x 256 output tile: packed rows [m0, m0 + mrows) of expert `ex`, columns [n0, n0 + 256)
 // (fused with the activation: the gate and up columns of the h columns [n0, n0 + 128)).
-template <int KIND, int NMT>
+template <int KIND, int NMT, bool SWZ>
 __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex, int m0, int mrows, int n0, Stage (&st)[2]) {
   const int tid = threadIdx.x, lane = tid & 63, c32 = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int k = p.k, nblk = k >> 7;
   constexpr int GS = is_nv(KIND) ? 16 : 32;
+  const uint32_t n16 = (uint32_t)(p.n + 15) >> 4, nq = (uint32_t)(nblk + 3) >> 2;
 
   Rsrc r;
-  r.w = make_rsrc(ex.w, (uint32_t)p.n * (uint32_t)(k / 2));
-  r.s = make_rsrc(ex.s, (uint32_t)p.n * (uint32_t)(k / GS));
+  if constexpr (SWZ) {
+    r.w = make_rsrc(ex.w, n16 * 16u * (uint32_t)(k / 2));
+    r.s = make_rsrc(ex.s, n16 * nq * (is_nv(KIND) ? 512u : 256u));
+  } else {
+    r.w = make_rsrc(ex.w, (uint32_t)p.n * (uint32_t)(k / 2));
+    r.s = make_rsrc(ex.s, (uint32_t)p.n * (uint32_t)(k / GS));
+  }
   if constexpr (KIND == kW4) {
     r.a = make_rsrc(p.a_codes, (uint32_t)p.a_rows * (uint32_t)(k / 2));
     r.as = make_rsrc(p.a_micro, (uint32_t)p.a_rows * (uint32_t)(k / 16));
@@ -443,8 +463,14 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) {
     const int col = tile_col(p, n0, wave, nt) + c32;
-    wo[nt] = col < p.n ? (uint32_t)col * (uint32_t)(k / 2) + 32u * h : kOffNone;
-    so[nt] = col < p.n ? (uint32_t)col * (uint32_t)(k / GS) + (is_nv(KIND) ? 4u : 2u) * h : kOffNone;
+    if constexpr (SWZ) {
+      const uint32_t t = (uint32_t)col >> 4, piece = 32u * h + ((uint32_t)col & 15u);   // lane piece 2h
+      wo[nt] = col < p.n ? t * (uint32_t)nblk * 1024u + 16u * piece : kOffNone;
+      so[nt] = col < p.n ? t * nq * (is_nv(KIND) ? 512u : 256u) + piece * (is_nv(KIND) ? 8u : 4u) : kOffNone;
+    } else {
+      wo[nt] = col < p.n ? (uint32_t)col * (uint32_t)(k / 2) + 32u * h : kOffNone;
+      so[nt] = col < p.n ? (uint32_t)col * (uint32_t)(k / GS) + (is_nv(KIND) ? 4u : 2u) * h : kOffNone;
+    }
   }
 
   f32x16 acc[kMT][kNT];
@@ -468,7 +494,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
   }
 #pragma unroll
   for (int j = 0; j + 1 < kWDepth; ++j) {
-    w_load<KIND>(r, wo, so, j, nblk, wr[j]);
+    w_load<KIND, SWZ>(r, wo, so, j, nblk, wr[j]);
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
@@ -476,7 +502,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
   __builtin_amdgcn_sched_barrier(0);
   stage_load<KIND>(r, ao, kADepth, nblk, sr[0]);
   __builtin_amdgcn_sched_barrier(0);
-  w_load<KIND>(r, wo, so, kWDepth - 1, nblk, wr[kWDepth - 1]);
+  w_load<KIND, SWZ>(r, wo, so, kWDepth - 1, nblk, wr[kWDepth - 1]);
   __builtin_amdgcn_sched_barrier(0);
   lds_barrier();
   Frags<KIND> f;
@@ -494,7 +520,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) {
       const int ja = (j + 1) % kADepth;
-      run_block<KIND, NMT>(st[j & 1], st[(j + 1) & 1], wr[j % kWDepth], wr[(j + 1) % kWDepth], sr[ja], sr[ja], r, ao,
+      run_block<KIND, NMT, SWZ>(st[j & 1], st[(j + 1) & 1], wr[j % kWDepth], wr[(j + 1) % kWDepth], sr[ja], sr[ja], r, ao,
                       b + j, nblk, wr[j % kWDepth], wo, so, f, acc);
     }
   }
@@ -574,6 +600,21 @@ __device__ __forceinline__ void nan_tile(const GemmArgs& p, int m0, int mrows, i
   }
 }
 
+// NVFP4 on f16 operands: only the occupied 32-row MFMA tiles of the slice are computed.
+template <bool SWZ>
+__device__ __forceinline__ void run_tile_nv16(const GemmArgs& p, const ExpertView& ex, int m0, int mrows, int nmt,
+                                              int n0, Stage (&st)[2]) {
+  if (nmt == 1) {
+    run_tile<kNV16, 1, SWZ>(p, ex, m0, mrows, n0, st);
+  } else if (nmt == 2) {
+    run_tile<kNV16, 2, SWZ>(p, ex, m0, mrows, n0, st);
+  } else if (nmt == 3) {
+    run_tile<kNV16, 3, SWZ>(p, ex, m0, mrows, n0, st);
+  } else {
+    run_tile<kNV16, 4, SWZ>(p, ex, m0, mrows, n0, st);
+  }
+}
+
 __global__ __launch_bounds__(kThreads, 2) void gemm_prefill_kernel(GemmArgs p, int ntn) {
   __shared__ Stage st[2];
   __shared__ int s_tile[3];
@@ -637,37 +678,35 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill_kernel(GemmArgs p, i
   // The last slice of an expert may hold fewer than 128 rows: only its occupied 32-row MFMA tiles
   // are computed.
   const int nmt = (mrows + 31) >> 5;
+  // kinds 0/1: plain planes; 2/3: the same formats in the swizzled layout
+  const bool swz = ex.kind == (kNV | kSwizzled) || ex.kind == (kMX | kSwizzled);
+  const int base_kind = swz ? ex.kind & ~kSwizzled : ex.kind;
   if (p.a_micro) {
-    // W4A4 activations: always exact in f16; NVFP4 weights only (other kinds give NaN below)
+    // W4A4 activations: always exact in f16; plain NVFP4 weights only (other kinds give NaN below)
     if (ex.kind == kNV) {
       if (nmt == 1) {
-        run_tile<kW4, 1>(p, ex, m0, mrows, n0, st);
+        run_tile<kW4, 1, false>(p, ex, m0, mrows, n0, st);
       } else if (nmt == 2) {
-        run_tile<kW4, 2>(p, ex, m0, mrows, n0, st);
+        run_tile<kW4, 2, false>(p, ex, m0, mrows, n0, st);
       } else if (nmt == 3) {
-        run_tile<kW4, 3>(p, ex, m0, mrows, n0, st);
+        run_tile<kW4, 3, false>(p, ex, m0, mrows, n0, st);
       } else {
-        run_tile<kW4, 4>(p, ex, m0, mrows, n0, st);
+        run_tile<kW4, 4, false>(p, ex, m0, mrows, n0, st);
       }
     } else {
       nan_tile(p, m0, mrows, n0, st);
     }
-  } else if (ex.kind == kNV) {
+  } else if (base_kind == kNV) {
     if (f16_operands_exact(p, m0, mrows)) {
-      if (nmt == 1) {
-        run_tile<kNV16, 1>(p, ex, m0, mrows, n0, st);
-      } else if (nmt == 2) {
-        run_tile<kNV16, 2>(p, ex, m0, mrows, n0, st);
-      } else if (nmt == 3) {
-        run_tile<kNV16, 3>(p, ex, m0, mrows, n0, st);
-      } else {
-        run_tile<kNV16, 4>(p, ex, m0, mrows, n0, st);
-      }
+      if (swz) run_tile_nv16<true>(p, ex, m0, mrows, nmt, n0, st);
+      else run_tile_nv16<false>(p, ex, m0, mrows, nmt, n0, st);
     } else {
-      run_tile<kNV, 4>(p, ex, m0, mrows, n0, st);
+      if (swz) run_tile<kNV, 4, true>(p, ex, m0, mrows, n0, st);
+      else run_tile<kNV, 4, false>(p, ex, m0, mrows, n0, st);
     }
-  } else if (ex.kind == kMX) {
-    run_tile<kMX, 4>(p, ex, m0, mrows, n0, st);
+  } else if (base_kind == kMX) {
+    if (swz) run_tile<kMX, 4, true>(p, ex, m0, mrows, n0, st);
+    else run_tile<kMX, 4, false>(p, ex, m0, mrows, n0, st);
   } else {
     nan_tile(p, m0, mrows, n0, st);
   }

@@ -88,6 +88,13 @@ hipError_t launch_w4a4_residual(const float* x, const int32_t* res_idx, int32_t 
                                 const uint8_t* s, float scale2, float* out, int32_t g, int32_t n, int32_t k,
                                 hipStream_t stream);
 
+// The swizzled weight layout (swizzle.hip): plane sizes and the reordering of one expert's planes
+// (kind 0 NVFP4 / 1 MXFP4; w, w_out and s_out 16-byte aligned).
+int64_t swizzled_weight_bytes(int32_t n, int32_t k);
+int64_t swizzled_scale_bytes(int32_t kind, int32_t n, int32_t k);
+hipError_t launch_weight_swizzle(const uint8_t* w, const uint8_t* s, int32_t kind, int32_t n, int32_t k,
+                                 uint8_t* w_out, uint8_t* s_out, hipStream_t stream);
+
 // Row-streaming kernel for few rows per expert (decode): every expert's weights are read once per
 // pass of 32 rows.
 hipError_t launch_gemm_decode(const GemmArgs& a, hipStream_t stream);

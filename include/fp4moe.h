@@ -47,7 +47,9 @@
 extern "C" {
 #endif
 
-enum { FP4MOE_NVFP4 = 0, FP4MOE_MXFP4 = 1 };
+/* Weight formats (the pages' kind codes), plus a layout flag OR'ed into them: kinds 2 and 3 are
+ * NVFP4 and MXFP4 planes in the swizzled layout written by fp4_weight_swizzle. */
+enum { FP4MOE_NVFP4 = 0, FP4MOE_MXFP4 = 1, FP4MOE_SWIZZLED = 2 };
 enum { FP4MOE_OK = 0, FP4MOE_EINVAL = 1, FP4MOE_ELAUNCH = 2 };
 
 /*
@@ -79,9 +81,11 @@ FP4MOE_API int act_quant_fp8(const float* x, uint8_t* codes, float* scales, int3
  * out:      f32 [g, n], overwritten.
  * Accuracy: |out - exact| <= k * 2^-24 * sum over k of |term| per output (f32 accumulation),
  * for inputs whose products stay in the f32 normal range.
- * Errors: EINVAL if g < 0, n <= 0, k <= 0, k % 128 != 0, kind not 0/1, a pointer is NULL while
- * g > 0, or g*k or n*k/2 is 2^31 or more (planes are addressed with 32-bit offsets).
- * g == 0 is a no-op.
+ * kind may also be 2 (NVFP4) or 3 (MXFP4): w_packed and w_scales are then the swizzled planes
+ * that fp4_weight_swizzle wrote for this n and k (same values, same result bit for bit).
+ * Errors: EINVAL if g < 0, n <= 0, k <= 0, k % 128 != 0, kind not in 0..3, a pointer is NULL
+ * while g > 0, or g*k or ceil(n/16)*16*k/2 is 2^31 or more (planes are addressed with 32-bit
+ * offsets).  g == 0 is a no-op.
  */
 FP4MOE_API int fp4_expert_gemm(const uint8_t* a_codes, const float* a_scales, const uint8_t* w_packed,
                     const uint8_t* w_scales, float scale2, int32_t kind, float* out, int32_t g,
@@ -98,20 +102,43 @@ FP4MOE_API int fp4_expert_gemm(const uint8_t* a_codes, const float* a_scales, co
  * offsets:  int32 [num_experts + 1], offsets[0] = 0, non-decreasing, offsets[E] = total_rows.
  * w_ptrs, s_ptrs: u64 [num_experts] device addresses of expert e's w_packed [n, k/2] and
  *           w_scales [n, k/gs] planes.
- * kinds:    int32 [num_experts] (0 NVFP4, 1 MXFP4);  scale2: f32 [num_experts] (NVFP4 only).
+ * kinds:    int32 [num_experts] (0 NVFP4, 1 MXFP4; 2 and 3 the same formats with swizzled
+ *           planes, see fp4_weight_swizzle);  scale2: f32 [num_experts] (NVFP4 only).
  * out:      f32 [total_rows, n], every row overwritten.
  * All tables are read on the device only.  Out-of-range table entries never cause an
  * out-of-bounds access: offsets are clamped to [0, total_rows]; a row whose row_ids entry is
- * outside [0, a_rows), or whose expert has a kind other than 0/1, is written as NaN.
+ * outside [0, a_rows), or whose expert has a kind outside 0..3, is written as NaN.
  * Errors: EINVAL if a_rows < 0, total_rows < 0, num_experts <= 0, n <= 0, k <= 0, k % 128 != 0,
  * row_ids is NULL while a_rows < total_rows, a pointer is NULL while total_rows > 0, or a_rows*k
- * or n*k/2 is 2^31 or more.  total_rows == 0 is a no-op.
+ * or ceil(n/16)*16*k/2 is 2^31 or more.  total_rows == 0 is a no-op.
  */
 FP4MOE_API int fp4_grouped_gemm(const uint8_t* a_codes, const float* a_scales, int32_t a_rows,
                      const int32_t* row_ids, const int32_t* offsets, int32_t num_experts,
                      int32_t total_rows, const uint64_t* w_ptrs, const uint64_t* s_ptrs,
                      const int32_t* kinds, const float* scale2, float* out, int32_t n, int32_t k,
                      hipStream_t stream);
+
+/*
+ * fp4_weight_swizzle -- a load-time reordering of one expert's planes ([GATE: ExpertRaw] values,
+ * unchanged) into the order in which the GEMM kernels' matrix-core lanes consume them, so that
+ * every 64-lane weight load reads one contiguous 1 KB run instead of 16 column rows.  With
+ * n16 = ceil(n/16), nblk = k/128, nq = ceil(nblk/4), column c = 16t + j (j < 16), 128-wide k block b,
+ * and k piece p < 4 (k = 128b + 32p .. +32 of the block):
+ *   w_swz[((t*nblk + b)*64 + 16p + j)*16 + i] = w_packed[c, 64b + 16p + i]          (i < 16)
+ *   NVFP4: s_swz[((t*nq + q)*64 + 16p + j)*8 + 2m + e] = w_scales[c, 8(4q+m) + 2p + e]  (m < 4, e < 2)
+ *   MXFP4: s_swz[((t*nq + q)*64 + 16p + j)*4 + m]      = w_scales[c, 4(4q+m) + p]       (m < 4)
+ * Entries for columns c >= n or blocks 4q+m >= nblk are written as 0.
+ * w_packed, w_scales: the plain planes of fp4_expert_gemm ([n, k/2] and [n, k/gs]), read only.
+ * kind:   0 (NVFP4) or 1 (MXFP4): the scale plane's format.
+ * w_swz:  u8 [fp4_swizzled_weight_bytes(n, k)], written.  s_swz: u8 [fp4_swizzled_scale_bytes(kind,
+ *         n, k)], written.  Must not overlap the inputs.  Pass kind | FP4MOE_SWIZZLED to the GEMMs.
+ * Errors: EINVAL if n <= 0, k <= 0, k % 128 != 0, kind not 0/1, a pointer is NULL, w_packed, w_swz
+ * or s_swz is not 16-byte aligned, or ceil(n/16)*16*k/2 is 2^31 or more.
+ */
+FP4MOE_API size_t fp4_swizzled_weight_bytes(int32_t n, int32_t k);
+FP4MOE_API size_t fp4_swizzled_scale_bytes(int32_t kind, int32_t n, int32_t k);
+FP4MOE_API int fp4_weight_swizzle(const uint8_t* w_packed, const uint8_t* w_scales, int32_t kind, int32_t n,
+                                  int32_t k, uint8_t* w_swz, uint8_t* s_swz, hipStream_t stream);
 
 /*
  * swiglu_quant_fp8 -- [GATE: the swiglu_limit saturation cell, then quant_rows].  The expert
@@ -142,7 +169,7 @@ FP4MOE_API int swiglu_quant_fp8(const float* gu, const float* row_weights, float
  *   swiglu_quant_fp8(gu, row_weights, limit, h_codes, h_scales, h_out, total_rows, inter)
  * without the f32 [total_rows, 2*inter] intermediate.  Expert planes are [2*inter, k/2] (gate columns
  * first, then up), as for fp4_grouped_gemm with n = 2*inter.  A packed row whose row_ids entry is
- * out of range, or whose expert has a kind other than 0/1, enters the activation as NaN gate and up
+ * out of range, or whose expert has a kind outside 0..3, enters the activation as NaN gate and up
  * values, exactly as the unfused route's NaN GEMM output would.
  * Arguments as for fp4_grouped_gemm and swiglu_quant_fp8:
  * row_weights: f32 [total_rows] or NULL (per packed row);  limit: [host] f32 > 0 (+Inf: no clamp).

@@ -76,7 +76,7 @@ def test_swiglu_quant_null_and_noop(lib):
 
 
 @pytest.mark.parametrize("g,n,k,kind", [(-1, 16, 128, 0), (4, 0, 128, 0), (4, 16, 96, 0),
-                                        (4, 16, 128, 2), (4, 16, 128, -1), (1 << 24, 16, 256, 0),
+                                        (4, 16, 128, 4), (4, 16, 128, -1), (1 << 24, 16, 256, 0),
                                         (4, 1 << 20, 8192, 1)])
 def test_expert_gemm_rejects(lib, g, n, k, kind):
     assert lib.fp4_expert_gemm(BAD, BAD, BAD, BAD, 1.0, kind, BAD, g, n, k, NULL) == 1
@@ -229,3 +229,23 @@ def test_w4a4_rejects(lib):
     assert lib.w4a4_gemm(NULL, NULL, NULL, NULL, NULL, ctypes.c_float(1.0), NULL, NULL, 0, NULL, 0, 8, 128, NULL) == 0
     for fn in ("act_quant_fp4", "loud_channels", "w4a4_gemm"):
         assert fn in declared_functions()
+
+
+def test_swizzle_sizes_and_rejects(lib):
+    # sizes: n rounded up to 16 columns; scales per chunk of 4 blocks (NVFP4 8 B, MXFP4 4 B per lane piece)
+    assert lib.fp4_swizzled_weight_bytes(2048, 7168) == 2048 * 3584
+    assert lib.fp4_swizzled_weight_bytes(20, 256) == 32 * 128
+    assert lib.fp4_swizzled_scale_bytes(0, 2048, 7168) == 2048 * 7168 // 16
+    assert lib.fp4_swizzled_scale_bytes(1, 2048, 7168) == 2048 * 7168 // 32
+    assert lib.fp4_swizzled_scale_bytes(0, 16, 128) == 1 * 1 * 64 * 8          # one partial chunk
+    assert lib.fp4_swizzled_scale_bytes(2, 16, 128) == 0                       # kind must be 0/1
+    assert lib.fp4_swizzled_weight_bytes(16, 100) == 0
+    A = ctypes.c_void_p(0x10000)
+    assert lib.fp4_weight_swizzle(A, A, 0, 16, 100, A, A, NULL) == 1          # k % 128
+    assert lib.fp4_weight_swizzle(A, A, 2, 16, 128, A, A, NULL) == 1          # kind
+    assert lib.fp4_weight_swizzle(A, A, 0, 0, 128, A, A, NULL) == 1           # n
+    assert lib.fp4_weight_swizzle(ctypes.c_void_p(0x10008), A, 0, 16, 128, A, A, NULL) == 1   # alignment
+    assert lib.fp4_weight_swizzle(NULL, A, 0, 16, 128, A, A, NULL) == 1
+    assert lib.fp4moe_last_error().decode().startswith("fp4_weight_swizzle")
+    # the GEMM takes kinds 0..3 and rejects others before any launch
+    assert lib.fp4_expert_gemm(A, A, A, A, ctypes.c_float(1.0), 4, A, 1, 16, 128, NULL) == 1
