@@ -138,7 +138,7 @@ def main():
                          "its epilogue (fused), or the GEMM writing f32 gate/up values followed by "
                          "swiglu_quant_fp8 (unfused)")
     ap.add_argument("--layout", default="swizzled", choices=["swizzled", "plain"],
-                    help="config3/config4: expert planes in the swizzled layout (fp4_weight_swizzle, "
+                    help="config3/config4/chain4: expert planes in the swizzled layout (fp4_weight_swizzle, "
                          "run once at load time before the timed region) or as the plain [n, k/2] and "
                          "[n, k/gs] planes")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
@@ -313,6 +313,11 @@ def run_chain(args, torch, fp4, dev):
     kinds = torch.from_numpy(ch.kinds).to(dev)
     up = upload_bank(ch.up, torch, dev)
     dn = upload_bank(ch.down, torch, dev)
+    if args.layout == "swizzled":
+        ub, us, uw, usp, kinds = swizzle_bank(ch.up, torch, fp4, dev, up[0], up[1])
+        up = (ub, us, uw, usp, up[4])
+        db, ds, dw, dsp, _ = swizzle_bank(ch.down, torch, fp4, dev, dn[0], dn[1])
+        dn = (db, ds, dw, dsp, dn[4])
     T, Hd = ch.x.shape
     R, I = T * top, ch.inter
     ids = torch.empty((T, top), dtype=torch.int32, device=dev)
@@ -392,7 +397,7 @@ def run_chain(args, torch, fp4, dev):
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8xfp4->f32", "data": "synthetic",
         "config": {"workload": ch.name, "tokens": int(T), "experts": int(E), "top_k": top,
                    "routed_rows": int(R), "hidden": int(Hd), "inter": int(I),
-                   "gate_up": args.gate_up, "us": {n: round(p * 1e3, 2) for n, p in zip(names, part)},
+                   "gate_up": args.gate_up, "weight_layout": args.layout, "us": {n: round(p * 1e3, 2) for n, p in zip(names, part)},
                    "swiglu_quant_gbs": None if fused else round(sw_gbs, 1), "combine_gbs": round(cb_gbs, 1)},
         "roofline": {"bound": "mfma", "achieved": round(tf_up, 1), "peak": MFMA_PEAK_TFLOPS["f16"],
                      "unit": "TFLOP/s", "frac": round(tf_up / MFMA_PEAK_TFLOPS["f16"], 4), "traffic": None},
