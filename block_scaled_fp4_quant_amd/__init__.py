@@ -90,11 +90,12 @@ def version() -> str:
     return lib().fp4moe_version().decode()
 
 
-SCHEDULE_AUTO, SCHEDULE_ROWSTREAM, SCHEDULE_TILED = 0, 1, 2
+SCHEDULE_AUTO, SCHEDULE_ROWSTREAM, SCHEDULE_TILED, SCHEDULE_SPLITK = 0, 1, 2, 3
 
 
 def set_gemm_schedule(schedule: int) -> None:
-    """Force the GEMM kernel choice (0 automatic, 1 row-streaming, 2 tiled); a test hook."""
+    """Force the GEMM kernel choice (0 automatic, 1 row-streaming, 2 tiled, 3 split-k for
+    single-expert calls with g <= 16 and k <= 8192); a test hook."""
     _check(lib().fp4moe_set_gemm_schedule(int(schedule)), "fp4moe_set_gemm_schedule")
 
 

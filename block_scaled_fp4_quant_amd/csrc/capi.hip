@@ -58,7 +58,13 @@ std::atomic<int> g_schedule{FP4MOE_SCHEDULE_AUTO};
 
 hipError_t launch_gemm(const fp4moe::GemmArgs& a, int64_t rows, int64_t experts, hipStream_t stream) {
   int s = g_schedule.load(std::memory_order_relaxed);
-  if (s == FP4MOE_SCHEDULE_AUTO) s = (rows <= 32 * experts) ? FP4MOE_SCHEDULE_ROWSTREAM : FP4MOE_SCHEDULE_TILED;
+  // One expert with few rows: the split-k kernel (the row-streaming kernel would launch only
+  // ceil(n/256) workgroups).
+  if ((s == FP4MOE_SCHEDULE_AUTO || s == FP4MOE_SCHEDULE_SPLITK) && !a.offsets &&
+      fp4moe::gemm_skinny_fits((int32_t)rows, a.n, a.k))
+    return fp4moe::launch_gemm_skinny(a, stream);
+  if (s == FP4MOE_SCHEDULE_AUTO || s == FP4MOE_SCHEDULE_SPLITK)
+    s = (rows <= 32 * experts) ? FP4MOE_SCHEDULE_ROWSTREAM : FP4MOE_SCHEDULE_TILED;
   return s == FP4MOE_SCHEDULE_TILED ? fp4moe::launch_gemm_prefill(a, stream) : fp4moe::launch_gemm_decode(a, stream);
 }
 
@@ -396,8 +402,8 @@ int fp4_weight_swizzle(const uint8_t* w_packed, const uint8_t* w_scales, int32_t
 }
 
 int fp4moe_set_gemm_schedule(int32_t schedule) {
-  if (schedule < FP4MOE_SCHEDULE_AUTO || schedule > FP4MOE_SCHEDULE_TILED)
-    return fail(FP4MOE_EINVAL, "fp4moe_set_gemm_schedule: schedule = %d is not 0, 1 or 2", (int)schedule);
+  if (schedule < FP4MOE_SCHEDULE_AUTO || schedule > FP4MOE_SCHEDULE_SPLITK)
+    return fail(FP4MOE_EINVAL, "fp4moe_set_gemm_schedule: schedule = %d is not 0, 1, 2 or 3", (int)schedule);
   g_schedule.store(schedule, std::memory_order_relaxed);
   return ok();
 }

@@ -1,0 +1,207 @@
+// gemm_skinny.hip -- FP8-activation x block-scaled FP4 GEMM of ONE expert with few rows (g <= 16),
+// split over k so that a single decode-shaped launch fills the chip.
+//
+// What is computed is the same definition as the other two GEMM kernels (memra-engine 0.98.0
+// dsv4_native_gemm_gate.rs page, `f64_ref` / `ExpertRaw`):
+//   out[r, c] = sum_j ( sum_{k in group j} E4M3(A[r,k]) * E2M1(W[c,k]) ) * ws[c,j] * as[r, k/128]
+// accumulated in f32.  A single expert of the decode shapes (n = 2048 or 7168 columns) gives the
+// row-streaming kernel only n/256 = 8..28 workgroups, far too few to stream 8 MB of weights; this
+// kernel gives each workgroup 16 columns (n/16 = 128..448 workgroups) and splits k over its 4
+// wavefronts: wavefront w takes the 128-wide blocks b = w, w+4, w+8, ..., so the 4 wavefronts of a
+// workgroup read 4 consecutive 1 KB weight runs at a time with swizzled planes.
+//
+// Data movement: every weight load of a wavefront (up to kRing blocks, all of them for k <= 8192) is
+// issued before anything else, with its scale bytes; then the workgroup stages the activation rows
+// (g x k bytes, rows padded by 16 bytes against LDS bank conflicts) and their scales in LDS with
+// coalesced 16-byte loads, which hit L2 after the first workgroup.
+//
+// Arithmetic per block (lane c16 = lane%16 holds column 16t + c16 and activation row c16; lane group
+// g = lane/16 holds k = 32g .. +32 of the block), as in the row-streaming kernel: NVFP4 on exact f16
+// operands (nibble -> f16 times the E4M3 scale in f16), MXFP4 on exact bf16 operands (the E8M0 scale
+// applied by the conversion), four 16x16x32 MFMAs cover one activation-scale group, whose partial
+// tile is scaled by as[r, b] with one f32 FMA per output.  The 4 wavefronts' f32 tiles are then
+// summed through LDS in wavefront order 0, 1, 2, 3 (a fixed order: the result does not depend on g
+// or on timing), and scale2 multiplies the sum.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace fp4moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kRing = 16;                    // weight blocks in flight per wavefront
+constexpr int kMaxRows = 16;
+constexpr int kMaxK = 8192;
+constexpr int kARow = kMaxK + 16;            // LDS row of activation codes (padded)
+constexpr int kNV = 0;
+constexpr int kMX = 1;
+constexpr int kSwizzled = 2;
+
+struct Smem {
+  uint8_t a[kMaxRows * kARow];               // activation codes [row][k (+16)]
+  float as[(kMaxK / 128) * kMaxRows];        // activation scales [block][row]
+  f32x4 red[kWaves][64];                     // per-wavefront result tiles
+};
+
+template <bool SWZ>
+__device__ __forceinline__ u32x4 wload(rsrc_t r, uint32_t off) {
+  if constexpr (SWZ) return buf_load_x4_nt(r, off);
+  else return buf_load_x4(r, off);
+}
+
+template <int KIND, bool SWZ>
+__device__ void run(const GemmArgs& p, int t, Smem& sm) {
+  const int tid = threadIdx.x, lane = tid & 63, c16 = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int k = p.k, nblk = k >> 7, nq = (nblk + 3) >> 2, rows = p.total_rows;
+  const int col = 16 * t + c16;
+  const uint32_t n16 = (uint32_t)(p.n + 15) >> 4;
+
+  rsrc_t rw, rs;
+  if constexpr (SWZ) {
+    rw = make_rsrc(p.w, n16 * 16u * (uint32_t)(k / 2));
+    rs = make_rsrc(p.s, n16 * (uint32_t)nq * (KIND == kNV ? 512u : 256u));
+  } else {
+    rw = make_rsrc(p.w, (uint32_t)p.n * (uint32_t)(k / 2));
+    rs = make_rsrc(p.s, (uint32_t)p.n * (uint32_t)(k / (KIND == kNV ? 16 : 32)));
+  }
+  // Block-0 offsets of this lane's weight piece and scale bytes (kOffNone past n).
+  const uint32_t piece = (uint32_t)(16 * g + c16);
+  uint32_t w0, s0;
+  if constexpr (SWZ) {
+    w0 = (uint32_t)t * (uint32_t)nblk * 1024u + 16u * piece;
+    s0 = ((uint32_t)t * (uint32_t)nq * 64u + piece) * (KIND == kNV ? 8u : 4u);
+  } else {
+    w0 = (uint32_t)col * (uint32_t)(k / 2) + 16u * g;
+    s0 = KIND == kNV ? (uint32_t)col * (uint32_t)(k / 16) + 2u * g : (uint32_t)col * (uint32_t)(k / 32) + g;
+  }
+  if (col >= p.n) w0 = s0 = kOffNone;
+  auto w_off = [&](int b) -> uint32_t {
+    if (b >= nblk || w0 == kOffNone) return kOffNone;
+    return w0 + (uint32_t)b * (SWZ ? 1024u : 64u);
+  };
+  // NVFP4: the scale pair of the lane's piece (2 bytes); MXFP4: its scale byte.
+  auto s_load = [&](int b) -> uint32_t {
+    uint32_t o = kOffNone;
+    if (b < nblk && s0 != kOffNone) {
+      const uint32_t ub = (uint32_t)b;
+      if constexpr (SWZ) o = s0 + (ub >> 2) * (KIND == kNV ? 512u : 256u) + (ub & 3u) * (KIND == kNV ? 2u : 1u);
+      else o = s0 + ub * (KIND == kNV ? 8u : 4u);
+    }
+    if constexpr (KIND == kNV) return buf_load_u16(rs, o);
+    else return buf_load_u8(rs, o);
+  };
+
+  // Weight ring: the wavefront's blocks b = wave + 4 i.
+  const int nbw = (nblk - wave + kWaves - 1) / kWaves;
+  u32x4 wq[kRing];
+  uint32_t sq[kRing];
+#pragma unroll
+  for (int j = 0; j < kRing; ++j) {
+    const int b = wave + kWaves * j;
+    wq[j] = wload<SWZ>(rw, j < nbw ? w_off(b) : kOffNone);
+    sq[j] = s_load(j < nbw ? b : nblk);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Stage the activation rows and their scales (rows >= g and scales of rows >= g read as zero).
+  {
+    const rsrc_t ra = make_rsrc(p.a_codes, (uint32_t)rows * (uint32_t)k);
+    const int per_row = k >> 4;                          // 16-byte pieces per row
+    for (int i = tid; i < kMaxRows * per_row; i += kThreads) {
+      const int r = i / per_row, q = i - r * per_row;
+      const u32x4 v = buf_load_x4(ra, r < rows ? (uint32_t)r * (uint32_t)k + 16u * q : kOffNone);
+      *reinterpret_cast<u32x4*>(sm.a + r * kARow + 16 * q) = v;
+    }
+    const rsrc_t rsa = make_rsrc(p.a_scales, (uint32_t)rows * (uint32_t)nblk * 4u);
+    for (int i = tid; i < kMaxRows * nblk; i += kThreads) {
+      const int b = i / kMaxRows, r = i - b * kMaxRows;
+      sm.as[i] = u2f(buf_load_u32(rsa, r < rows ? ((uint32_t)r * (uint32_t)nblk + b) * 4u : kOffNone));
+    }
+  }
+  __syncthreads();
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int i0 = 0; i0 < nbw; i0 += kRing) {
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) {
+      const int i = i0 + j;
+      if (i < nbw) {
+        const int b = wave + kWaves * i;
+        const uint8_t* ap = sm.a + c16 * kARow + b * 128 + 32 * g;
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(ap);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(ap + 16);
+        f32x4 part = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (KIND == kNV) {
+          const h16x2 ws = e4m3x2_to_f16<false>(sq[j]);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const u32x4& aq = m < 2 ? a0 : a1;
+            const h16x8 af = e4m3x8_to_f16(aq[2 * (m & 1)], aq[2 * (m & 1) + 1]);
+            part = mfma16x16x32_f16(af, e2m1x8_scaled_f16(wq[j][m], ws[m >> 1]), part);
+          }
+        } else {
+          const float sv = u2f((sq[j] & 0xFFu) << 23);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const u32x4& aq = m < 2 ? a0 : a1;
+            const bf16x8 af = e4m3x8_to_bf16(aq[2 * (m & 1)], aq[2 * (m & 1) + 1]);
+            part = mfma16x16x32_bf16(af, e2m1x8_pow2_bf16(wq[j][m], sv), part);
+          }
+        }
+        // the partial tile covers one activation-scale group: result row 4g+v takes as[4g+v, b]
+        const f32x4 as = *reinterpret_cast<const f32x4*>(sm.as + b * kMaxRows + 4 * g);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[v] = fmaf(part[v], as[v], acc[v]);
+      }
+      // refill the slot with the block kRing further on
+      const int inext = i + kRing;
+      wq[j] = wload<SWZ>(rw, inext < nbw ? w_off(wave + kWaves * inext) : kOffNone);
+      sq[j] = s_load(inext < nbw ? wave + kWaves * inext : nblk);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Sum the wavefronts' tiles in wavefront order, apply scale2, store rows 4g+v of column col.
+  sm.red[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    f32x4 sum = sm.red[0][lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      const f32x4 o = sm.red[w][lane];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sum[v] += o[v];
+    }
+    const float post = KIND == kNV ? p.scale2 : 1.0f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = 4 * g + v;
+      if (r < rows && col < p.n) p.out[(size_t)r * p.n + col] = sum[v] * post;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void gemm_skinny_kernel(GemmArgs p) {
+  __shared__ Smem sm;
+  const int t = blockIdx.x;
+  if (p.kind == kNV) run<kNV, false>(p, t, sm);
+  else if (p.kind == kMX) run<kMX, false>(p, t, sm);
+  else if (p.kind == (kNV | kSwizzled)) run<kNV, true>(p, t, sm);
+  else if (p.kind == (kMX | kSwizzled)) run<kMX, true>(p, t, sm);
+}
+
+}  // namespace
+
+bool gemm_skinny_fits(int32_t g, int32_t n, int32_t k) {
+  return g >= 1 && g <= kMaxRows && k >= 128 && k <= kMaxK && n >= 1;
+}
+
+hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
+  const int tiles = (a.n + 15) / 16;
+  hipLaunchKernelGGL(gemm_skinny_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace fp4moe

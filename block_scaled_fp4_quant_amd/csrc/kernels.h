@@ -99,6 +99,11 @@ hipError_t launch_weight_swizzle(const uint8_t* w, const uint8_t* s, int32_t kin
 // pass of 32 rows.
 hipError_t launch_gemm_decode(const GemmArgs& a, hipStream_t stream);
 
+// Split-k kernel for ONE expert with few rows (single-expert calls, offsets == nullptr): 16-column
+// workgroups whose 4 wavefronts split k; requires gemm_skinny_fits(g, n, k) (g <= 16, k <= 8192).
+bool gemm_skinny_fits(int32_t g, int32_t n, int32_t k);
+hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);
+
 // Tiled matrix-core kernel for many rows per expert (prefill): 128 x 256 output tiles.
 hipError_t launch_gemm_prefill(const GemmArgs& a, hipStream_t stream);
 

@@ -33,12 +33,12 @@ def orc():
     return oracle
 
 
-@pytest.fixture(params=[1, 2], ids=["rowstream", "tiled"])
+@pytest.fixture(params=[1, 2, 3], ids=["rowstream", "tiled", "splitk"])
 def schedule(request):
-    """Run a GPU test with each GEMM kernel forced (row-streaming = 1, tiled = 2): both must meet
-    the same contract."""
+    """Run a GPU test with each GEMM kernel forced (row-streaming = 1, tiled = 2, split-k = 3 for
+    single-expert calls with g <= 16, other calls as automatic): all must meet the same contract."""
     import block_scaled_fp4_quant_amd as fp4
-    assert request.param in (fp4.SCHEDULE_ROWSTREAM, fp4.SCHEDULE_TILED)
+    assert request.param in (fp4.SCHEDULE_ROWSTREAM, fp4.SCHEDULE_TILED, fp4.SCHEDULE_SPLITK)
     fp4.set_gemm_schedule(request.param)
     yield request.param
     fp4.set_gemm_schedule(fp4.SCHEDULE_AUTO)

@@ -93,14 +93,17 @@ def test_exact_arm_bit_identity(orc, schedule, kind, g, n, k):
 
 
 def test_determinism_and_row_invariance(orc, schedule):
-    wl = workloads.single_random(5, 24, 256, 1024, NV)
+    # 24 rows, or 16 under the split-k schedule (the largest batch that kernel takes: the batch and
+    # its single rows must run on the same kernel)
+    g = 16 if schedule == fp4.SCHEDULE_SPLITK else 24
+    wl = workloads.single_random(5, g, 256, 1024, NV)
     codes, scales = fp4.act_quant_fp8(dev(wl.x))
     w, s = dev(wl.expert.w), dev(wl.expert.s)
     o1 = fp4.fp4_expert_gemm(codes, scales, w, s, wl.expert.scale2, NV)
     o2 = fp4.fp4_expert_gemm(codes, scales, w, s, wl.expert.scale2, NV)
     assert torch.equal(o1, o2)
     # each row alone gives the same bits as in the batched launch
-    for r in (0, 7, 16, 23):
+    for r in (0, 7, g - 8, g - 1):
         o_r = fp4.fp4_expert_gemm(codes[r:r + 1].contiguous(), scales[r:r + 1].contiguous(), w, s,
                                   wl.expert.scale2, NV)
         assert torch.equal(o_r[0], o1[r])
@@ -132,6 +135,9 @@ def test_grouped_small_mixed(orc, schedule, seed, T, E, top, n, k):
 
 
 def test_grouped_matches_single_expert_bits(orc, schedule):
+    if schedule == fp4.SCHEDULE_SPLITK:
+        pytest.skip("split-k runs single-expert calls only: its additions are ordered differently "
+                    "from the grouped kernels' (both within the bound, tested elsewhere)")
     wl = workloads.grouped_random(4, 96, 8, 3, 128, 512, kinds=[NV, MX] * 4)
     gd = GroupedDevice(wl)
     codes, scales, out = gd.step()
@@ -269,3 +275,46 @@ def test_tiles_outside_the_f16_range(orc, schedule, factor):
     if factor != 1.0:
         assert ((s < 2.0 ** -15) | (s > 2.0 ** 7)).any()
     grouped_check(gd, orc, out)
+
+
+@pytest.mark.parametrize("kind", [NV, MX])
+@pytest.mark.parametrize("swz", [False, True])
+@pytest.mark.parametrize("g,n,k", [(16, 2048, 8192), (1, 100, 128), (7, 2000, 1152), (16, 7168, 2048),
+                                   (2, 33, 640)])
+def test_splitk_single_expert(orc, kind, swz, g, n, k):
+    """The split-k kernel at its limits (g = 16, k = 8192), ragged n and k, both layouts: within the
+    bound, run-to-run identical, and each row alone gives the batch's bits."""
+    fp4.set_gemm_schedule(fp4.SCHEDULE_SPLITK)
+    try:
+        wl = workloads.single_random(900 + g + n + k + kind, g, n, k, kind, scale2=2.0 ** -7, x_scale=3.0)
+        ex = wl.expert
+        codes, scales = fp4.act_quant_fp8(dev(wl.x))
+        if swz:
+            w, s = fp4.fp4_weight_swizzle(dev(ex.w), dev(ex.s), kind)
+            kd = kind | fp4.SWIZZLED
+        else:
+            w, s, kd = dev(ex.w), dev(ex.s), kind
+        o1 = fp4.fp4_expert_gemm(codes, scales, w, s, ex.scale2, kd, n=n)
+        o2 = fp4.fp4_expert_gemm(codes, scales, w, s, ex.scale2, kd, n=n)
+        last = fp4.fp4_expert_gemm(codes[g - 1:].contiguous(), scales[g - 1:].contiguous(), w, s, ex.scale2, kd, n=n)
+        torch.cuda.synchronize()
+    finally:
+        fp4.set_gemm_schedule(fp4.SCHEDULE_AUTO)
+    assert torch.equal(o1, o2)
+    assert torch.equal(last[0], o1[g - 1])
+    rc, rs = orc.act_quant(wl.x)
+    ref, absp = orc.expert_gemm(rc, rs, ex.w, ex.s, ex.scale2, kind)
+    check_bound(o1.cpu().numpy(), ref, absp, k, f"split-k g={g} n={n} k={k} kind={kind} swz={swz}")
+
+
+def test_splitk_limits_fall_back(orc):
+    """g = 17 or k = 8320 do not fit the split-k kernel: the call runs the row-streaming kernel and
+    still meets the bound."""
+    for g, k in ((17, 1024), (4, 8320)):
+        fp4.set_gemm_schedule(fp4.SCHEDULE_SPLITK)
+        try:
+            wl = workloads.single_random(31 + g + k, g, 96, k, NV)
+            got, ref, absp = run_single(wl, orc)
+        finally:
+            fp4.set_gemm_schedule(fp4.SCHEDULE_AUTO)
+        check_bound(got, ref, absp, k, f"fallback g={g} k={k}")
