@@ -128,7 +128,8 @@ def main():
     # before the rate settles; the default warm-up covers that so the timed steps see the steady
     # state.
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="config3", choices=["config3", "config4", "chain4", "w4a4"],
+    ap.add_argument("--workload", default="config3",
+                    choices=["config3", "config4", "chain4", "w4a4", "config1", "config2"],
                     help="config3: grouped decode GEMM; config4: grouped prefill GEMM; chain4: the "
                          "whole prefill expert layer from router logits (top-k, packing, gate/up GEMM, "
                          "swiglu+quant, down GEMM, combine); w4a4: the W4A4 variant on one NVFP4 "
@@ -137,6 +138,8 @@ def main():
                     help="chain4 only: the gate/up GEMM with the activation and its quantization in "
                          "its epilogue (fused), or the GEMM writing f32 gate/up values followed by "
                          "swiglu_quant_fp8 (unfused)")
+    ap.add_argument("--rows", type=int, default=8,
+                    help="config1 only: activation rows g (1, 2, 4 or 8)")
     ap.add_argument("--layout", default="swizzled", choices=["swizzled", "plain"],
                     help="config3/config4/chain4: expert planes in the swizzled layout (fp4_weight_swizzle, "
                          "run once at load time before the timed region) or as the plain [n, k/2] and "
@@ -166,6 +169,8 @@ def main():
         return run_chain(args, torch, fp4, dev)
     if args.workload == "w4a4":
         return run_w4a4(args, torch, fp4, dev)
+    if args.workload in ("config1", "config2"):
+        return run_single_expert(args, torch, fp4, dev)
 
     t0 = time.perf_counter()
     wl = workloads.config3() if args.workload == "config3" else workloads.config4()
@@ -289,6 +294,78 @@ def swizzle_bank(wl, torch, fp4, dev, w_bank, s_bank):
     s_ptrs = torch.from_numpy((s_swz.data_ptr() + s_off[:-1]).astype(np.int64)).to(dev)
     kinds = torch.from_numpy((wl.kinds | fp4.SWIZZLED).astype(np.int32)).to(dev)
     return w_swz, s_swz, w_ptrs, s_ptrs, kinds
+
+
+def run_single_expert(args, torch, fp4, dev):
+    """One expert of a decode shape (config1: MXFP4, g rows, k=7168, n=2048; config2: NVFP4, 16 rows,
+    k=2048, n=7168): act_quant_fp8 + fp4_expert_gemm per step.  A single expert's 8 MB fits the
+    256 MB Infinity Cache, so the steps rotate over enough copies of the planes (>= 72 and
+    >= 560 MB) that every step streams its weights from HBM.  value = weight-stream TB/s."""
+    wl = workloads.config1(args.rows) if args.workload == "config1" else workloads.config2()
+    ex = wl.expert
+    g, k = wl.x.shape
+    n = ex.w.shape[0]
+    log(f"workload: {wl.name}")
+    x = torch.from_numpy(wl.x).to(dev)
+    w0, s0 = torch.from_numpy(ex.w).to(dev), torch.from_numpy(ex.s).to(dev)
+    wbytes = ex.w.size + ex.s.size + (4 if ex.kind == workloads.NVFP4 else 0)
+    ncopy = max(72, -(-(560 << 20) // wbytes))
+    if args.layout == "swizzled":
+        planes = [fp4.fp4_weight_swizzle(w0, s0, ex.kind) for _ in range(ncopy)]
+        kind = ex.kind | fp4.SWIZZLED
+    else:
+        planes = [(w0.clone(), s0.clone()) for _ in range(ncopy)]
+        kind = ex.kind
+    codes = torch.empty((g, k), dtype=torch.uint8, device=dev)
+    scales = torch.empty((g, k // 128), dtype=torch.float32, device=dev)
+    out = torch.empty((g, n), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        if ev:
+            ev[0].record(stream)
+        fp4.act_quant_fp8(x, codes, scales, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        w, sc = planes[i % ncopy]
+        fp4.fp4_expert_gemm(codes, scales, w, sc, ex.scale2, kind, out=out, stream=stream, n=n)
+        if ev:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for i in range(K):
+        step(args.warmup + i, ev[i])
+    torch.cuda.synchronize()
+    step_ms = ev[0][0].elapsed_time(ev[K - 1][2]) / K
+    aq_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    alg = wbytes + g * k + g * (k // 128) * 4 + g * n * 4
+    achieved = alg / (gemm_ms * 1e-3) / 1e9
+    log(f"{K} steps: {step_ms * 1e3:.2f} us/step (act_quant {aq_ms * 1e3:.2f} us, GEMM {gemm_ms * 1e3:.2f} us); "
+        f"{ncopy} weight copies rotated")
+    import oracle
+    oracle.build()
+    t0 = time.perf_counter()
+    rc, rs = oracle.act_quant(wl.x)
+    oracle.expert_gemm(rc, rs, ex.w, ex.s, ex.scale2, ex.kind, threads=1)
+    t_cpu = time.perf_counter() - t0
+    result = {
+        "metric": METRIC, "value": round(wbytes / (step_ms * 1e-3) / 1e12, 4), "unit": "TB/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8xfp4->f32", "data": "synthetic",
+        "config": {"workload": wl.name, "rows": int(g), "k": int(k), "n": int(n), "weight_layout": args.layout,
+                   "weight_copies_rotated": int(ncopy), "weight_stream_bytes": int(wbytes),
+                   "gemm_us": round(gemm_ms * 1e3, 2), "act_quant_us": round(aq_ms * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": {"value": wbytes / t_cpu / 1e12, "unit": "TB/s", "cores": 1, "kind": "oracle",
+                         "sample": f"oracle act-quant + f64 expert GEMM of the whole step, one thread, {t_cpu:.2f} s"},
+    }
+    print(json.dumps(result), flush=True)
 
 
 def upload_bank(gw, torch, dev):

@@ -10,10 +10,10 @@
 // wavefronts: wavefront w takes the 128-wide blocks b = w, w+4, w+8, ..., so the 4 wavefronts of a
 // workgroup read 4 consecutive 1 KB weight runs at a time with swizzled planes.
 //
-// Data movement: every weight load of a wavefront (up to kRing blocks, all of them for k <= 8192) is
-// issued before anything else, with its scale bytes; then the workgroup stages the activation rows
-// (g x k bytes, rows padded by 16 bytes against LDS bank conflicts) and their scales in LDS with
-// coalesced 16-byte loads, which hit L2 after the first workgroup.
+// Data movement: every load of a wavefront (up to kRing blocks, all of them for k <= 8192) is issued
+// before anything waits: per block the lane's 16 weight bytes, its scale bytes and its 32 bytes of
+// the activation operand (which hit L2 after the first workgroup).  Only the activation scales go
+// through LDS, loaded together at the start.
 //
 // Arithmetic per block (lane c16 = lane%16 holds column 16t + c16 and activation row c16; lane group
 // g = lane/16 holds k = 32g .. +32 of the block), as in the row-streaming kernel: NVFP4 on exact f16
@@ -28,18 +28,16 @@
 namespace fp4moe {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-constexpr int kRing = 16;                    // weight blocks in flight per wavefront
+constexpr int kThreads = 512;
+constexpr int kWaves = 8;
+constexpr int kRing = 7;                    // blocks in flight per wavefront (all of them for k <= 8192)
 constexpr int kMaxRows = 16;
 constexpr int kMaxK = 8192;
-constexpr int kARow = kMaxK + 16;            // LDS row of activation codes (padded)
 constexpr int kNV = 0;
 constexpr int kMX = 1;
 constexpr int kSwizzled = 2;
 
 struct Smem {
-  uint8_t a[kMaxRows * kARow];               // activation codes [row][k (+16)]
   float as[(kMaxK / 128) * kMaxRows];        // activation scales [block][row]
   f32x4 red[kWaves][64];                     // per-wavefront result tiles
 };
@@ -93,32 +91,37 @@ __device__ void run(const GemmArgs& p, int t, Smem& sm) {
     else return buf_load_u8(rs, o);
   };
 
-  // Weight ring: the wavefront's blocks b = wave + 4 i.
+  // Activation operand of block b: row c16, bytes 32g .. +32 of the block (rows >= g read zero).
+  const rsrc_t ra = make_rsrc(p.a_codes, (uint32_t)rows * (uint32_t)k);
+  const uint32_t a0 = c16 < rows ? (uint32_t)c16 * (uint32_t)k + 32u * g : kOffNone;
+  auto a_off = [&](int b) -> uint32_t { return (b < nblk && a0 != kOffNone) ? a0 + (uint32_t)b * 128u : kOffNone; };
+
+  // Ring: the wavefront's blocks b = wave + 4 i, weights, scale bytes and activation operand of
+  // each, all issued before anything waits.
   const int nbw = (nblk - wave + kWaves - 1) / kWaves;
-  u32x4 wq[kRing];
+  u32x4 wq[kRing], aq[kRing][2];
   uint32_t sq[kRing];
 #pragma unroll
   for (int j = 0; j < kRing; ++j) {
-    const int b = wave + kWaves * j;
-    wq[j] = wload<SWZ>(rw, j < nbw ? w_off(b) : kOffNone);
-    sq[j] = s_load(j < nbw ? b : nblk);
+    const int b = j < nbw ? wave + kWaves * j : nblk;
+    wq[j] = wload<SWZ>(rw, w_off(b));
+    sq[j] = s_load(b);
+    aq[j][0] = buf_load_x4(ra, a_off(b));
+    aq[j][1] = buf_load_x4(ra, a_off(b) == kOffNone ? kOffNone : a_off(b) + 16u);
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // Stage the activation rows and their scales (rows >= g and scales of rows >= g read as zero).
+  // Activation scales [block][row] in LDS (at most 4 per thread, loaded together).
   {
-    const rsrc_t ra = make_rsrc(p.a_codes, (uint32_t)rows * (uint32_t)k);
-    const int per_row = k >> 4;                          // 16-byte pieces per row
-    for (int i = tid; i < kMaxRows * per_row; i += kThreads) {
-      const int r = i / per_row, q = i - r * per_row;
-      const u32x4 v = buf_load_x4(ra, r < rows ? (uint32_t)r * (uint32_t)k + 16u * q : kOffNone);
-      *reinterpret_cast<u32x4*>(sm.a + r * kARow + 16 * q) = v;
-    }
     const rsrc_t rsa = make_rsrc(p.a_scales, (uint32_t)rows * (uint32_t)nblk * 4u);
-    for (int i = tid; i < kMaxRows * nblk; i += kThreads) {
-      const int b = i / kMaxRows, r = i - b * kMaxRows;
-      sm.as[i] = u2f(buf_load_u32(rsa, r < rows ? ((uint32_t)r * (uint32_t)nblk + b) * 4u : kOffNone));
+    float v[kMaxRows * (kMaxK / 128) / kThreads];
+#pragma unroll
+    for (int j = 0; j < kMaxRows * (kMaxK / 128) / kThreads; ++j) {
+      const int i = tid + kThreads * j, b = i / kMaxRows, r = i % kMaxRows;
+      v[j] = u2f(buf_load_u32(rsa, (b < nblk && r < rows) ? ((uint32_t)r * (uint32_t)nblk + b) * 4u : kOffNone));
     }
+#pragma unroll
+    for (int j = 0; j < kMaxRows * (kMaxK / 128) / kThreads; ++j) sm.as[tid + kThreads * j] = v[j];
   }
   __syncthreads();
 
@@ -129,24 +132,21 @@ __device__ void run(const GemmArgs& p, int t, Smem& sm) {
       const int i = i0 + j;
       if (i < nbw) {
         const int b = wave + kWaves * i;
-        const uint8_t* ap = sm.a + c16 * kARow + b * 128 + 32 * g;
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(ap);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(ap + 16);
         f32x4 part = {0.f, 0.f, 0.f, 0.f};
         if constexpr (KIND == kNV) {
           const h16x2 ws = e4m3x2_to_f16<false>(sq[j]);
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
-            const u32x4& aq = m < 2 ? a0 : a1;
-            const h16x8 af = e4m3x8_to_f16(aq[2 * (m & 1)], aq[2 * (m & 1) + 1]);
+            const u32x4& a = aq[j][m >> 1];
+            const h16x8 af = e4m3x8_to_f16(a[2 * (m & 1)], a[2 * (m & 1) + 1]);
             part = mfma16x16x32_f16(af, e2m1x8_scaled_f16(wq[j][m], ws[m >> 1]), part);
           }
         } else {
           const float sv = u2f((sq[j] & 0xFFu) << 23);
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
-            const u32x4& aq = m < 2 ? a0 : a1;
-            const bf16x8 af = e4m3x8_to_bf16(aq[2 * (m & 1)], aq[2 * (m & 1) + 1]);
+            const u32x4& a = aq[j][m >> 1];
+            const bf16x8 af = e4m3x8_to_bf16(a[2 * (m & 1)], a[2 * (m & 1) + 1]);
             part = mfma16x16x32_bf16(af, e2m1x8_pow2_bf16(wq[j][m], sv), part);
           }
         }
@@ -155,10 +155,15 @@ __device__ void run(const GemmArgs& p, int t, Smem& sm) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[v] = fmaf(part[v], as[v], acc[v]);
       }
-      // refill the slot with the block kRing further on
-      const int inext = i + kRing;
-      wq[j] = wload<SWZ>(rw, inext < nbw ? w_off(wave + kWaves * inext) : kOffNone);
-      sq[j] = s_load(inext < nbw ? wave + kWaves * inext : nblk);
+      // refill the slot with the block kRing further on (k > kRing * 512 only)
+      if (i0 + kRing < nbw) {
+        const int inext = i + kRing;
+        const int bn = inext < nbw ? wave + kWaves * inext : nblk;
+        wq[j] = wload<SWZ>(rw, w_off(bn));
+        sq[j] = s_load(bn);
+        aq[j][0] = buf_load_x4(ra, a_off(bn));
+        aq[j][1] = buf_load_x4(ra, a_off(bn) == kOffNone ? kOffNone : a_off(bn) + 16u);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -183,7 +188,7 @@ __device__ void run(const GemmArgs& p, int t, Smem& sm) {
   }
 }
 
-__global__ __launch_bounds__(kThreads, 1) void gemm_skinny_kernel(GemmArgs p) {
+__global__ __launch_bounds__(kThreads, 2) void gemm_skinny_kernel(GemmArgs p) {
   __shared__ Smem sm;
   const int t = blockIdx.x;
   if (p.kind == kNV) run<kNV, false>(p, t, sm);
