@@ -214,7 +214,8 @@ def fp4_expert_gemm(a_codes, a_scales, w_packed, w_scales, scale2: float, kind: 
     _dev(a_codes, torch.uint8, "a_codes", 2)
     _dev(a_scales, torch.float32, "a_scales", 2)
     g, k = a_codes.shape
-    base = kind & ~SWIZZLED if isinstance(kind, int) and kind >= 0 else kind
+    kind = int(kind)
+    base = kind & ~SWIZZLED if kind >= 0 else kind
     if base not in GROUP_SIZE or kind > (MXFP4 | SWIZZLED):
         raise ValueError(f"kind must be 0/1 (NVFP4/MXFP4), or 2/3 for swizzled planes, got {kind}")
     if kind & SWIZZLED:
