@@ -129,7 +129,7 @@ def main():
     # state.
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="config3",
-                    choices=["config3", "config4", "chain4", "w4a4", "config1", "config2"],
+                    choices=["config3", "config4", "chain4", "w4a4", "config1", "config2", "peaks"],
                     help="config3: grouped decode GEMM; config4: grouped prefill GEMM; chain4: the "
                          "whole prefill expert layer from router logits (top-k, packing, gate/up GEMM, "
                          "swiglu+quant, down GEMM, combine); w4a4: the W4A4 variant on one NVFP4 "
@@ -140,6 +140,9 @@ def main():
                          "swiglu_quant_fp8 (unfused)")
     ap.add_argument("--rows", type=int, default=8,
                     help="config1 only: activation rows g (1, 2, 4 or 8)")
+    ap.add_argument("--cached", action="store_true",
+                    help="config1/config2: one copy of the weights (served from the Infinity Cache "
+                         "after the first step) instead of rotating over >= 560 MB of copies")
     ap.add_argument("--layout", default="swizzled", choices=["swizzled", "plain"],
                     help="config3/config4/chain4: expert planes in the swizzled layout (fp4_weight_swizzle, "
                          "run once at load time before the timed region) or as the plain [n, k/2] and "
@@ -171,6 +174,8 @@ def main():
         return run_w4a4(args, torch, fp4, dev)
     if args.workload in ("config1", "config2"):
         return run_single_expert(args, torch, fp4, dev)
+    if args.workload == "peaks":
+        return run_peaks(args, torch, dev)
 
     t0 = time.perf_counter()
     wl = workloads.config3() if args.workload == "config3" else workloads.config4()
@@ -218,7 +223,9 @@ def main():
     step_ms = ev[0][0].elapsed_time(ev[K - 1][2]) / K
     aq_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    gemm_ms_min = float(np.min([e[1].elapsed_time(e[2]) for e in ev]))
+    gemm_all = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    gemm_ms_min = float(np.min(gemm_all))
+    gemm_pct = {f"p{q}": round(float(np.percentile(gemm_all, q)) * 1e3, 2) for q in (10, 50, 90)}
     log(f"timed {K} steps: wall {wall * 1e3 / K:.3f} ms/step, events {step_ms:.3f} ms/step "
         f"(act_quant {aq_ms * 1e3:.1f} us, grouped GEMM {gemm_ms * 1e3:.1f} us avg / "
         f"{gemm_ms_min * 1e3:.1f} us min)")
@@ -254,7 +261,7 @@ def main():
                    "routed_rows": int(wl.R), "k": int(wl.k), "n": int(wl.n),
                    "weight_layout": args.layout,
                    "weight_stream_bytes": int(ws_bytes), "gemm_us": round(gemm_ms * 1e3, 2),
-                   "act_quant_us": round(aq_ms * 1e3, 2)},
+                   "gemm_us_percentiles": gemm_pct, "act_quant_us": round(aq_ms * 1e3, 2)},
         "roofline": roofline,
         "cpu_baseline": None,
     }
@@ -309,7 +316,7 @@ def run_single_expert(args, torch, fp4, dev):
     x = torch.from_numpy(wl.x).to(dev)
     w0, s0 = torch.from_numpy(ex.w).to(dev), torch.from_numpy(ex.s).to(dev)
     wbytes = ex.w.size + ex.s.size + (4 if ex.kind == workloads.NVFP4 else 0)
-    ncopy = max(72, -(-(560 << 20) // wbytes))
+    ncopy = 1 if args.cached else max(72, -(-(560 << 20) // wbytes))
     if args.layout == "swizzled":
         planes = [fp4.fp4_weight_swizzle(w0, s0, ex.kind) for _ in range(ncopy)]
         kind = ex.kind | fp4.SWIZZLED
@@ -342,7 +349,9 @@ def run_single_expert(args, torch, fp4, dev):
     torch.cuda.synchronize()
     step_ms = ev[0][0].elapsed_time(ev[K - 1][2]) / K
     aq_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    gemm_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    gemm_all = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    gemm_ms = float(np.mean(gemm_all))
+    gemm_pct = {f"p{q}": round(float(np.percentile(gemm_all, q)) * 1e3, 2) for q in (10, 50, 90)}
     alg = wbytes + g * k + g * (k // 128) * 4 + g * n * 4
     achieved = alg / (gemm_ms * 1e-3) / 1e9
     log(f"{K} steps: {step_ms * 1e3:.2f} us/step (act_quant {aq_ms * 1e3:.2f} us, GEMM {gemm_ms * 1e3:.2f} us); "
@@ -358,12 +367,57 @@ def run_single_expert(args, torch, fp4, dev):
         "steps": K, "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8xfp4->f32", "data": "synthetic",
         "config": {"workload": wl.name, "rows": int(g), "k": int(k), "n": int(n), "weight_layout": args.layout,
-                   "weight_copies_rotated": int(ncopy), "weight_stream_bytes": int(wbytes),
-                   "gemm_us": round(gemm_ms * 1e3, 2), "act_quant_us": round(aq_ms * 1e3, 2)},
+                   "weight_copies_rotated": int(ncopy), "cached": bool(args.cached),
+                   "weight_stream_bytes": int(wbytes), "gemm_us": round(gemm_ms * 1e3, 2),
+                   "gemm_us_percentiles": gemm_pct, "act_quant_us": round(aq_ms * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
         "cpu_baseline": {"value": wbytes / t_cpu / 1e12, "unit": "TB/s", "cores": 1, "kind": "oracle",
                          "sample": f"oracle act-quant + f64 expert GEMM of the whole step, one thread, {t_cpu:.2f} s"},
+    }
+    print(json.dumps(result), flush=True)
+
+
+def run_peaks(args, torch, dev):
+    """The roofline denominators re-measured on this GPU with library-independent torch kernels: a
+    device-to-device copy of 4 GiB (HBM read + write), a read-only reduction of 4 GiB, and a dense
+    bf16 matrix product 8192^3 (hipBLASLt).  Not part of the method: context for the fractions of
+    the published figures (8 TB/s, 2.5 PFLOP/s) that the other workloads report."""
+    nbytes = 4 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).uniform_()
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
+
+    def timed(fn, reps):
+        for _ in range(max(3, reps // 4)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    t_copy = timed(lambda: dst.copy_(src), 20)
+    t_read = timed(lambda: src.sum(), 20)
+    t_mm = timed(lambda: torch.mm(a, b), 50)
+    copy_gbs = 2 * nbytes / t_copy / 1e9
+    read_gbs = nbytes / t_read / 1e9
+    mm_tf = 2 * 8192 ** 3 / t_mm / 1e12
+    log(f"copy {copy_gbs:.0f} GB/s (read+write), read {read_gbs:.0f} GB/s, bf16 mm {mm_tf:.0f} TFLOP/s")
+    result = {
+        "metric": "roofline denominators re-measured (copy GB/s, read GB/s, bf16 GEMM TFLOP/s)",
+        "value": round(read_gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": 20, "warmup": 5,
+        "ms_per_step": round(t_read * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32 / bf16", "data": "synthetic",
+        "config": {"workload": "peaks: 4 GiB f32 copy and sum, bf16 mm 8192^3",
+                   "copy_gbs": round(copy_gbs, 1), "read_gbs": round(read_gbs, 1),
+                   "bf16_mm_tflops": round(mm_tf, 1), "published_hbm_gbs": HBM_PEAK_GBS,
+                   "published_bf16_tflops": MFMA_PEAK_TFLOPS["f16"]},
+        "roofline": None, "cpu_baseline": None,
     }
     print(json.dumps(result), flush=True)
 
