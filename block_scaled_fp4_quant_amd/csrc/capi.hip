@@ -58,10 +58,11 @@ std::atomic<int> g_schedule{FP4MOE_SCHEDULE_AUTO};
 
 hipError_t launch_gemm(const fp4moe::GemmArgs& a, int64_t rows, int64_t experts, hipStream_t stream) {
   int s = g_schedule.load(std::memory_order_relaxed);
-  // One expert with few rows: the split-k kernel (the row-streaming kernel would launch only
-  // ceil(n/256) workgroups).
-  if ((s == FP4MOE_SCHEDULE_AUTO || s == FP4MOE_SCHEDULE_SPLITK) && !a.offsets &&
-      fp4moe::gemm_skinny_fits((int32_t)rows, a.n, a.k))
+  // Very few rows: the split-k kernel (the row-streaming kernel would launch only ceil(n/256)
+  // workgroups per active expert).
+  if ((s == FP4MOE_SCHEDULE_AUTO || s == FP4MOE_SCHEDULE_SPLITK) &&
+      (a.offsets ? fp4moe::gemm_skinny_grouped_fits(rows, a.num_experts, a.n, a.k, s == FP4MOE_SCHEDULE_SPLITK)
+                 : fp4moe::gemm_skinny_fits((int32_t)rows, a.n, a.k)))
     return fp4moe::launch_gemm_skinny(a, stream);
   if (s == FP4MOE_SCHEDULE_AUTO || s == FP4MOE_SCHEDULE_SPLITK)
     s = (rows <= 32 * experts) ? FP4MOE_SCHEDULE_ROWSTREAM : FP4MOE_SCHEDULE_TILED;

@@ -1,5 +1,6 @@
-// gemm_skinny.hip -- FP8-activation x block-scaled FP4 GEMM of ONE expert with few rows (g <= 16),
-// split over k so that a single decode-shaped launch fills the chip.
+// gemm_skinny.hip -- FP8-activation x block-scaled FP4 GEMM for very few rows: one expert with
+// g <= 16 rows, or a grouped launch with at most 128 packed rows (a decode step of a few tokens),
+// split over k so that such a launch fills the chip.
 //
 // What is computed is the same definition as the other two GEMM kernels (memra-engine 0.98.0
 // dsv4_native_gemm_gate.rs page, `f64_ref` / `ExpertRaw`):
@@ -22,6 +23,8 @@
 // tile is scaled by as[r, b] with one f32 FMA per output.  The 4 wavefronts' f32 tiles are then
 // summed through LDS in wavefront order 0, 1, 2, 3 (a fixed order: the result does not depend on g
 // or on timing), and scale2 multiplies the sum.
+#include <algorithm>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -33,6 +36,14 @@ constexpr int kWaves = 8;
 constexpr int kRing = 7;                    // blocks in flight per wavefront (all of them for k <= 8192)
 constexpr int kMaxRows = 16;
 constexpr int kMaxK = 8192;
+// Grouped launches take this kernel automatically when they hold at most kGroupedAutoRows packed
+// rows (two tokens at top-8: measured over 256 experts of k = 7168, n = 2048, one token takes 31 us
+// here against 60 us in the row-streaming kernel, two tokens 55 against 63, four tokens 100 against
+// 66), and up to kGroupedMaxRows when the schedule forces it.
+constexpr int kGroupedMaxRows = 128;
+constexpr int kGroupedAutoRows = 16;
+constexpr int kMaxExperts = 1024;
+constexpr int kGridCap = 256;                // persistent grid of the grouped form (one per compute unit)
 constexpr int kNV = 0;
 constexpr int kMX = 1;
 constexpr int kSwizzled = 2;
@@ -40,6 +51,9 @@ constexpr int kSwizzled = 2;
 struct Smem {
   float as[(kMaxK / 128) * kMaxRows];        // activation scales [block][row]
   f32x4 red[kWaves][64];                     // per-wavefront result tiles
+  int active[kMaxExperts];                   // grouped: the experts with rows, in id order
+  int wave_count[kWaves];
+  int n_active;
 };
 
 template <bool SWZ>
@@ -48,21 +62,36 @@ __device__ __forceinline__ u32x4 wload(rsrc_t r, uint32_t off) {
   else return buf_load_x4(r, off);
 }
 
+// One expert's planes and scale2.
+struct View {
+  const uint8_t* w;
+  const uint8_t* s;
+  float scale2;
+};
+
+// Activation row of packed row `prow`: row_ids[prow] (or prow), -2 when the entry is out of range.
+__device__ __forceinline__ int act_row(const GemmArgs& p, int prow) {
+  if (!p.row_ids) return prow;
+  const int r = p.row_ids[prow];
+  return (r >= 0 && r < p.a_rows) ? r : -2;
+}
+
+// Packed rows [m0, m0 + mrows) (mrows <= 16) of expert `ex`, columns 16t .. 16t+15.
 template <int KIND, bool SWZ>
-__device__ void run(const GemmArgs& p, int t, Smem& sm) {
+__device__ void run(const GemmArgs& p, const View& ex, int t, int m0, int mrows, Smem& sm) {
   const int tid = threadIdx.x, lane = tid & 63, c16 = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int k = p.k, nblk = k >> 7, nq = (nblk + 3) >> 2, rows = p.total_rows;
+  const int k = p.k, nblk = k >> 7, nq = (nblk + 3) >> 2;
   const int col = 16 * t + c16;
   const uint32_t n16 = (uint32_t)(p.n + 15) >> 4;
 
   rsrc_t rw, rs;
   if constexpr (SWZ) {
-    rw = make_rsrc(p.w, n16 * 16u * (uint32_t)(k / 2));
-    rs = make_rsrc(p.s, n16 * (uint32_t)nq * (KIND == kNV ? 512u : 256u));
+    rw = make_rsrc(ex.w, n16 * 16u * (uint32_t)(k / 2));
+    rs = make_rsrc(ex.s, n16 * (uint32_t)nq * (KIND == kNV ? 512u : 256u));
   } else {
-    rw = make_rsrc(p.w, (uint32_t)p.n * (uint32_t)(k / 2));
-    rs = make_rsrc(p.s, (uint32_t)p.n * (uint32_t)(k / (KIND == kNV ? 16 : 32)));
+    rw = make_rsrc(ex.w, (uint32_t)p.n * (uint32_t)(k / 2));
+    rs = make_rsrc(ex.s, (uint32_t)p.n * (uint32_t)(k / (KIND == kNV ? 16 : 32)));
   }
   // Block-0 offsets of this lane's weight piece and scale bytes (kOffNone past n).
   const uint32_t piece = (uint32_t)(16 * g + c16);
@@ -91,9 +120,11 @@ __device__ void run(const GemmArgs& p, int t, Smem& sm) {
     else return buf_load_u8(rs, o);
   };
 
-  // Activation operand of block b: row c16, bytes 32g .. +32 of the block (rows >= g read zero).
-  const rsrc_t ra = make_rsrc(p.a_codes, (uint32_t)rows * (uint32_t)k);
-  const uint32_t a0 = c16 < rows ? (uint32_t)c16 * (uint32_t)k + 32u * g : kOffNone;
+  // Activation operand of block b: packed row m0 + c16, bytes 32g .. +32 of the block (rows past
+  // mrows and rows whose row_ids entry is invalid read zero).
+  const rsrc_t ra = make_rsrc(p.a_codes, (uint32_t)p.a_rows * (uint32_t)k);
+  const int arow = c16 < mrows ? act_row(p, m0 + c16) : -1;
+  const uint32_t a0 = arow >= 0 ? (uint32_t)arow * (uint32_t)k + 32u * g : kOffNone;
   auto a_off = [&](int b) -> uint32_t { return (b < nblk && a0 != kOffNone) ? a0 + (uint32_t)b * 128u : kOffNone; };
 
   // Ring: the wavefront's blocks b = wave + 4 i, weights, scale bytes and activation operand of
@@ -113,12 +144,13 @@ __device__ void run(const GemmArgs& p, int t, Smem& sm) {
 
   // Activation scales [block][row] in LDS (at most 4 per thread, loaded together).
   {
-    const rsrc_t rsa = make_rsrc(p.a_scales, (uint32_t)rows * (uint32_t)nblk * 4u);
+    const rsrc_t rsa = make_rsrc(p.a_scales, (uint32_t)p.a_rows * (uint32_t)nblk * 4u);
     float v[kMaxRows * (kMaxK / 128) / kThreads];
 #pragma unroll
     for (int j = 0; j < kMaxRows * (kMaxK / 128) / kThreads; ++j) {
       const int i = tid + kThreads * j, b = i / kMaxRows, r = i % kMaxRows;
-      v[j] = u2f(buf_load_u32(rsa, (b < nblk && r < rows) ? ((uint32_t)r * (uint32_t)nblk + b) * 4u : kOffNone));
+      const int ar = (b < nblk && r < mrows) ? act_row(p, m0 + r) : -1;
+      v[j] = u2f(buf_load_u32(rsa, ar >= 0 ? ((uint32_t)ar * (uint32_t)nblk + b) * 4u : kOffNone));
     }
 #pragma unroll
     for (int j = 0; j < kMaxRows * (kMaxK / 128) / kThreads; ++j) sm.as[tid + kThreads * j] = v[j];
@@ -179,22 +211,97 @@ __device__ void run(const GemmArgs& p, int t, Smem& sm) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) sum[v] += o[v];
     }
-    const float post = KIND == kNV ? p.scale2 : 1.0f;
+    const float post = KIND == kNV ? ex.scale2 : 1.0f;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int r = 4 * g + v;
-      if (r < rows && col < p.n) p.out[(size_t)r * p.n + col] = sum[v] * post;
+      if (r < mrows && col < p.n) {
+        const bool bad = act_row(p, m0 + r) < 0;
+        p.out[(size_t)(m0 + r) * p.n + col] = bad ? __builtin_nanf("") : sum[v] * post;
+      }
     }
   }
 }
 
-__global__ __launch_bounds__(kThreads, 2) void gemm_skinny_kernel(GemmArgs p) {
+// Packed rows [lo, hi) of expert `ex` for tile t, in passes of 16 rows (every pass streams the
+// tile's weights again; the host sends only launches with few rows per expert here).
+__device__ void run_rows(const GemmArgs& p, const View& ex, int kind, int t, int lo, int hi, Smem& sm) {
+  for (int m0 = lo; m0 < hi; m0 += kMaxRows) {
+    const int mrows = min(kMaxRows, hi - m0);
+    if (kind == kNV) {
+      run<kNV, false>(p, ex, t, m0, mrows, sm);
+    } else if (kind == kMX) {
+      run<kMX, false>(p, ex, t, m0, mrows, sm);
+    } else if (kind == (kNV | kSwizzled)) {
+      run<kNV, true>(p, ex, t, m0, mrows, sm);
+    } else if (kind == (kMX | kSwizzled)) {
+      run<kMX, true>(p, ex, t, m0, mrows, sm);
+    } else {
+      // a weight format the kernel does not take: NaN rows
+      for (int i = threadIdx.x; i < mrows * 16; i += kThreads) {
+        const int col = 16 * t + (i & 15);
+        if (col < p.n) p.out[(size_t)(m0 + (i >> 4)) * p.n + col] = __builtin_nanf("");
+      }
+    }
+    __syncthreads();                         // the next pass reuses the LDS
+  }
+}
+
+// Rows [lo, hi) of expert e after clamping its offsets to [0, total_rows].
+__device__ __forceinline__ int2 expert_rows(const GemmArgs& p, int e) {
+  const int lo = min(max(p.offsets[e], 0), p.total_rows);
+  const int hi = min(max(p.offsets[e + 1], lo), p.total_rows);
+  return make_int2(lo, hi);
+}
+
+// Single expert: workgroup t owns tile t.  Grouped (persistent): every workgroup lists the experts
+// that have rows (a block-wide scan over the offsets into LDS), then takes the (active expert, tile)
+// items blockIdx.x, blockIdx.x + gridDim.x, ... -- no workgroup is spent on an empty expert.
+__global__ __launch_bounds__(kThreads, 2) void gemm_skinny_kernel(GemmArgs p, int ntiles) {
   __shared__ Smem sm;
-  const int t = blockIdx.x;
-  if (p.kind == kNV) run<kNV, false>(p, t, sm);
-  else if (p.kind == kMX) run<kMX, false>(p, t, sm);
-  else if (p.kind == (kNV | kSwizzled)) run<kNV, true>(p, t, sm);
-  else if (p.kind == (kMX | kSwizzled)) run<kMX, true>(p, t, sm);
+  if (!p.offsets) {
+    run_rows(p, View{p.w, p.s, p.scale2}, p.kind, blockIdx.x, 0, p.total_rows, sm);
+    return;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = p.num_experts;
+  constexpr int kPer = kMaxExperts / kThreads;                 // experts per thread
+  int flags[kPer], cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = tid * kPer + j;
+    int2 r = make_int2(0, 0);
+    if (e < E) r = expert_rows(p, e);
+    flags[j] = r.y > r.x;
+    cnt += flags[j];
+  }
+  int incl = cnt;                                              // inclusive scan inside the wavefront
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  if (lane == 63) sm.wave_count[wave] = incl;
+  __syncthreads();
+  int base = 0, total = 0;
+  for (int w = 0; w < kWaves; ++w) {
+    const int c = sm.wave_count[w];
+    if (w < wave) base += c;
+    total += c;
+  }
+  int pos = base + incl - cnt;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (flags[j]) sm.active[pos++] = tid * kPer + j;
+  __syncthreads();
+  const int items = total * ntiles;
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int e = sm.active[it / ntiles], t = it % ntiles;
+    const int2 r = expert_rows(p, e);
+    const View ex{reinterpret_cast<const uint8_t*>(p.w_ptrs[e]), reinterpret_cast<const uint8_t*>(p.s_ptrs[e]),
+                  p.scale2s[e]};
+    run_rows(p, ex, p.kinds[e], t, r.x, r.y, sm);
+  }
 }
 
 }  // namespace
@@ -203,9 +310,16 @@ bool gemm_skinny_fits(int32_t g, int32_t n, int32_t k) {
   return g >= 1 && g <= kMaxRows && k >= 128 && k <= kMaxK && n >= 1;
 }
 
+bool gemm_skinny_grouped_fits(int64_t total_rows, int32_t num_experts, int32_t n, int32_t k, bool forced) {
+  const int64_t items = (int64_t)num_experts * ((n + 15) / 16);
+  return total_rows >= 1 && total_rows <= (forced ? kGroupedMaxRows : kGroupedAutoRows) && k >= 128 &&
+         k <= kMaxK && n >= 1 && num_experts <= kMaxExperts && items < ((int64_t)1 << 31);
+}
+
 hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
   const int tiles = (a.n + 15) / 16;
-  hipLaunchKernelGGL(gemm_skinny_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, stream, a);
+  const int64_t grid = a.offsets ? std::min<int64_t>((int64_t)a.num_experts * tiles, kGridCap) : tiles;
+  hipLaunchKernelGGL(gemm_skinny_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a, tiles);
   return hipGetLastError();
 }
 

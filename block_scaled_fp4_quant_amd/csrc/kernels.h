@@ -99,9 +99,12 @@ hipError_t launch_weight_swizzle(const uint8_t* w, const uint8_t* s, int32_t kin
 // pass of 32 rows.
 hipError_t launch_gemm_decode(const GemmArgs& a, hipStream_t stream);
 
-// Split-k kernel for ONE expert with few rows (single-expert calls, offsets == nullptr): 16-column
-// workgroups whose 4 wavefronts split k; requires gemm_skinny_fits(g, n, k) (g <= 16, k <= 8192).
+// Split-k kernel for very few rows: 16-column workgroups whose 8 wavefronts split k.  Single expert
+// (offsets == nullptr): requires gemm_skinny_fits(g, n, k) (g <= 16, k <= 8192).  Grouped: requires
+// gemm_skinny_grouped_fits (at most 16 packed rows, 128 when the schedule is forced; k <= 8192;
+// at most 1024 experts).
 bool gemm_skinny_fits(int32_t g, int32_t n, int32_t k);
+bool gemm_skinny_grouped_fits(int64_t total_rows, int32_t num_experts, int32_t n, int32_t k, bool forced);
 hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);
 
 // Tiled matrix-core kernel for many rows per expert (prefill): 128 x 256 output tiles.

@@ -318,3 +318,92 @@ def test_splitk_limits_fall_back(orc):
         finally:
             fp4.set_gemm_schedule(fp4.SCHEDULE_AUTO)
         check_bound(got, ref, absp, k, f"fallback g={g} k={k}")
+
+
+@pytest.mark.parametrize("sched", [fp4.SCHEDULE_AUTO, fp4.SCHEDULE_SPLITK], ids=["auto", "splitk"])
+@pytest.mark.parametrize("T", [1, 4, 16])
+@pytest.mark.parametrize("swz", [False, True])
+def test_grouped_few_tokens_splitk(orc, config3_dev, T, swz, sched):
+    """A decode step of a few tokens over the 256 NVFP4 experts of the decode workload (k = 7168,
+    n = 2048, top-8: 8 to 128 packed rows), under the automatic schedule (split-k for 8 rows,
+    row-streaming above 16) and with split-k forced.  Every output within the bound, run-to-run
+    identical."""
+    gd = config3_dev
+    fp4.set_gemm_schedule(sched)
+    try:
+        _few_tokens_case(orc, gd, T, swz)
+    finally:
+        fp4.set_gemm_schedule(fp4.SCHEDULE_AUTO)
+
+
+def _few_tokens_case(orc, gd, T, swz):
+    wl = gd.wl
+    row_ids, offsets = workloads.route_topk(wl.logits[:T], 8)
+    x = wl.x[:T]
+    codes, scales = fp4.act_quant_fp8(dev(x))
+    rid, offs = dev(row_ids), dev(offsets)
+    if swz:
+        w_ptrs, s_ptrs, kinds, keep = _swizzled_planes(gd)
+    else:
+        w_ptrs, s_ptrs, kinds, keep = gd.w_ptrs, gd.s_ptrs, gd.kinds, None
+    o1 = fp4.fp4_grouped_gemm(codes, scales, rid, offs, w_ptrs, s_ptrs, kinds, gd.scale2, wl.n)
+    o2 = fp4.fp4_grouped_gemm(codes, scales, rid, offs, w_ptrs, s_ptrs, kinds, gd.scale2, wl.n)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    rc, rs = orc.act_quant(x)
+    ref, absp = orc.grouped_gemm(rc[row_ids], rs[row_ids], offsets, [wl.w_of(e) for e in range(wl.E)],
+                                 [wl.s_of(e) for e in range(wl.E)], wl.kinds, wl.scale2, wl.n)
+    check_bound(o1.cpu().numpy(), ref, absp, wl.k, f"{T} tokens swz={swz}")
+    del keep
+
+
+_SWZ_CACHE = {}
+
+
+def _swizzled_planes(gd):
+    """Swizzled copies of every expert of a GroupedDevice (kept for the module)."""
+    key = id(gd)
+    if key not in _SWZ_CACHE:
+        wl = gd.wl
+        w_ptrs, s_ptrs, kinds = gd.w_ptrs.clone(), gd.s_ptrs.clone(), gd.kinds.clone()
+        keep = []
+        for e in range(wl.E):
+            kd = int(wl.kinds[e])
+            w_swz, s_swz = fp4.fp4_weight_swizzle(gd.w_bank[int(wl.w_off[e]):int(wl.w_off[e]) + wl.n * wl.k // 2]
+                                                  .view(wl.n, wl.k // 2),
+                                                  gd.s_bank[int(wl.s_off[e]):int(wl.s_off[e]) + wl.n * wl.k // 16]
+                                                  .view(wl.n, wl.k // 16) if kd == NV else
+                                                  gd.s_bank[int(wl.s_off[e]):int(wl.s_off[e]) + wl.n * wl.k // 32]
+                                                  .view(wl.n, wl.k // 32), kd)
+            keep += [w_swz, s_swz]
+            w_ptrs[e], s_ptrs[e], kinds[e] = w_swz.data_ptr(), s_swz.data_ptr(), kd | fp4.SWIZZLED
+        _SWZ_CACHE[key] = (w_ptrs, s_ptrs, kinds, keep)
+    return _SWZ_CACHE[key]
+
+
+@pytest.mark.parametrize("schedule_id", [fp4.SCHEDULE_AUTO, fp4.SCHEDULE_ROWSTREAM])
+def test_grouped_multipass_few_experts(orc, schedule_id):
+    """40 tokens over 2 experts at top-1 (about 20 rows per expert, over the split-k kernel's
+    16-row pass) and ragged n, k: within the bound under the automatic (split-k) and the
+    row-streaming schedule; invalid row ids and kinds give NaN rows."""
+    wl = workloads.grouped_random(24, 40, 2, 1, 200, 640, kinds=[NV, MX])
+    gd = GroupedDevice(wl)
+    fp4.set_gemm_schedule(schedule_id)
+    try:
+        codes, scales, out = gd.step()
+        bad_ids = gd.row_ids.clone()
+        bad_ids[3] = -5
+        bad_kinds = gd.kinds.clone()
+        bad_kinds[1] = 9
+        bad = fp4.fp4_grouped_gemm(codes, scales, bad_ids, gd.offsets, gd.w_ptrs, gd.s_ptrs, bad_kinds,
+                                   gd.scale2, wl.n)
+        torch.cuda.synchronize()
+    finally:
+        fp4.set_gemm_schedule(fp4.SCHEDULE_AUTO)
+    grouped_check(gd, orc, out)
+    lo1 = int(wl.offsets[1])
+    for r in range(wl.R):
+        if r == 3 or r >= lo1:
+            assert bool(torch.isnan(bad[r]).all()), r
+        else:
+            assert torch.equal(bad[r], out[r]), r
