@@ -12,6 +12,7 @@ Prints ONE JSON line on stdout; human-readable detail goes to stderr.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -138,6 +139,9 @@ def main():
                     help="chain4 only: the gate/up GEMM with the activation and its quantization in "
                          "its epilogue (fused), or the GEMM writing f32 gate/up values followed by "
                          "swiglu_quant_fp8 (unfused)")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="config3 only: a decode step of the first T tokens (top-8 over the same 256 "
+                         "experts; default all 512)")
     ap.add_argument("--rows", type=int, default=8,
                     help="config1 only: activation rows g (1, 2, 4 or 8)")
     ap.add_argument("--cached", action="store_true",
@@ -179,6 +183,12 @@ def main():
 
     t0 = time.perf_counter()
     wl = workloads.config3() if args.workload == "config3" else workloads.config4()
+    if args.workload == "config3" and 0 < args.tokens < wl.x.shape[0]:
+        T = args.tokens
+        rid, off = workloads.route_topk(wl.logits[:T], 8)
+        wl = dataclasses.replace(wl, x=np.ascontiguousarray(wl.x[:T]), row_ids=rid, offsets=off,
+                                 logits=wl.logits[:T],
+                                 name=f"config3 experts, decode step of {T} tokens: E=256, top-8, k=7168, n=2048")
     log(f"workload: {wl.name}  (generated in {time.perf_counter() - t0:.1f} s)")
 
     x = torch.from_numpy(wl.x).to(dev)
@@ -235,7 +245,8 @@ def main():
     ws_bytes = alg["weights"]
     gemm_s = gemm_ms * 1e-3
     achieved_gbs = alg["total"] / gemm_s / 1e9
-    traffic = recorded_traffic(args.workload, args.layout)
+    # the recorded counters belong to the whole 512-token step
+    traffic = None if args.tokens else recorded_traffic(args.workload, args.layout)
     if args.workload == "config3":
         value = ws_bytes / (step_ms * 1e-3) / 1e12
         unit = "TB/s"
