@@ -11,8 +11,8 @@
 // wavefronts: wavefront w takes the 128-wide blocks b = w, w+4, w+8, ..., so the 4 wavefronts of a
 // workgroup read 4 consecutive 1 KB weight runs at a time with swizzled planes.
 //
-// Data movement: every load of a wavefront (up to kRing blocks, all of them for k <= 8192) is issued
-// before anything waits: per block the lane's 16 weight bytes, its scale bytes and its 32 bytes of
+// Data movement: a wavefront keeps kRing blocks of loads in flight, refilling a slot as soon as it
+// has computed on it: per block the lane's 16 weight bytes, its scale bytes and its 32 bytes of
 // the activation operand (which hit L2 after the first workgroup).  Only the activation scales go
 // through LDS, loaded together at the start.
 //
@@ -33,7 +33,7 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWaves = 8;
-constexpr int kRing = 7;                    // blocks in flight per wavefront (all of them for k <= 8192)
+constexpr int kRing = 4;                    // blocks in flight per wavefront (refilled as they are consumed)
 constexpr int kMaxRows = 16;
 constexpr int kMaxK = 8192;
 // Grouped launches take this kernel automatically when they hold at most kGroupedAutoRows packed
@@ -43,7 +43,7 @@ constexpr int kMaxK = 8192;
 constexpr int kGroupedMaxRows = 128;
 constexpr int kGroupedAutoRows = 16;
 constexpr int kMaxExperts = 1024;
-constexpr int kGridCap = 256;                // persistent grid of the grouped form (one per compute unit)
+constexpr int kGridCap = 512;                // persistent grid of the grouped form (two per compute unit)
 constexpr int kNV = 0;
 constexpr int kMX = 1;
 constexpr int kSwizzled = 2;
@@ -187,7 +187,7 @@ __device__ void run(const GemmArgs& p, const View& ex, int t, int m0, int mrows,
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[v] = fmaf(part[v], as[v], acc[v]);
       }
-      // refill the slot with the block kRing further on (k > kRing * 512 only)
+      // refill the slot with the block kRing further on (when the wavefront has more than kRing blocks)
       if (i0 + kRing < nbw) {
         const int inext = i + kRing;
         const int bn = inext < nbw ? wave + kWaves * inext : nblk;
@@ -257,7 +257,10 @@ __device__ __forceinline__ int2 expert_rows(const GemmArgs& p, int e) {
 // Single expert: workgroup t owns tile t.  Grouped (persistent): every workgroup lists the experts
 // that have rows (a block-wide scan over the offsets into LDS), then takes the (active expert, tile)
 // items blockIdx.x, blockIdx.x + gridDim.x, ... -- no workgroup is spent on an empty expert.
-__global__ __launch_bounds__(kThreads, 2) void gemm_skinny_kernel(GemmArgs p, int ntiles) {
+// At most 128 registers (4 wavefronts per SIMD): two workgroups share a compute unit, so one computes
+// while the other waits for its loads (one token over 256 experts: 26 us, against 30 us with every
+// block of k in flight and one workgroup per compute unit).
+__global__ __launch_bounds__(kThreads, 4) void gemm_skinny_kernel(GemmArgs p, int ntiles) {
   __shared__ Smem sm;
   if (!p.offsets) {
     run_rows(p, View{p.w, p.s, p.scale2}, p.kind, blockIdx.x, 0, p.total_rows, sm);
