@@ -7,9 +7,9 @@
 //   out[r, c] = sum_j ( sum_{k in group j} E4M3(A[r,k]) * E2M1(W[c,k]) ) * ws[c,j] * as[r, k/128]
 // accumulated in f32.  A single expert of the decode shapes (n = 2048 or 7168 columns) gives the
 // row-streaming kernel only n/256 = 8..28 workgroups, far too few to stream 8 MB of weights; this
-// kernel gives each workgroup 16 columns (n/16 = 128..448 workgroups) and splits k over its 4
-// wavefronts: wavefront w takes the 128-wide blocks b = w, w+4, w+8, ..., so the 4 wavefronts of a
-// workgroup read 4 consecutive 1 KB weight runs at a time with swizzled planes.
+// kernel gives each workgroup 16 columns (n/16 = 128..448 workgroups) and splits k over its 8
+// wavefronts: wavefront w takes the 128-wide blocks b = w, w+8, w+16, ..., so the 8 wavefronts of a
+// workgroup read 8 consecutive 1 KB weight runs at a time with swizzled planes.
 //
 // Data movement: a wavefront keeps kRing blocks of loads in flight, refilling a slot as soon as it
 // has computed on it: per block the lane's 16 weight bytes, its scale bytes and its 32 bytes of
@@ -20,9 +20,9 @@
 // g = lane/16 holds k = 32g .. +32 of the block), as in the row-streaming kernel: NVFP4 on exact f16
 // operands (nibble -> f16 times the E4M3 scale in f16), MXFP4 on exact bf16 operands (the E8M0 scale
 // applied by the conversion), four 16x16x32 MFMAs cover one activation-scale group, whose partial
-// tile is scaled by as[r, b] with one f32 FMA per output.  The 4 wavefronts' f32 tiles are then
-// summed through LDS in wavefront order 0, 1, 2, 3 (a fixed order: the result does not depend on g
-// or on timing), and scale2 multiplies the sum.
+// tile is scaled by as[r, b] with one f32 FMA per output.  The 8 wavefronts' f32 tiles are then
+// summed through LDS in wavefront order 0, 1, ..., 7 (a fixed order: the result does not depend on
+// g or on timing), and scale2 multiplies the sum.
 #include <algorithm>
 
 #include "device_common.h"
@@ -37,8 +37,8 @@ constexpr int kRing = 4;                    // blocks in flight per wavefront (r
 constexpr int kMaxRows = 16;
 constexpr int kMaxK = 8192;
 // Grouped launches take this kernel automatically when they hold at most kGroupedAutoRows packed
-// rows (two tokens at top-8: measured over 256 experts of k = 7168, n = 2048, one token takes 31 us
-// here against 60 us in the row-streaming kernel, two tokens 55 against 63, four tokens 100 against
+// rows (two tokens at top-8: measured over 256 experts of k = 7168, n = 2048, one token takes 26 us
+// here against 60 us in the row-streaming kernel, two tokens 46 against 63, four tokens 82 against
 // 66), and up to kGroupedMaxRows when the schedule forces it.
 constexpr int kGroupedMaxRows = 128;
 constexpr int kGroupedAutoRows = 16;
@@ -53,7 +53,6 @@ struct Smem {
   f32x4 red[kWaves][64];                     // per-wavefront result tiles
   int active[kMaxExperts];                   // grouped: the experts with rows, in id order
   int wave_count[kWaves];
-  int n_active;
 };
 
 template <bool SWZ>
