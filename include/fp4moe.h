@@ -134,6 +134,9 @@ FP4MOE_API int fp4_grouped_gemm(const uint8_t* a_codes, const float* a_scales, i
  *         n, k)], written.  Must not overlap the inputs.  Pass kind | FP4MOE_SWIZZLED to the GEMMs.
  * Errors: EINVAL if n <= 0, k <= 0, k % 128 != 0, kind not 0/1, a pointer is NULL, w_packed, w_swz
  * or s_swz is not 16-byte aligned, or ceil(n/16)*16*k/2 is 2^31 or more.
+ * fp4_swizzled_weight_bytes / fp4_swizzled_scale_bytes: the plane sizes in bytes (host-only, no
+ * device work): ceil(n/16)*16*k/2 and ceil(n/16)*nq*512 (NVFP4) or *256 (MXFP4); 0 when n <= 0,
+ * k is not a positive multiple of 128, or kind is not 0/1.
  */
 FP4MOE_API size_t fp4_swizzled_weight_bytes(int32_t n, int32_t k);
 FP4MOE_API size_t fp4_swizzled_scale_bytes(int32_t kind, int32_t n, int32_t k);
