@@ -6,9 +6,9 @@
 // weights.  Grouped form: rows packed per expert with a CSR offsets array (kernel_check.rs page,
 // f16g grouped GEMM section).
 //
-// Work decomposition.  A workgroup of 4 wavefronts owns 256 output columns of one expert; each
-// wavefront owns 64 of them (4 MFMA column tiles) over the whole of k, for every row of a pass of up
-// to 32 activation rows.  With decode-sized row counts a pass covers all rows, so every weight byte
+// Work decomposition.  A workgroup of 4 wavefronts owns 256 output columns of one expert (128 for
+// launches with few rows in total: see launch_gemm_decode); each wavefront owns 64 (32) of them, 4 (2)
+// MFMA column tiles, over the whole of k, for every row of a pass of up to 32 activation rows.  With decode-sized row counts a pass covers all rows, so every weight byte
 // is read from HBM exactly once.
 //
 // Data movement (the path is HBM-bound; what costs is the number and geometry of load requests):
@@ -48,9 +48,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kCT = 4;                       // MFMA column tiles per wavefront
-constexpr int kWaveCols = 16 * kCT;          // 64
-constexpr int kTileN = kWaves * kWaveCols;   // 256 columns per workgroup
+// CT = MFMA column tiles per wavefront (a template parameter): 4 (64 columns per wavefront, 256 per
+// workgroup) or 2 (128 per workgroup, twice the workgroups for launches with few rows).
+template <int CT> constexpr int kTileNT = kWaves * 16 * CT;
 constexpr int kRows = 32;                    // rows per pass (2 MFMA row tiles)
 constexpr int kChunkK = 512;                 // k per LDS stage
 constexpr int kBlk = kChunkK / 128;          // 4 blocks of 128 per stage = register ring depth
@@ -60,10 +60,11 @@ constexpr int kNV = 0;
 constexpr int kMX = 1;
 constexpr int kSwizzled = 2;                 // kind flag: planes in the swizzled layout
 
+template <int CT>
 struct Stage {
   uint8_t a[kRows * kARow];                  // activation codes, [row][512 (+16 pad)]
   float as[kBlk * kRows];                    // activation scales, [block][row]
-  uint8_t s[kTileN * kSCol];                 // weight scales, [column][chunk bytes (+pad)]
+  uint8_t s[kTileNT<CT> * kSCol];            // weight scales, [column][chunk bytes (+pad)]
 };
 
 struct ExpertView {
@@ -90,20 +91,20 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Per-thread staging registers of one chunk, and their global byte offsets for chunk 0.  With
 // swizzled weight planes (SWZ) the weight scales are not staged: each lane loads its own.
-template <int KIND>
-constexpr int kStagedScales = KIND == kNV ? 2 : 1;
+template <int KIND, int CT>
+constexpr int kStagedScales = KIND == kNV ? CT / 2 : 1;
 
-template <int KIND>
+template <int KIND, int CT>
 struct StageRegs {
   u32x4 a[4];                                 // activation codes: 4 x 16 bytes
-  u32x4 s[kStagedScales<KIND>];               // weight scales: 16 bytes per column half (NV) / column (MX)
+  u32x4 s[kStagedScales<KIND, CT>];           // weight scales: 16 bytes per column half (NV) / column (MX)
   float as;                                   // one activation scale (threads < 128)
 };
 
-template <int KIND>
+template <int KIND, int CT>
 struct StageOffsets {
   uint32_t a[4];                              // row * k + 16 * part, or kOffNone
-  uint32_t s[kStagedScales<KIND>];            // column * k/gs + 16 * half, or kOffNone
+  uint32_t s[kStagedScales<KIND, CT>];        // column * k/gs + 16 * half, or kOffNone
   uint32_t as;                                // (row * nblk + blk) * 4, or kOffNone
 };
 
@@ -111,23 +112,23 @@ struct Rsrc {
   rsrc_t w, s, a, as;
 };
 
-template <int KIND, bool SWZ>
-__device__ __forceinline__ void stage_load(const Rsrc& r, const StageOffsets<KIND>& o, int c, bool valid,
-                                           StageRegs<KIND>& d) {
+template <int KIND, bool SWZ, int CT>
+__device__ __forceinline__ void stage_load(const Rsrc& r, const StageOffsets<KIND, CT>& o, int c, bool valid,
+                                           StageRegs<KIND, CT>& d) {
   const uint32_t uc = (uint32_t)c;
 #pragma unroll
   for (int j = 0; j < 4; ++j) d.a[j] = buf_load_x4(r.a, valid ? o.a[j] + uc * kChunkK : kOffNone);
   if constexpr (!SWZ) {
 #pragma unroll
-    for (int h = 0; h < kStagedScales<KIND>; ++h)
+    for (int h = 0; h < kStagedScales<KIND, CT>; ++h)
       d.s[h] = buf_load_x4(r.s, valid ? o.s[h] + uc * (KIND == kNV ? 32u : 16u) : kOffNone);
   }
   d.as = u2f(buf_load_u32(r.as, valid ? o.as + uc * (uint32_t)(kBlk * 4) : kOffNone));
 }
 
 // Store one chunk's staged data into an LDS stage.
-template <int KIND, bool SWZ>
-__device__ __forceinline__ void stage_store(Stage& st, const StageRegs<KIND>& d) {
+template <int KIND, bool SWZ, int CT>
+__device__ __forceinline__ void stage_store(Stage<CT>& st, const StageRegs<KIND, CT>& d) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -142,7 +143,7 @@ __device__ __forceinline__ void stage_store(Stage& st, const StageRegs<KIND>& d)
     // groups g = 0..3).  For each g, the two pairs become one dword at [col][8g + 4h], so the
     // reader lane (column, g) finds the pairs of blocks 0..3 in 8 contiguous bytes.
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int hh = 0; hh < kStagedScales<KIND, CT>; ++hh) {
       const int q = tid + kThreads * hh, col = q >> 1, h = q & 1;
       const u32x4 v = d.s[hh];
       uint32_t* base = reinterpret_cast<uint32_t*>(st.s + col * kSCol + 4 * h);
@@ -153,21 +154,23 @@ __device__ __forceinline__ void stage_store(Stage& st, const StageRegs<KIND>& d)
     }
   } else {
     // MXFP4: 16 bytes = blocks 0..3 x 4 lane groups, stored as is at [col][0..15].
-    uint64_t* base = reinterpret_cast<uint64_t*>(st.s + tid * kSCol);
-    base[0] = ((uint64_t)d.s[0][1] << 32) | d.s[0][0];
-    base[1] = ((uint64_t)d.s[0][3] << 32) | d.s[0][2];
+    if (tid < kTileNT<CT>) {
+      uint64_t* base = reinterpret_cast<uint64_t*>(st.s + tid * kSCol);
+      base[0] = ((uint64_t)d.s[0][1] << 32) | d.s[0][0];
+      base[1] = ((uint64_t)d.s[0][3] << 32) | d.s[0][2];
+    }
   }
 }
 
-template <int MT>
-__device__ __forceinline__ void compute_block_nv(const Stage& st, int bq, const u32x4 (&wq)[kCT],
-                                                 const uint32_t (&sc)[kCT], f32x4 (&acc)[MT][kCT]) {
+template <int MT, int CT>
+__device__ __forceinline__ void compute_block_nv(const Stage<CT>& st, int bq, const u32x4 (&wq)[CT],
+                                                 const uint32_t (&sc)[CT], f32x4 (&acc)[MT][CT]) {
   const int lane = threadIdx.x & 63, c16 = lane & 15, g = lane >> 4;
-  f32x4 part[MT][kCT];
+  f32x4 part[MT][CT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int ct = 0; ct < kCT; ++ct) part[mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < CT; ++ct) part[mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   u32x4 aq[MT][2];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -175,9 +178,9 @@ __device__ __forceinline__ void compute_block_nv(const Stage& st, int bq, const 
     aq[mt][0] = *reinterpret_cast<const u32x4*>(ap);
     aq[mt][1] = *reinterpret_cast<const u32x4*>(ap + 16);
   }
-  h16x2 ws[kCT];
+  h16x2 ws[CT];
 #pragma unroll
-  for (int ct = 0; ct < kCT; ++ct) ws[ct] = e4m3x2_to_f16<false>(sc[ct]);
+  for (int ct = 0; ct < CT; ++ct) ws[ct] = e4m3x2_to_f16<false>(sc[ct]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     h16x8 af[MT];
@@ -185,7 +188,7 @@ __device__ __forceinline__ void compute_block_nv(const Stage& st, int bq, const 
     for (int mt = 0; mt < MT; ++mt)
       af[mt] = e4m3x8_to_f16(aq[mt][i >> 1][2 * (i & 1)], aq[mt][i >> 1][2 * (i & 1) + 1]);
 #pragma unroll
-    for (int ct = 0; ct < kCT; ++ct) {
+    for (int ct = 0; ct < CT; ++ct) {
       const h16x8 bf = e2m1x8_scaled_f16(wq[ct][i], ws[ct][i >> 1]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) part[mt][ct] = mfma16x16x32_f16(af[mt], bf, part[mt][ct]);
@@ -197,7 +200,7 @@ __device__ __forceinline__ void compute_block_nv(const Stage& st, int bq, const 
   for (int mt = 0; mt < MT; ++mt) {
     const f32x4 as = *reinterpret_cast<const f32x4*>(st.as + bq * kRows + 16 * mt + 4 * g);
 #pragma unroll
-    for (int ct = 0; ct < kCT; ++ct)
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[mt][ct][v] = fmaf(part[mt][ct][v], as[v], acc[mt][ct][v]);
   }
@@ -206,15 +209,15 @@ __device__ __forceinline__ void compute_block_nv(const Stage& st, int bq, const 
 // MXFP4 block: exact bf16 operands (E4M3 activation bytes -> bf16; nibbles -> bf16 with the E8M0
 // scale applied by the conversion, a pure exponent) and the same per-block partial tile as NVFP4.
 // bf16 rather than f16 because an E8M0 scale can lie outside the f16 range.
-template <int MT>
-__device__ __forceinline__ void compute_block_mx(const Stage& st, int bq, const uint32_t (&sb)[kCT],
-                                                 const u32x4 (&wq)[kCT], f32x4 (&acc)[MT][kCT]) {
+template <int MT, int CT>
+__device__ __forceinline__ void compute_block_mx(const Stage<CT>& st, int bq, const uint32_t (&sb)[CT],
+                                                 const u32x4 (&wq)[CT], f32x4 (&acc)[MT][CT]) {
   const int lane = threadIdx.x & 63, c16 = lane & 15, g = lane >> 4;
-  f32x4 part[MT][kCT];
+  f32x4 part[MT][CT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int ct = 0; ct < kCT; ++ct) part[mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < CT; ++ct) part[mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   u32x4 aq[MT][2];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -224,16 +227,16 @@ __device__ __forceinline__ void compute_block_mx(const Stage& st, int bq, const 
   }
   // The lane's k = 32g .. +32 of the block is one MXFP4 group: its E8M0 byte sb[ct], used as the
   // exponent field of the conversion's scale operand.
-  float sv[kCT];
+  float sv[CT];
 #pragma unroll
-  for (int ct = 0; ct < kCT; ++ct) sv[ct] = u2f((sb[ct] & 0xFFu) << 23);
+  for (int ct = 0; ct < CT; ++ct) sv[ct] = u2f((sb[ct] & 0xFFu) << 23);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     bf16x8 af[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) af[mt] = e4m3x8_to_bf16(aq[mt][i >> 1][2 * (i & 1)], aq[mt][i >> 1][2 * (i & 1) + 1]);
 #pragma unroll
-    for (int ct = 0; ct < kCT; ++ct) {
+    for (int ct = 0; ct < CT; ++ct) {
       const bf16x8 bf = e2m1x8_pow2_bf16(wq[ct][i], sv[ct]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) part[mt][ct] = mfma16x16x32_bf16(af[mt], bf, part[mt][ct]);
@@ -243,7 +246,7 @@ __device__ __forceinline__ void compute_block_mx(const Stage& st, int bq, const 
   for (int mt = 0; mt < MT; ++mt) {
     const f32x4 as = *reinterpret_cast<const f32x4*>(st.as + bq * kRows + 16 * mt + 4 * g);
 #pragma unroll
-    for (int ct = 0; ct < kCT; ++ct)
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[mt][ct][v] = fmaf(part[mt][ct][v], as[v], acc[mt][ct][v]);
   }
@@ -273,8 +276,8 @@ __device__ __forceinline__ u32x4 wload(rsrc_t r, uint32_t off) {
 // SWZ: the expert's planes are in the swizzled layout (fp4_weight_swizzle): a weight load of the
 // wavefront reads 1 KB of consecutive bytes, and each lane loads the weight scales of its pieces
 // for a whole chunk directly into registers, one chunk ahead, instead of staging them in LDS.
-template <int MT, int KIND, bool SWZ>
-__device__ void run_pass(const GemmArgs& p, const ExpertView& ex, int n0, int m0, int mend, Stage (&st)[2]) {
+template <int MT, int KIND, bool SWZ, int CT>
+__device__ void run_pass(const GemmArgs& p, const ExpertView& ex, int n0, int m0, int mend, Stage<CT> (&st)[2]) {
   const int tid = threadIdx.x, lane = tid & 63, c16 = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int k = p.k, nblk = k >> 7;
@@ -300,7 +303,7 @@ __device__ void run_pass(const GemmArgs& p, const ExpertView& ex, int n0, int m0
   // load zeros.  A partial last chunk reads zeros past k (the descriptors end at the planes' ends,
   // and every row's data beyond k belongs to the next row, so those lanes are also masked below by
   // the block check: blocks >= nblk are never computed).
-  StageOffsets<KIND> so;
+  StageOffsets<KIND, CT> so;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int q = tid + kThreads * j, row = q >> 5, part = q & 31;
@@ -315,17 +318,18 @@ __device__ void run_pass(const GemmArgs& p, const ExpertView& ex, int n0, int m0
   }
   if constexpr (!SWZ) {
 #pragma unroll
-    for (int h = 0; h < kStagedScales<KIND>; ++h) {
+    for (int h = 0; h < kStagedScales<KIND, CT>; ++h) {
       const int q = tid + kThreads * h;
       const int col = KIND == kNV ? (q >> 1) : q, half = KIND == kNV ? (q & 1) : 0;
-      so.s[h] = (n0 + col < p.n) ? (uint32_t)(n0 + col) * (uint32_t)(k / GS) + 16u * half : kOffNone;
+      so.s[h] = (col < kTileNT<CT> && n0 + col < p.n) ? (uint32_t)(n0 + col) * (uint32_t)(k / GS) + 16u * half
+                                                      : kOffNone;
     }
   }
   // Weight stream offsets of this wavefront's 4 column tiles (and, swizzled, of their scales).
-  uint32_t wo[kCT], sco[kCT];
+  uint32_t wo[CT], sco[CT];
 #pragma unroll
-  for (int ct = 0; ct < kCT; ++ct) {
-    const int col = n0 + wave * kWaveCols + 16 * ct + c16;
+  for (int ct = 0; ct < CT; ++ct) {
+    const int col = n0 + wave * (16 * CT) + 16 * ct + c16;
     if constexpr (SWZ) {
       const uint32_t t = (uint32_t)col >> 4, piece = (uint32_t)(16 * g + c16);
       wo[ct] = col < p.n ? t * (uint32_t)nblk * 1024u + 16u * piece : kOffNone;
@@ -336,11 +340,11 @@ __device__ void run_pass(const GemmArgs& p, const ExpertView& ex, int n0, int m0
     }
   }
 
-  f32x4 acc[MT][kCT];
+  f32x4 acc[MT][CT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int ct = 0; ct < kCT; ++ct) acc[mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < CT; ++ct) acc[mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Prologue: chunk 0 staged into LDS stage 0, chunk 1 loaded into the staging registers, then
   // (swizzled) the weight scales of chunk 0 and the weight ring for the blocks of chunk 0 -- the
@@ -349,22 +353,22 @@ __device__ void run_pass(const GemmArgs& p, const ExpertView& ex, int n0, int m0
   // entry and the back edge, stay exact.  Every group of loads is pinned where it is written
   // (sched_barrier): the machine scheduler would otherwise sink loads toward their first use.  All
   // loads are issued on every path (out-of-range ones return zero without touching memory).
-  StageRegs<KIND> sr;
-  stage_load<KIND, SWZ>(r, so, 0, true, sr);
+  StageRegs<KIND, CT> sr;
+  stage_load<KIND, SWZ, CT>(r, so, 0, true, sr);
   __builtin_amdgcn_sched_barrier(0);
-  stage_store<KIND, SWZ>(st[0], sr);
-  stage_load<KIND, SWZ>(r, so, 1, 1 < nch, sr);
+  stage_store<KIND, SWZ, CT>(st[0], sr);
+  stage_load<KIND, SWZ, CT>(r, so, 1, 1 < nch, sr);
   __builtin_amdgcn_sched_barrier(0);
-  typename ChunkScale<KIND>::T scn[kCT], scc[kCT];   // next chunk's / this chunk's scales (SWZ)
+  typename ChunkScale<KIND>::T scn[CT], scc[CT];   // next chunk's / this chunk's scales (SWZ)
   if constexpr (SWZ) {
 #pragma unroll
-    for (int ct = 0; ct < kCT; ++ct) scn[ct] = scale_load<KIND>(r.s, sco[ct]);
+    for (int ct = 0; ct < CT; ++ct) scn[ct] = scale_load<KIND>(r.s, sco[ct]);
   }
-  u32x4 wq[kBlk][kCT];
+  u32x4 wq[kBlk][CT];
 #pragma unroll
   for (int j = 0; j < kBlk; j += 2) {
 #pragma unroll
-    for (int ct = 0; ct < kCT; ++ct) {
+    for (int ct = 0; ct < CT; ++ct) {
       wq[j][ct] = wload<SWZ>(r.w, j < nblk ? wo[ct] + (uint32_t)j * kWB : kOffNone);
       wq[j + 1][ct] = wload<SWZ>(r.w, j + 1 < nblk ? wo[ct] + (uint32_t)(j + 1) * kWB : kOffNone);
     }
@@ -373,40 +377,40 @@ __device__ void run_pass(const GemmArgs& p, const ExpertView& ex, int n0, int m0
 
   for (int c = 0; c < nch; ++c) {
     lds_barrier();                           // stage c&1 complete; stage (c+1)&1 no longer read
-    stage_store<KIND, SWZ>(st[(c + 1) & 1], sr);  // chunk c+1 (zeros past the end)
-    stage_load<KIND, SWZ>(r, so, c + 2, c + 2 < nch, sr);
+    stage_store<KIND, SWZ, CT>(st[(c + 1) & 1], sr);  // chunk c+1 (zeros past the end)
+    stage_load<KIND, SWZ, CT>(r, so, c + 2, c + 2 < nch, sr);
     __builtin_amdgcn_sched_barrier(0);
-    const Stage& cur = st[c & 1];
-    uint2 scp[kCT];                          // NVFP4 scale pairs of blocks 0..3 of this chunk
-    uint32_t mxs[kCT];                       // MXFP4 scale bytes of blocks 0..3 of this chunk
+    const Stage<CT>& cur = st[c & 1];
+    uint2 scp[CT];                          // NVFP4 scale pairs of blocks 0..3 of this chunk
+    uint32_t mxs[CT];                       // MXFP4 scale bytes of blocks 0..3 of this chunk
     if constexpr (SWZ) {
 #pragma unroll
-      for (int ct = 0; ct < kCT; ++ct) {
+      for (int ct = 0; ct < CT; ++ct) {
         scc[ct] = scn[ct];
         if constexpr (KIND == kNV) scp[ct] = scc[ct];
         else mxs[ct] = scc[ct];
       }
     } else if constexpr (KIND == kNV) {
 #pragma unroll
-      for (int ct = 0; ct < kCT; ++ct)
-        scp[ct] = *reinterpret_cast<const uint2*>(cur.s + (wave * kWaveCols + 16 * ct + c16) * kSCol + 8 * g);
+      for (int ct = 0; ct < CT; ++ct)
+        scp[ct] = *reinterpret_cast<const uint2*>(cur.s + (wave * (16 * CT) + 16 * ct + c16) * kSCol + 8 * g);
     }
 #pragma unroll
     for (int bq = 0; bq < kBlk; ++bq) {
       const int b = c * kBlk + bq;
       if (b < nblk) {
         if constexpr (KIND == kNV) {
-          uint32_t sc[kCT];
+          uint32_t sc[CT];
 #pragma unroll
-          for (int ct = 0; ct < kCT; ++ct) sc[ct] = (bq < 2 ? scp[ct].x : scp[ct].y) >> (16 * (bq & 1));
-          compute_block_nv<MT>(cur, bq, wq[bq], sc, acc);
+          for (int ct = 0; ct < CT; ++ct) sc[ct] = (bq < 2 ? scp[ct].x : scp[ct].y) >> (16 * (bq & 1));
+          compute_block_nv<MT, CT>(cur, bq, wq[bq], sc, acc);
         } else {
-          uint32_t sb[kCT];
+          uint32_t sb[CT];
 #pragma unroll
-          for (int ct = 0; ct < kCT; ++ct)
+          for (int ct = 0; ct < CT; ++ct)
             sb[ct] = SWZ ? mxs[ct] >> (8 * bq)
-                         : (uint32_t)cur.s[(wave * kWaveCols + 16 * ct + c16) * kSCol + 4 * bq + g];
-          compute_block_mx<MT>(cur, bq, sb, wq[bq], acc);
+                         : (uint32_t)cur.s[(wave * (16 * CT) + 16 * ct + c16) * kSCol + 4 * bq + g];
+          compute_block_mx<MT, CT>(cur, bq, sb, wq[bq], acc);
         }
       }
       // Refill the ring two blocks at a time: the two 64-byte halves of each column's 128-byte
@@ -417,12 +421,12 @@ __device__ void run_pass(const GemmArgs& p, const ExpertView& ex, int n0, int m0
         if constexpr (SWZ) {
           if (bq == 1) {
 #pragma unroll
-            for (int ct = 0; ct < kCT; ++ct)
+            for (int ct = 0; ct < CT; ++ct)
               scn[ct] = scale_load<KIND>(r.s, c + 1 < nch ? sco[ct] + (uint32_t)(c + 1) * kSQ : kOffNone);
           }
         }
 #pragma unroll
-        for (int ct = 0; ct < kCT; ++ct) {
+        for (int ct = 0; ct < CT; ++ct) {
           wq[bq - 1][ct] = wload<SWZ>(r.w, bn - 1 < nblk ? wo[ct] + (uint32_t)(bn - 1) * kWB : kOffNone);
           wq[bq][ct] = wload<SWZ>(r.w, bn < nblk ? wo[ct] + (uint32_t)bn * kWB : kOffNone);
         }
@@ -441,26 +445,28 @@ __device__ void run_pass(const GemmArgs& p, const ExpertView& ex, int n0, int m0
       if (prow < mend) {
         const bool bad = act_row(p, prow) < 0;
 #pragma unroll
-        for (int ct = 0; ct < kCT; ++ct) {
-          const int col = n0 + wave * kWaveCols + 16 * ct + c16;
+        for (int ct = 0; ct < CT; ++ct) {
+          const int col = n0 + wave * (16 * CT) + 16 * ct + c16;
           if (col < p.n) p.out[(size_t)prow * p.n + col] = bad ? __builtin_nanf("") : acc[mt][ct][v] * post;
         }
       }
     }
 }
 
-template <int KIND, bool SWZ>
-__device__ void run_expert(const GemmArgs& p, const ExpertView& ex, int n0, Stage (&st)[2]) {
+template <int KIND, bool SWZ, int CT>
+__device__ void run_expert(const GemmArgs& p, const ExpertView& ex, int n0, Stage<CT> (&st)[2]) {
   for (int m0 = ex.rb; m0 < ex.re; m0 += kRows) {
     const int mend = min(m0 + kRows, ex.re);
     if (m0 > ex.rb) lds_barrier();           // the previous pass may still be reading the stages
-    if (mend - m0 > 16) run_pass<2, KIND, SWZ>(p, ex, n0, m0, mend, st);
-    else run_pass<1, KIND, SWZ>(p, ex, n0, m0, mend, st);
+    if (mend - m0 > 16) run_pass<2, KIND, SWZ, CT>(p, ex, n0, m0, mend, st);
+    else run_pass<1, KIND, SWZ, CT>(p, ex, n0, m0, mend, st);
   }
 }
 
+template <int CT>
 __global__ __launch_bounds__(kThreads, 2) void gemm_decode_kernel(GemmArgs p, int ntn, int xcd_map) {
-  __shared__ Stage st[2];
+  constexpr int kTileN = kTileNT<CT>;
+  __shared__ Stage<CT> st[2];
   const int L = blockIdx.x;
   int e, nt;
   if (xcd_map) {
@@ -485,13 +491,13 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_decode_kernel(GemmArgs p, in
   const int n0 = nt * kTileN;
   // kinds 0/1: plain planes; 2/3: the same formats in the swizzled layout
   if (ex.kind == kNV) {
-    run_expert<kNV, false>(p, ex, n0, st);
+    run_expert<kNV, false, CT>(p, ex, n0, st);
   } else if (ex.kind == kMX) {
-    run_expert<kMX, false>(p, ex, n0, st);
+    run_expert<kMX, false, CT>(p, ex, n0, st);
   } else if (ex.kind == (kNV | kSwizzled)) {
-    run_expert<kNV, true>(p, ex, n0, st);
+    run_expert<kNV, true, CT>(p, ex, n0, st);
   } else if (ex.kind == (kMX | kSwizzled)) {
-    run_expert<kMX, true>(p, ex, n0, st);
+    run_expert<kMX, true, CT>(p, ex, n0, st);
   } else {
     for (int i = threadIdx.x; i < (ex.re - ex.rb) * kTileN; i += kThreads) {
       const int r = ex.rb + i / kTileN, col = n0 + i % kTileN;
@@ -502,14 +508,27 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_decode_kernel(GemmArgs p, in
 
 }  // namespace
 
+#ifndef FP4MOE_DECODE_NARROW_ROWS
+#define FP4MOE_DECODE_NARROW_ROWS 1024
+#endif
+
+// Launches with few packed rows in total (a decode step of up to 128 tokens at top-8) leave most
+// experts with a few rows: 128-column workgroups (twice as many, three per compute unit) stream
+// their weights faster (over the 256 experts of k = 7168, n = 2048: 4 tokens 59.6 us against 66.4,
+// 64 tokens 275 against 285, 128 tokens 303 against 307); the full 512-token step (4096 rows) is
+// faster with 256 columns per workgroup (358 us against 367).
 hipError_t launch_gemm_decode(const GemmArgs& a, hipStream_t stream) {
-  const int ntn = (a.n + kTileN - 1) / kTileN;
+  const bool narrow = a.total_rows <= FP4MOE_DECODE_NARROW_ROWS;
+  const int tile_n = narrow ? kTileNT<2> : kTileNT<4>;
+  const int ntn = (a.n + tile_n - 1) / tile_n;
   const int xcd_map = a.num_experts >= 8 ? 1 : 0;
   const int64_t eg = xcd_map ? (int64_t)(a.num_experts + 7) / 8 * 8 : a.num_experts;
   const int64_t blocks = eg * ntn;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(gemm_decode_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, ntn,
-                     xcd_map);
+  if (narrow)
+    hipLaunchKernelGGL(gemm_decode_kernel<2>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, ntn, xcd_map);
+  else
+    hipLaunchKernelGGL(gemm_decode_kernel<4>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, ntn, xcd_map);
   return hipGetLastError();
 }
 
