@@ -250,7 +250,8 @@ def fp4_grouped_gemm(a_codes, a_scales, row_ids, offsets, w_ptrs, s_ptrs, kinds,
                      out=None, stream=None):
     """Routed rows packed per expert.  a_codes u8 [a_rows, k], a_scales f32 [a_rows, k/128],
     row_ids int32 [R] or None, offsets int32 [E+1], w_ptrs/s_ptrs int64 [E] (device addresses),
-    kinds int32 [E], scale2 f32 [E] -> out f32 [R, n] with R = offsets[-1] (read on the host
+    kinds int32 [E] (0/1 NVFP4/MXFP4, | SWIZZLED for swizzled planes), scale2 f32 [E]
+    -> out f32 [R, n] with R = offsets[-1] (read on the host
     only from `out`'s shape when out is given; otherwise from row_ids' length)."""
     _dev(a_codes, torch.uint8, "a_codes", 2)
     _dev(a_scales, torch.float32, "a_scales", 2)
