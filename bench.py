@@ -79,6 +79,18 @@ def algorithmic_bytes(wl) -> dict:
             "total": weights + acts + tables + out}
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, budget_s: float):
     """Time the oracle (as it stands) on a bounded sample of the same workload: act-quant of every
     token row, then the grouped GEMM of the first experts' packed rows, adding experts until about
@@ -114,7 +126,7 @@ def cpu_baseline(wl, budget_s: float):
     frac = done_e / wl.E
     elapsed = t_gemm + t_aq * frac
     return {"value": nbytes / elapsed / 1e12, "unit": "TB/s", "cores": used_threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": (f"oracle act-quant of all {wl.x.shape[0]} token rows (time pro-rated to the "
                        f"sampled share) + f64 grouped GEMM of experts 0..{done_e - 1} "
                        f"({rows} packed rows, {nbytes} weight bytes) of the same workload; "
@@ -384,6 +396,7 @@ def run_single_expert(args, torch, fp4, dev):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
         "cpu_baseline": {"value": wbytes / t_cpu / 1e12, "unit": "TB/s", "cores": 1, "kind": "oracle",
+                         "cpu": cpu_model(),
                          "sample": f"oracle act-quant + f64 expert GEMM of the whole step, one thread, {t_cpu:.2f} s"},
     }
     print(json.dumps(result), flush=True)
