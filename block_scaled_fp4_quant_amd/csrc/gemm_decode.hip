@@ -435,7 +435,9 @@ __device__ void run_pass(const GemmArgs& p, const ExpertView& ex, int n0, int m0
     }
   }
 
-  // Store: the lane holds column (16ct + c16) and rows 4g+v of each row tile.
+  // Store: the lane holds column (16ct + c16) and rows 4g+v of each row tile.  Non-temporal: the
+  // output is not read again by this launch, and keeping it out of the caches leaves them to the
+  // activation rows (measured: 346 us against 357 us for the grouped decode step).
   const float post = (KIND == kNV) ? ex.scale2 : 1.0f;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -447,7 +449,8 @@ __device__ void run_pass(const GemmArgs& p, const ExpertView& ex, int n0, int m0
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           const int col = n0 + wave * (16 * CT) + 16 * ct + c16;
-          if (col < p.n) p.out[(size_t)prow * p.n + col] = bad ? __builtin_nanf("") : acc[mt][ct][v] * post;
+          if (col < p.n)
+            __builtin_nontemporal_store(bad ? __builtin_nanf("") : acc[mt][ct][v] * post, &p.out[(size_t)prow * p.n + col]);
         }
       }
     }
