@@ -109,6 +109,20 @@ def test_config3_swizzled_bits_equal_plain():
     del keep
 
 
+def test_config4_swizzled_bits_equal_plain():
+    """The prefill step at its full size (8192 tokens, Zipf top-8, 255 NVFP4 + 1 MXFP4 experts,
+    k=7168, n=4096) on swizzled planes: bit-identical to the plain layout's result, which the
+    sampled oracle check covers."""
+    gd = GroupedDevice(workloads.config4())
+    codes, scales, plain = gd.step()
+    w_ptrs, s_ptrs, kinds_t, keep = _swizzled_tables(gd, lambda e: True)
+    got = fp4.fp4_grouped_gemm(codes, scales, gd.row_ids, gd.offsets, w_ptrs, s_ptrs, kinds_t, gd.scale2, gd.n)
+    torch.cuda.synchronize()
+    assert not bool(torch.isnan(got).any())
+    assert torch.equal(got, plain)
+    del keep
+
+
 def test_swiglu_fused_swizzled_bits_equal_plain(orc):
     inter, k = 256, 512
     wl = workloads.grouped_random(12, 200, 6, 2, 2 * inter, k, kinds=[NV, MX, NV, NV, MX, NV])
