@@ -9,7 +9,9 @@
 // row-streaming kernel only n/256 = 8..28 workgroups, far too few to stream 8 MB of weights; this
 // kernel gives each workgroup 16 columns (n/16 = 128..448 workgroups) and splits k over its 8
 // wavefronts: wavefront w takes the 128-wide blocks b = w, w+8, w+16, ..., so the 8 wavefronts of a
-// workgroup read 8 consecutive 1 KB weight runs at a time with swizzled planes.
+// workgroup read 8 consecutive 1 KB weight runs at a time with swizzled planes.  A grouped launch
+// may give a 16-column tile fewer wavefronts (KS = 4, 2 or 1, the workgroup then owning 8 / KS
+// tiles), so that each wavefront streams a longer run of blocks.
 //
 // Data movement: a wavefront keeps kRing blocks of loads in flight, refilling a slot as soon as it
 // has computed on it: per block the lane's 16 weight bytes, its scale bytes and its 32 bytes of
@@ -20,9 +22,9 @@
 // g = lane/16 holds k = 32g .. +32 of the block), as in the row-streaming kernel: NVFP4 on exact f16
 // operands (nibble -> f16 times the E4M3 scale in f16), MXFP4 on exact bf16 operands (the E8M0 scale
 // applied by the conversion), four 16x16x32 MFMAs cover one activation-scale group, whose partial
-// tile is scaled by as[r, b] with one f32 FMA per output.  The 8 wavefronts' f32 tiles are then
-// summed through LDS in wavefront order 0, 1, ..., 7 (a fixed order: the result does not depend on
-// g or on timing), and scale2 multiplies the sum.
+// tile is scaled by as[r, b] with one f32 FMA per output.  The KS wavefronts' f32 tiles of a column
+// tile are then summed through LDS in wavefront order (a fixed order for a given KS, n and k: the
+// result does not depend on g or on timing), and scale2 multiplies the sum.
 #include <algorithm>
 
 #include "device_common.h"
@@ -37,9 +39,9 @@ constexpr int kRing = 4;                    // blocks in flight per wavefront (r
 constexpr int kMaxRows = 16;
 constexpr int kMaxK = 8192;
 // Grouped launches take this kernel automatically when they hold at most kGroupedAutoRows packed
-// rows (two tokens at top-8: measured over 256 experts of k = 7168, n = 2048, one token takes 26 us
-// here against 60 us in the row-streaming kernel, two tokens 46 against 63, four tokens 82 against
-// 66), and up to kGroupedMaxRows when the schedule forces it.
+// rows (two tokens at top-8: measured over 256 experts of k = 7168, n = 2048, one token takes 21 us
+// here against 44 us in the row-streaming kernel, two tokens 33 against 51, four tokens 58 against
+// 56-60, eight 107 against 100), and up to kGroupedMaxRows when the schedule forces it.
 constexpr int kGroupedMaxRows = 128;
 constexpr int kGroupedAutoRows = 16;
 constexpr int kMaxExperts = 1024;
@@ -75,11 +77,16 @@ __device__ __forceinline__ int act_row(const GemmArgs& p, int prow) {
   return (r >= 0 && r < p.a_rows) ? r : -2;
 }
 
-// Packed rows [m0, m0 + mrows) (mrows <= 16) of expert `ex`, columns 16t .. 16t+15.
-template <int KIND, bool SWZ>
-__device__ void run(const GemmArgs& p, const View& ex, int t, int m0, int mrows, Smem& sm) {
+// Packed rows [m0, m0 + mrows) (mrows <= 16) of expert `ex`, column tile group tg: KS wavefronts
+// per 16-column tile, so the group holds kWaves / KS tiles, tiles (kWaves / KS) tg + sub, and the
+// wavefront kw = wave % KS of a tile takes the blocks b = kw, kw + KS, ...
+template <int KIND, bool SWZ, int KS>
+__device__ void run(const GemmArgs& p, const View& ex, int tg, int m0, int mrows, Smem& sm) {
+  static_assert(KS >= 1 && kWaves % KS == 0, "wavefronts per tile");
   const int tid = threadIdx.x, lane = tid & 63, c16 = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sub = wave / KS, kw = wave % KS;
+  const int t = (kWaves / KS) * tg + sub;
   const int k = p.k, nblk = k >> 7, nq = (nblk + 3) >> 2;
   const int col = 16 * t + c16;
   const uint32_t n16 = (uint32_t)(p.n + 15) >> 4;
@@ -126,14 +133,14 @@ __device__ void run(const GemmArgs& p, const View& ex, int t, int m0, int mrows,
   const uint32_t a0 = arow >= 0 ? (uint32_t)arow * (uint32_t)k + 32u * g : kOffNone;
   auto a_off = [&](int b) -> uint32_t { return (b < nblk && a0 != kOffNone) ? a0 + (uint32_t)b * 128u : kOffNone; };
 
-  // Ring: the wavefront's blocks b = wave + 4 i, weights, scale bytes and activation operand of
+  // Ring: the wavefront's blocks b = kw + KS i, weights, scale bytes and activation operand of
   // each, all issued before anything waits.
-  const int nbw = (nblk - wave + kWaves - 1) / kWaves;
+  const int nbw = (nblk - kw + KS - 1) / KS;
   u32x4 wq[kRing], aq[kRing][2];
   uint32_t sq[kRing];
 #pragma unroll
   for (int j = 0; j < kRing; ++j) {
-    const int b = j < nbw ? wave + kWaves * j : nblk;
+    const int b = j < nbw ? kw + KS * j : nblk;
     wq[j] = wload<SWZ>(rw, w_off(b));
     sq[j] = s_load(b);
     aq[j][0] = buf_load_x4(ra, a_off(b));
@@ -162,7 +169,7 @@ __device__ void run(const GemmArgs& p, const View& ex, int t, int m0, int mrows,
     for (int j = 0; j < kRing; ++j) {
       const int i = i0 + j;
       if (i < nbw) {
-        const int b = wave + kWaves * i;
+        const int b = kw + KS * i;
         f32x4 part = {0.f, 0.f, 0.f, 0.f};
         if constexpr (KIND == kNV) {
           const h16x2 ws = e4m3x2_to_f16<false>(sq[j]);
@@ -189,7 +196,7 @@ __device__ void run(const GemmArgs& p, const View& ex, int t, int m0, int mrows,
       // refill the slot with the block kRing further on (when the wavefront has more than kRing blocks)
       if (i0 + kRing < nbw) {
         const int inext = i + kRing;
-        const int bn = inext < nbw ? wave + kWaves * inext : nblk;
+        const int bn = inext < nbw ? kw + KS * inext : nblk;
         wq[j] = wload<SWZ>(rw, w_off(bn));
         sq[j] = s_load(bn);
         aq[j][0] = buf_load_x4(ra, a_off(bn));
@@ -199,14 +206,15 @@ __device__ void run(const GemmArgs& p, const View& ex, int t, int m0, int mrows,
     }
   }
 
-  // Sum the wavefronts' tiles in wavefront order, apply scale2, store rows 4g+v of column col.
+  // Sum the tile's KS wavefront partials in wavefront order, apply scale2, store rows 4g+v of
+  // column col.
   sm.red[wave][lane] = acc;
   __syncthreads();
-  if (wave == 0) {
-    f32x4 sum = sm.red[0][lane];
+  if (kw == 0) {
+    f32x4 sum = sm.red[wave][lane];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
-      const f32x4 o = sm.red[w][lane];
+    for (int w = 1; w < KS; ++w) {
+      const f32x4 o = sm.red[wave + w][lane];
 #pragma unroll
       for (int v = 0; v < 4; ++v) sum[v] += o[v];
     }
@@ -222,24 +230,26 @@ __device__ void run(const GemmArgs& p, const View& ex, int t, int m0, int mrows,
   }
 }
 
-// Packed rows [lo, hi) of expert `ex` for tile t, in passes of 16 rows (every pass streams the
-// tile's weights again; the host sends only launches with few rows per expert here).
-__device__ void run_rows(const GemmArgs& p, const View& ex, int kind, int t, int lo, int hi, Smem& sm) {
+// Packed rows [lo, hi) of expert `ex` for tile group tg, in passes of 16 rows (every pass streams
+// the group's weights again; the host sends only launches with few rows per expert here).
+template <int KS>
+__device__ void run_rows(const GemmArgs& p, const View& ex, int kind, int tg, int lo, int hi, Smem& sm) {
+  constexpr int kTilesPerGroup = kWaves / KS;
   for (int m0 = lo; m0 < hi; m0 += kMaxRows) {
     const int mrows = min(kMaxRows, hi - m0);
     if (kind == kNV) {
-      run<kNV, false>(p, ex, t, m0, mrows, sm);
+      run<kNV, false, KS>(p, ex, tg, m0, mrows, sm);
     } else if (kind == kMX) {
-      run<kMX, false>(p, ex, t, m0, mrows, sm);
+      run<kMX, false, KS>(p, ex, tg, m0, mrows, sm);
     } else if (kind == (kNV | kSwizzled)) {
-      run<kNV, true>(p, ex, t, m0, mrows, sm);
+      run<kNV, true, KS>(p, ex, tg, m0, mrows, sm);
     } else if (kind == (kMX | kSwizzled)) {
-      run<kMX, true>(p, ex, t, m0, mrows, sm);
+      run<kMX, true, KS>(p, ex, tg, m0, mrows, sm);
     } else {
       // a weight format the kernel does not take: NaN rows
-      for (int i = threadIdx.x; i < mrows * 16; i += kThreads) {
-        const int col = 16 * t + (i & 15);
-        if (col < p.n) p.out[(size_t)(m0 + (i >> 4)) * p.n + col] = __builtin_nanf("");
+      for (int i = threadIdx.x; i < mrows * 16 * kTilesPerGroup; i += kThreads) {
+        const int col = 16 * kTilesPerGroup * tg + (i % (16 * kTilesPerGroup));
+        if (col < p.n) p.out[(size_t)(m0 + i / (16 * kTilesPerGroup)) * p.n + col] = __builtin_nanf("");
       }
     }
     __syncthreads();                         // the next pass reuses the LDS
@@ -253,16 +263,19 @@ __device__ __forceinline__ int2 expert_rows(const GemmArgs& p, int e) {
   return make_int2(lo, hi);
 }
 
-// Single expert: workgroup t owns tile t.  Grouped (persistent): every workgroup lists the experts
-// that have rows (a block-wide scan over the offsets into LDS), then takes the (active expert, tile)
-// items blockIdx.x, blockIdx.x + gridDim.x, ... -- no workgroup is spent on an empty expert.
-// At most 128 registers (4 wavefronts per SIMD): two workgroups share a compute unit, so one computes
-// while the other waits for its loads (one token over 256 experts: 26 us, against 30 us with every
-// block of k in flight and one workgroup per compute unit).
-__global__ __launch_bounds__(kThreads, 4) void gemm_skinny_kernel(GemmArgs p, int ntiles) {
+// Single expert (KS = 8): workgroup t owns tile t.  Grouped (persistent): every workgroup lists the
+// experts that have rows (a block-wide scan over the offsets into LDS), then takes the (active
+// expert, tile group) items blockIdx.x, blockIdx.x + gridDim.x, ... -- no workgroup is spent on an
+// empty expert.  The host picks KS so that there are about as many items as workgroups: a wavefront
+// then streams one long run of blocks, and its load ring does not drain between short items.
+// At most 128 registers (4 wavefronts per SIMD): two workgroups share a compute unit, so one
+// computes while the other waits for its loads (one token over 256 experts, 8 wavefronts per tile:
+// 26 us, against 30 us with every block of k in flight and one workgroup per compute unit).
+template <int KS>
+__global__ __launch_bounds__(kThreads, 4) void gemm_skinny_kernel(GemmArgs p, int ngroups) {
   __shared__ Smem sm;
   if (!p.offsets) {
-    run_rows(p, View{p.w, p.s, p.scale2}, p.kind, blockIdx.x, 0, p.total_rows, sm);
+    run_rows<KS>(p, View{p.w, p.s, p.scale2}, p.kind, blockIdx.x, 0, p.total_rows, sm);
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -296,14 +309,23 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_skinny_kernel(GemmArgs p, in
   for (int j = 0; j < kPer; ++j)
     if (flags[j]) sm.active[pos++] = tid * kPer + j;
   __syncthreads();
-  const int items = total * ntiles;
+  const int items = total * ngroups;
   for (int it = blockIdx.x; it < items; it += gridDim.x) {
-    const int e = sm.active[it / ntiles], t = it % ntiles;
+    const int e = sm.active[it / ngroups], tg = it % ngroups;
     const int2 r = expert_rows(p, e);
     const View ex{reinterpret_cast<const uint8_t*>(p.w_ptrs[e]), reinterpret_cast<const uint8_t*>(p.s_ptrs[e]),
                   p.scale2s[e]};
-    run_rows(p, ex, p.kinds[e], t, r.x, r.y, sm);
+    run_rows<KS>(p, ex, p.kinds[e], tg, r.x, r.y, sm);
   }
+}
+
+template <int KS>
+hipError_t launch_ks(const GemmArgs& a, int tiles, hipStream_t stream) {
+  constexpr int kTilesPerGroup = kWaves / KS;
+  const int ngroups = (tiles + kTilesPerGroup - 1) / kTilesPerGroup;
+  const int64_t grid = a.offsets ? std::min<int64_t>((int64_t)a.num_experts * ngroups, kGridCap) : ngroups;
+  hipLaunchKernelGGL(gemm_skinny_kernel<KS>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a, ngroups);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -320,9 +342,20 @@ bool gemm_skinny_grouped_fits(int64_t total_rows, int32_t num_experts, int32_t n
 
 hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
   const int tiles = (a.n + 15) / 16;
-  const int64_t grid = a.offsets ? std::min<int64_t>((int64_t)a.num_experts * tiles, kGridCap) : tiles;
-  hipLaunchKernelGGL(gemm_skinny_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a, tiles);
-  return hipGetLastError();
+  if (!a.offsets) return launch_ks<kWaves>(a, tiles, stream);
+  // Grouped: at most min(E, rows) experts hold rows.  Take the fewest wavefronts per tile that
+  // still give every workgroup of the persistent grid an item (one token at top-8 over n = 2048:
+  // 8 experts x 128 tiles -> 4 wavefronts per tile, 512 items).
+  const int64_t active = std::min<int64_t>(a.num_experts, a.total_rows);
+  for (int ks = 1; ks < kWaves; ks *= 2) {
+    const int64_t items = active * ((tiles + kWaves / ks - 1) / (kWaves / ks));
+    if (items >= kGridCap) {
+      if (ks == 1) return launch_ks<1>(a, tiles, stream);
+      if (ks == 2) return launch_ks<2>(a, tiles, stream);
+      return launch_ks<4>(a, tiles, stream);
+    }
+  }
+  return launch_ks<kWaves>(a, tiles, stream);
 }
 
 }  // namespace fp4moe

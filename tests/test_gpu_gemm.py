@@ -321,7 +321,7 @@ def test_splitk_limits_fall_back(orc):
 
 
 @pytest.mark.parametrize("sched", [fp4.SCHEDULE_AUTO, fp4.SCHEDULE_SPLITK], ids=["auto", "splitk"])
-@pytest.mark.parametrize("T", [1, 4, 16])
+@pytest.mark.parametrize("T", [1, 2, 4, 16])
 @pytest.mark.parametrize("swz", [False, True])
 def test_grouped_few_tokens_splitk(orc, config3_dev, T, swz, sched):
     """A decode step of a few tokens over the 256 NVFP4 experts of the decode workload (k = 7168,
@@ -334,6 +334,32 @@ def test_grouped_few_tokens_splitk(orc, config3_dev, T, swz, sched):
         _few_tokens_case(orc, gd, T, swz)
     finally:
         fp4.set_gemm_schedule(fp4.SCHEDULE_AUTO)
+
+
+@pytest.mark.parametrize("seed,T,E,n,ks", [(21, 2, 16, 1592, 4), (22, 16, 128, 200, 2), (23, 16, 128, 1000, 1)],
+                         ids=["ks4", "ks2", "ks1"])
+def test_grouped_splitk_tile_groups(orc, seed, T, E, n, ks):
+    """Grouped split-k launches whose size gives a 16-column tile 4, 2 or 1 wavefronts (the workgroup
+    then owns 2, 4 or 8 tiles): min(E, rows) x ceil(tiles * ks / 8) first reaches 512 items at that
+    ks.  n is not a multiple of the group width, so the last tile group holds a ragged tile and tiles
+    past n.  Mixed NVFP4/MXFP4 experts, top-8, k = 256; every output within the bound, run-to-run
+    identical."""
+    tiles = (n + 15) // 16
+    est = min(E, 8 * T)
+    pick = next((c for c in (1, 2, 4) if est * -(-tiles * c // 8) >= 512), 8)
+    assert pick == ks and (n % (16 * 8 // ks)) != 0
+    kinds = [NV if e % 3 else MX for e in range(E)]
+    wl = workloads.grouped_random(seed, T, E, 8, n, 256, kinds=kinds)
+    gd = GroupedDevice(wl)
+    fp4.set_gemm_schedule(fp4.SCHEDULE_SPLITK)
+    try:
+        _, _, o1 = gd.step()
+        _, _, o2 = gd.step()
+    finally:
+        fp4.set_gemm_schedule(fp4.SCHEDULE_AUTO)
+    assert torch.equal(o1, o2)
+    assert not bool(torch.isnan(o1).any())
+    grouped_check(gd, orc, o1)
 
 
 def _few_tokens_case(orc, gd, T, swz):
