@@ -362,6 +362,32 @@ def test_grouped_splitk_tile_groups(orc, seed, T, E, n, ks):
     grouped_check(gd, orc, o1)
 
 
+@pytest.mark.parametrize("seed,T,E,n", [(24, 2, 16, 1592), (25, 16, 128, 200), (26, 16, 128, 1000)],
+                         ids=["ks4", "ks2", "ks1"])
+def test_grouped_splitk_tile_groups_unknown_kind(seed, T, E, n):
+    """The same tile-group launches with one expert of a kind the kernels do not take: all of that
+    expert's outputs (every tile of its groups, ragged tile included) are NaN, the other experts'
+    outputs keep their bits."""
+    wl = workloads.grouped_random(seed, T, E, 8, n, 256, kinds=[NV if e % 3 else MX for e in range(E)])
+    gd = GroupedDevice(wl)
+    counts = np.diff(wl.offsets)
+    bad = int(np.argmax(counts))
+    fp4.set_gemm_schedule(fp4.SCHEDULE_SPLITK)
+    try:
+        codes, scales, good = gd.step()
+        bad_kinds = gd.kinds.clone()
+        bad_kinds[bad] = 6
+        out = fp4.fp4_grouped_gemm(codes, scales, gd.row_ids, gd.offsets, gd.w_ptrs, gd.s_ptrs, bad_kinds,
+                                   gd.scale2, wl.n)
+        torch.cuda.synchronize()
+    finally:
+        fp4.set_gemm_schedule(fp4.SCHEDULE_AUTO)
+    lo, hi = int(wl.offsets[bad]), int(wl.offsets[bad + 1])
+    assert hi > lo
+    assert bool(torch.isnan(out[lo:hi]).all())
+    assert torch.equal(out[:lo], good[:lo]) and torch.equal(out[hi:], good[hi:])
+
+
 def _few_tokens_case(orc, gd, T, swz):
     wl = gd.wl
     row_ids, offsets = workloads.route_topk(wl.logits[:T], 8)
