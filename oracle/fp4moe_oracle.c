@@ -113,26 +113,32 @@ float or_pow2_ceil(float p) {
     return ldexpf(1.0f, e);
 }
 
-/* Per row, per 128-column group: amax of |x| floored at 1e-4, times 1/448 rounded once to f32,
- * rounded up to a power of two -> scale s; code = E4M3(clamp(x / s, -448, 448)).
+/* The step of one block of 128 consecutive activations [GATE: quant_rows, the activation
+ * quantizer]: the largest magnitude in the block, never below the floor 1e-4 (the f32 literal),
+ * times 1/448 rounded once to f32, in one f32 multiply, rounded up to a power of two. */
+static float block_step(const float* v) {
+    float peak = 1e-4f;
+    for (int i = 0; i < 128; ++i) {
+        float m = fabsf(v[i]);
+        if (m > peak) peak = m;
+    }
+    return or_pow2_ceil(peak * (float)(1.0 / 448.0));
+}
+
+/* Activation quantization by its definition: every element of a row is divided by the step of the
+ * 128-column block it sits in, clamped to +-448 and encoded as E4M3; the steps are the scales.
  * x: f32 [rows, k] row-major; codes: u8 [rows, k]; scales: f32 [rows, k/128].  k % 128 == 0. */
 void or_act_quant(const float* x, int64_t rows, int64_t k, uint8_t* codes, float* scales) {
-    const int64_t kq = k / 128;
-    const float inv = (float)(1.0 / 448.0);
-    for (int64_t r = 0; r < rows; ++r) {
-        for (int64_t q = 0; q < kq; ++q) {
-            const float* grp = x + r * k + q * 128;
-            float amax = 0.0f;
-            for (int i = 0; i < 128; ++i) amax = fmaxf(amax, fabsf(grp[i]));
-            amax = fmaxf(amax, 1e-4f);
-            float s = or_pow2_ceil(amax * inv);
-            scales[r * kq + q] = s;
-            for (int i = 0; i < 128; ++i) {
-                float v = grp[i] / s;
-                if (v < -448.0f) v = -448.0f;
-                if (v > 448.0f) v = 448.0f;
-                codes[r * k + q * 128 + i] = (uint8_t)or_e4m3_encode(v);
-            }
+    const int64_t nblk = k / 128;
+    for (int64_t row = 0; row < rows; ++row) {
+        const float* xr = x + row * k;
+        float* step = scales + row * nblk;
+        for (int64_t b = 0; b < nblk; ++b) step[b] = block_step(xr + 128 * b);
+        for (int64_t col = 0; col < k; ++col) {
+            float q = xr[col] / step[col / 128];
+            if (q > 448.0f) q = 448.0f;
+            else if (q < -448.0f) q = -448.0f;
+            codes[row * k + col] = (uint8_t)or_e4m3_encode(q);
         }
     }
 }
@@ -153,33 +159,28 @@ static double weight_scale(int kind, uint8_t sbyte, float scale2) {
     return (double)(float)or_e8m0_value(sbyte);
 }
 
-/* One output (row r, column c) of one expert: ref = sum over k of
- *   E4M3(A[r,k]) * E2M1(W[c,k]) * (ws[c, k/gs] * as[r, k/128])
- * in ascending k, and absp = the same sum of magnitudes.  W is nibble-packed [n, k/2] with even k
- * in the low nibble; S is [n, k/gs] (gs = 16 NVFP4, 32 MXFP4); as is [g, k/128]. */
-static void gemm_one(const uint8_t* a_codes, const float* a_scales, const uint8_t* w,
-                     const uint8_t* s, float scale2, int kind, int64_t k, int64_t r, int64_t c,
-                     double* ref, double* absp) {
+/* One output of one expert, the defining sum written out term by term [GATE: f64_ref]:
+ *   out[r, c] = sum over t < k of  E4M3(A[r, t]) * E2M1(W[c, t]) * (ws(c, t / gs) * as[r, t / 128])
+ * where W[c, t] is the low nibble of byte t/2 of column c's row for even t and the high nibble for
+ * odd t, ws is the weight scale of the group holding t (gs = 16 NVFP4, 32 MXFP4) and as the
+ * activation scale of the 128-block holding t.  Every term is formed in f64 (exact for the
+ * power-of-two activation scales act-quant writes) and the terms are added in ascending t; `mag`
+ * is the same sum of |term|, the scale of the f32 error bound. */
+static void dot_one(const uint8_t* A, const float* AS, const uint8_t* W, const uint8_t* S, float scale2,
+                    int kind, int64_t k, int64_t r, int64_t c, double* sum_out, double* mag_out) {
     const int64_t gs = (kind == OR_NVFP4) ? 16 : 32;
-    const int64_t ngroups = k / gs, kq = k / 128;
-    const uint8_t* arow = a_codes + r * k;
-    const float* asrow = a_scales + r * kq;
-    const uint8_t* wrow = w + c * (k / 2);
-    const uint8_t* srow = s + c * ngroups;
-    double acc = 0.0, aabs = 0.0;
-    for (int64_t j = 0; j < ngroups; ++j) {
-        double sc = weight_scale(kind, srow[j], scale2) * (double)asrow[j * gs / 128];
-        for (int64_t i = 0; i < gs; ++i) {
-            int64_t kk = j * gs + i;
-            uint8_t byte = wrow[kk >> 1];
-            unsigned code = (kk & 1) ? (byte >> 4) : (byte & 0x0Fu);
-            double p = or_e4m3_value(arow[kk]) * or_e2m1_value(code) * sc;
-            acc += p;
-            aabs += fabs(p);
-        }
+    double sum = 0.0, mag = 0.0;
+    for (int64_t t = 0; t < k; ++t) {
+        const double act = or_e4m3_value(A[r * k + t]);
+        const uint8_t pair = W[c * (k / 2) + t / 2];
+        const double wt = or_e2m1_value((t % 2 == 0) ? (pair & 0x0Fu) : (unsigned)(pair >> 4));
+        const double scale = weight_scale(kind, S[c * (k / gs) + t / gs], scale2) * (double)AS[r * (k / 128) + t / 128];
+        const double term = act * wt * scale;
+        sum += term;
+        mag += fabs(term);
     }
-    *ref = acc;
-    *absp = aabs;
+    *sum_out = sum;
+    *mag_out = mag;
 }
 
 typedef struct {
@@ -192,7 +193,7 @@ static void* gemm_rows(void* p) {
     gemm_job* j = (gemm_job*)p;
     for (int64_t r = j->r0; r < j->r1; ++r)
         for (int64_t c = 0; c < j->n; ++c)
-            gemm_one(j->a_codes, j->a_scales, j->w, j->s, j->scale2, j->kind, j->k, r, c,
+            dot_one(j->a_codes, j->a_scales, j->w, j->s, j->scale2, j->kind, j->k, r, c,
                      &j->out[r * j->n + c], &j->absp[r * j->n + c]);
     return NULL;
 }
@@ -223,7 +224,7 @@ void or_expert_gemm_points(const uint8_t* a_codes, const float* a_scales, const 
                            const int64_t* rows, const int64_t* cols, int64_t count,
                            double* out, double* absp) {
     for (int64_t i = 0; i < count; ++i)
-        gemm_one(a_codes, a_scales, w, s, scale2, kind, k, rows[i], cols[i], &out[i], &absp[i]);
+        dot_one(a_codes, a_scales, w, s, scale2, kind, k, rows[i], cols[i], &out[i], &absp[i]);
 }
 
 /* ---------------------------------------------------------------------------------------------
@@ -252,8 +253,8 @@ static void* grouped_rows(void* p) {
         int32_t e = expert_of_row(j->offsets, j->num_experts, r);
         if (e < 0) continue;
         for (int64_t c = 0; c < j->n; ++c) {
-            /* gemm_one indexes A and as by row within the segment; pass the row's own base. */
-            gemm_one(j->a_codes + r * j->k, j->a_scales + r * kq, j->w_ptrs[e], j->s_ptrs[e],
+            /* dot_one indexes A and as by row: pass the row's own base with r = 0. */
+            dot_one(j->a_codes + r * j->k, j->a_scales + r * kq, j->w_ptrs[e], j->s_ptrs[e],
                      j->scale2[e], j->kinds[e], j->k, 0, c, &j->out[(r - j->row0) * j->n + c],
                      &j->absp[(r - j->row0) * j->n + c]);
         }
@@ -296,7 +297,7 @@ void or_grouped_gemm_points(const uint8_t* a_codes, const float* a_scales, const
     for (int64_t i = 0; i < count; ++i) {
         int32_t e = expert_of_row(offsets, num_experts, rows[i]);
         if (e < 0) { out[i] = NAN; absp[i] = NAN; continue; }
-        gemm_one(a_codes + rows[i] * k, a_scales + rows[i] * kq, w_ptrs[e], s_ptrs[e], scale2[e],
+        dot_one(a_codes + rows[i] * k, a_scales + rows[i] * kq, w_ptrs[e], s_ptrs[e], scale2[e],
                  kinds[e], k, 0, cols[i], &out[i], &absp[i]);
     }
 }
