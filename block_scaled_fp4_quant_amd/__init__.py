@@ -42,8 +42,14 @@ def lib() -> ctypes.CDLL:
         L.swiglu_quant_fp8.restype = ctypes.c_int
         L.fp4_expert_gemm.argtypes = [P, P, P, P, F32, I32, P, I32, I32, I32, P]
         L.fp4_expert_gemm.restype = ctypes.c_int
-        L.fp4_grouped_gemm.argtypes = [P, P, I32, P, P, I32, I32, P, P, P, P, P, I32, I32, P]
+        L.fp4_grouped_gemm.argtypes = [P, P, P, I32, I32, P, P, P, P, P, I32, I32, P, ctypes.c_size_t, P]
         L.fp4_grouped_gemm.restype = ctypes.c_int
+        L.fp4_grouped_gemm_workspace_size.argtypes = [I32, I32, I32, I32]
+        L.fp4_grouped_gemm_workspace_size.restype = ctypes.c_size_t
+        L.fp4_grouped_gemm_gather.argtypes = [P, P, I32, P, P, I32, I32, P, P, P, P, P, I32, I32, P]
+        L.fp4_grouped_gemm_gather.restype = ctypes.c_int
+        L.fp4moe_set_debug_checks.argtypes = [I32]
+        L.fp4moe_set_debug_checks.restype = ctypes.c_int
         L.fp4_grouped_gemm_swiglu_quant.argtypes = [P, P, I32, P, P, I32, I32, P, P, P, P, I32, I32, P, F32,
                                                     P, P, P, P]
         L.fp4_grouped_gemm_swiglu_quant.restype = ctypes.c_int
@@ -99,9 +105,26 @@ def set_gemm_schedule(schedule: int) -> None:
     _check(lib().fp4moe_set_gemm_schedule(int(schedule)), "fp4moe_set_gemm_schedule")
 
 
+def set_debug_checks(on: bool) -> None:
+    """Validate every grouped call's tables on the device first (synchronizes; FP4MOE_EDEVICE,
+    raised as Fp4MoeError, when they break the CSR contract); a debugging aid."""
+    _check(lib().fp4moe_set_debug_checks(1 if on else 0), "fp4moe_set_debug_checks")
+
+
+OK, EINVAL, ELAUNCH, EDEVICE = 0, 1, 2, 3
+
+
+class Fp4MoeCallError(Fp4MoeError):
+    """A library call returned a nonzero code (rc: EINVAL, ELAUNCH or EDEVICE)."""
+
+    def __init__(self, msg: str, rc: int):
+        super().__init__(msg)
+        self.rc = rc
+
+
 def _check(rc: int, what: str):
     if rc != 0:
-        raise Fp4MoeError(f"{what} failed (rc={rc}): {lib().fp4moe_last_error().decode()}")
+        raise Fp4MoeCallError(f"{what} failed (rc={rc}): {lib().fp4moe_last_error().decode()}", rc)
 
 
 def _ptr(t):
@@ -246,24 +269,64 @@ def fp4_expert_gemm(a_codes, a_scales, w_packed, w_scales, scale2: float, kind: 
     return out
 
 
-def fp4_grouped_gemm(a_codes, a_scales, row_ids, offsets, w_ptrs, s_ptrs, kinds, scale2, n: int,
-                     out=None, stream=None):
-    """Routed rows packed per expert.  a_codes u8 [a_rows, k], a_scales f32 [a_rows, k/128],
-    row_ids int32 [R] or None, offsets int32 [E+1], w_ptrs/s_ptrs int64 [E] (device addresses),
-    kinds int32 [E] (0/1 NVFP4/MXFP4, | SWIZZLED for swizzled planes), scale2 f32 [E]
-    -> out f32 [R, n] with R = offsets[-1] (read on the host
-    only from `out`'s shape when out is given; otherwise from row_ids' length)."""
-    _dev(a_codes, torch.uint8, "a_codes", 2)
-    _dev(a_scales, torch.float32, "a_scales", 2)
+def _grouped_tables(offsets, w_ptrs, s_ptrs, kinds, scale2):
     _dev(offsets, torch.int32, "offsets", 1)
     _dev(w_ptrs, torch.int64, "w_ptrs", 1)
     _dev(s_ptrs, torch.int64, "s_ptrs", 1)
     _dev(kinds, torch.int32, "kinds", 1)
     _dev(scale2, torch.float32, "scale2", 1)
-    a_rows, k = a_codes.shape
     E = offsets.shape[0] - 1
     if not (w_ptrs.shape[0] == s_ptrs.shape[0] == kinds.shape[0] == scale2.shape[0] == E):
         raise ValueError("per-expert tables must all have num_experts entries")
+    return E
+
+
+def _act_operands(a_codes, a_scales):
+    _dev(a_codes, torch.uint8, "a_codes", 2)
+    _dev(a_scales, torch.float32, "a_scales", 2)
+    a_rows, k = a_codes.shape
+    if k % 128 or a_scales.shape != (a_rows, k // 128):
+        raise ValueError("a_codes must be [rows, k] with k % 128 == 0 and a_scales [rows, k/128]")
+    return a_rows, k
+
+
+def grouped_gemm_workspace_size(num_experts: int, total_rows: int, n: int, k: int) -> int:
+    return int(lib().fp4_grouped_gemm_workspace_size(int(num_experts), int(total_rows), int(n), int(k)))
+
+
+def fp4_grouped_gemm(a_codes, a_scales, offsets, w_ptrs, s_ptrs, kinds, scale2, n: int, out=None,
+                     workspace=None, stream=None):
+    """Routed rows packed per expert (the C ABI's fp4_grouped_gemm).  a_codes u8 [R, k] and
+    a_scales f32 [R, k/128] in packed order, offsets int32 [E+1], w_ptrs/s_ptrs int64 [E] (device
+    addresses), kinds int32 [E] (0/1 NVFP4/MXFP4, | SWIZZLED for swizzled planes), scale2 f32 [E]
+    -> out f32 [R, n].  workspace: a uint8 device tensor of at least grouped_gemm_workspace_size()
+    bytes, or None when that size is 0."""
+    R, k = _act_operands(a_codes, a_scales)
+    E = _grouped_tables(offsets, w_ptrs, s_ptrs, kinds, scale2)
+    if out is None:
+        out = torch.empty((R, n), dtype=torch.float32, device=a_codes.device)
+    _dev(out, torch.float32, "out", 2)
+    if out.shape != (R, n):
+        raise ValueError("out shape must be [total_rows, n]")
+    wbytes = 0
+    if workspace is not None:
+        _dev(workspace, torch.uint8, "workspace", 1)
+        wbytes = workspace.numel()
+    _check(lib().fp4_grouped_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(offsets), E, R, _ptr(w_ptrs),
+                                  _ptr(s_ptrs), _ptr(kinds), _ptr(scale2), _ptr(out), int(n), k,
+                                  _ptr(workspace), wbytes, _stream(stream)),
+           "fp4_grouped_gemm")
+    return out
+
+
+def fp4_grouped_gemm_gather(a_codes, a_scales, row_ids, offsets, w_ptrs, s_ptrs, kinds, scale2, n: int,
+                            out=None, stream=None):
+    """fp4_grouped_gemm with the activations read through a gather table.  a_codes u8 [a_rows, k],
+    a_scales f32 [a_rows, k/128] (e.g. one row per token), row_ids int32 [R] or None, offsets int32
+    [E+1], the per-expert tables as for fp4_grouped_gemm -> out f32 [R, n] with R = offsets[-1]
+    (taken on the host from `out`'s shape when out is given, otherwise from row_ids' length)."""
+    a_rows, k = _act_operands(a_codes, a_scales)
+    E = _grouped_tables(offsets, w_ptrs, s_ptrs, kinds, scale2)
     if row_ids is not None:
         _dev(row_ids, torch.int32, "row_ids", 1)
         R = row_ids.shape[0]
@@ -276,10 +339,10 @@ def fp4_grouped_gemm(a_codes, a_scales, row_ids, offsets, w_ptrs, s_ptrs, kinds,
     _dev(out, torch.float32, "out", 2)
     if out.shape != (R, n):
         raise ValueError("out shape must be [total_rows, n]")
-    _check(lib().fp4_grouped_gemm(_ptr(a_codes), _ptr(a_scales), a_rows, _ptr(row_ids),
-                                  _ptr(offsets), E, R, _ptr(w_ptrs), _ptr(s_ptrs), _ptr(kinds),
-                                  _ptr(scale2), _ptr(out), int(n), k, _stream(stream)),
-           "fp4_grouped_gemm")
+    _check(lib().fp4_grouped_gemm_gather(_ptr(a_codes), _ptr(a_scales), a_rows, _ptr(row_ids),
+                                         _ptr(offsets), E, R, _ptr(w_ptrs), _ptr(s_ptrs), _ptr(kinds),
+                                         _ptr(scale2), _ptr(out), int(n), k, _stream(stream)),
+           "fp4_grouped_gemm_gather")
     return out
 
 
@@ -287,20 +350,11 @@ def fp4_grouped_gemm_swiglu_quant(a_codes, a_scales, row_ids, offsets, w_ptrs, s
                                   inter: int, limit: float, row_weights=None, h_codes=None, h_scales=None,
                                   h_out=None, stream=None):
     """The gate/up projection fused with the expert activation and its FP8 quantization: the
-    arguments of fp4_grouped_gemm (expert planes [2*inter, k/2], gate columns first) plus those of
+    arguments of fp4_grouped_gemm_gather (expert planes [2*inter, k/2], gate columns first) plus those of
     swiglu_quant_fp8 -> (h_codes u8 [R, inter], h_scales f32 [R, inter/128]), R = len(row_ids)
     (or h_codes' rows when row_ids is None).  h_out (f32 [R, inter]) receives h when given."""
-    _dev(a_codes, torch.uint8, "a_codes", 2)
-    _dev(a_scales, torch.float32, "a_scales", 2)
-    _dev(offsets, torch.int32, "offsets", 1)
-    _dev(w_ptrs, torch.int64, "w_ptrs", 1)
-    _dev(s_ptrs, torch.int64, "s_ptrs", 1)
-    _dev(kinds, torch.int32, "kinds", 1)
-    _dev(scale2, torch.float32, "scale2", 1)
-    a_rows, k = a_codes.shape
-    E = offsets.shape[0] - 1
-    if not (w_ptrs.shape[0] == s_ptrs.shape[0] == kinds.shape[0] == scale2.shape[0] == E):
-        raise ValueError("per-expert tables must all have num_experts entries")
+    a_rows, k = _act_operands(a_codes, a_scales)
+    E = _grouped_tables(offsets, w_ptrs, s_ptrs, kinds, scale2)
     inter = int(inter)
     if inter <= 0 or inter % 128:
         raise ValueError("inter must be a positive multiple of 128")

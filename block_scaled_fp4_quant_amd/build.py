@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfp4moe.so")
-SOURCES = ["act_quant.hip", "swiglu_quant.hip", "route.hip", "rung.hip", "w4a4.hip", "swizzle.hip", "gemm_decode.hip", "gemm_skinny.hip", "gemm_prefill.hip", "capi.hip"]
+SOURCES = ["act_quant.hip", "swiglu_quant.hip", "route.hip", "rung.hip", "w4a4.hip", "swizzle.hip", "gemm_decode.hip", "gemm_skinny.hip", "gemm_prefill.hip", "table_check.hip", "capi.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

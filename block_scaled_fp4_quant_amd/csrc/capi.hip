@@ -1,6 +1,7 @@
 // capi.hip -- the extern "C" entry points of libfp4moe (declared and documented in
 // include/fp4moe.h): host-side argument validation, kernel dispatch, per-thread error messages.
 #include <atomic>
+#include <mutex>
 #include <cstdarg>
 #include <cstdio>
 
@@ -67,6 +68,85 @@ hipError_t launch_gemm(const fp4moe::GemmArgs& a, int64_t rows, int64_t experts,
   if (s == FP4MOE_SCHEDULE_AUTO || s == FP4MOE_SCHEDULE_SPLITK)
     s = (rows <= 32 * experts) ? FP4MOE_SCHEDULE_ROWSTREAM : FP4MOE_SCHEDULE_TILED;
   return s == FP4MOE_SCHEDULE_TILED ? fp4moe::launch_gemm_prefill(a, stream) : fp4moe::launch_gemm_decode(a, stream);
+}
+
+// Optional device-side validation of the grouped tables (fp4moe_set_debug_checks).  The status words
+// live in a file-scope device array; host code reaches them only through the address that
+// hipGetSymbolAddress returns for the current device (the array's name is a host-side stand-in).
+__device__ __align__(256) int32_t g_table_status[fp4moe::kTableCheckWords];
+std::atomic<int> g_debug_checks{0};
+std::mutex g_check_mutex;
+constexpr int kMaxDevices = 64;
+int32_t* g_status_ptr[kMaxDevices] = {};
+
+int debug_check_tables(const char* what, const int32_t* offsets, int32_t num_experts, int32_t total_rows,
+                       const int32_t* row_ids, int32_t a_rows, const int32_t* kinds, hipStream_t stream) {
+  if (!g_debug_checks.load(std::memory_order_relaxed)) return FP4MOE_OK;
+  std::lock_guard<std::mutex> lock(g_check_mutex);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FP4MOE_ELAUNCH, "%s: hipGetDevice: %s", what, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FP4MOE_ELAUNCH, "%s: device %d out of range", what, dev);
+  if (!g_status_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_table_status));
+    if (e != hipSuccess || !p)
+      return fail(FP4MOE_ELAUNCH, "%s: hipGetSymbolAddress: %s", what, hipGetErrorString(e));
+    g_status_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  e = fp4moe::launch_table_check(offsets, num_experts, total_rows, row_ids, a_rows, kinds, g_status_ptr[dev], stream);
+  if (e != hipSuccess) return fail(FP4MOE_ELAUNCH, "%s: table check launch: %s", what, hipGetErrorString(e));
+  int32_t st[fp4moe::kTableCheckWords];
+  e = hipMemcpyAsync(st, g_status_ptr[dev], sizeof st, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(FP4MOE_ELAUNCH, "%s: table check readback: %s", what, hipGetErrorString(e));
+  if (st[0] >= 0) return fail(FP4MOE_EDEVICE, "%s: device check: offsets[0] is not 0", what);
+  if (st[1] >= 0)
+    return fail(FP4MOE_EDEVICE, "%s: device check: offsets decrease at expert %d (offsets[%d] < offsets[%d])", what,
+                (int)st[1], (int)st[1] + 1, (int)st[1]);
+  if (st[2] >= 0) return fail(FP4MOE_EDEVICE, "%s: device check: offsets[%d] != total_rows = %d", what, (int)st[2],
+                              (int)total_rows);
+  if (st[3] >= 0)
+    return fail(FP4MOE_EDEVICE, "%s: device check: row_ids[%d] is outside [0, %d)", what, (int)st[3], (int)a_rows);
+  if (st[4] >= 0) return fail(FP4MOE_EDEVICE, "%s: device check: kinds[%d] is not in 0..3", what, (int)st[4]);
+  return FP4MOE_OK;
+}
+
+// The grouped GEMM behind fp4_grouped_gemm (row_ids == nullptr, a_rows == total_rows) and
+// fp4_grouped_gemm_gather.
+int grouped_gemm(const char* what, const uint8_t* a_codes, const float* a_scales, int32_t a_rows,
+                 const int32_t* row_ids, const int32_t* offsets, int32_t num_experts, int32_t total_rows,
+                 const uint64_t* w_ptrs, const uint64_t* s_ptrs, const int32_t* kinds, const float* scale2, float* out,
+                 int32_t n, int32_t k, hipStream_t stream) {
+  if (a_rows < 0 || total_rows < 0)
+    return fail(FP4MOE_EINVAL, "%s: a_rows = %d, total_rows = %d must be >= 0", what, (int)a_rows, (int)total_rows);
+  if (num_experts <= 0) return fail(FP4MOE_EINVAL, "%s: num_experts = %d must be positive", what, (int)num_experts);
+  if (n <= 0) return fail(FP4MOE_EINVAL, "%s: n = %d must be positive", what, (int)n);
+  if (int rc = check_k(k, what)) return rc;
+  if (!row_ids && a_rows < total_rows)
+    return fail(FP4MOE_EINVAL, "%s: row_ids is NULL but a_rows = %d < total_rows = %d", what, (int)a_rows,
+                (int)total_rows);
+  if (total_rows == 0) return ok();
+  if (!a_codes || !a_scales || !offsets || !w_ptrs || !s_ptrs || !kinds || !scale2 || !out)
+    return fail(FP4MOE_EINVAL, "%s: NULL buffer with total_rows > 0", what);
+  if (int rc = check_planes(a_rows, n, k, what)) return rc;
+  if (int rc = debug_check_tables(what, offsets, num_experts, total_rows, row_ids, a_rows, kinds, stream)) return rc;
+  fp4moe::GemmArgs a{};
+  a.a_codes = a_codes;
+  a.a_scales = a_scales;
+  a.row_ids = row_ids;
+  a.a_rows = a_rows;
+  a.offsets = offsets;
+  a.num_experts = num_experts;
+  a.total_rows = total_rows;
+  a.w_ptrs = w_ptrs;
+  a.s_ptrs = s_ptrs;
+  a.kinds = kinds;
+  a.scale2s = scale2;
+  a.out = out;
+  a.n = n;
+  a.k = k;
+  return launched(launch_gemm(a, total_rows, num_experts, stream), what);
 }
 
 }  // namespace
@@ -294,41 +374,34 @@ int fp4_expert_gemm(const uint8_t* a_codes, const float* a_scales, const uint8_t
   return launched(launch_gemm(a, g, 1, stream), "fp4_expert_gemm");
 }
 
-int fp4_grouped_gemm(const uint8_t* a_codes, const float* a_scales, int32_t a_rows,
-                     const int32_t* row_ids, const int32_t* offsets, int32_t num_experts,
-                     int32_t total_rows, const uint64_t* w_ptrs, const uint64_t* s_ptrs,
-                     const int32_t* kinds, const float* scale2, float* out, int32_t n, int32_t k,
+size_t fp4_grouped_gemm_workspace_size(int32_t num_experts, int32_t total_rows, int32_t n, int32_t k) {
+  (void)num_experts;
+  (void)total_rows;
+  (void)n;
+  (void)k;
+  return 0;  // every grouped kernel finds its tiles from the offsets on the device
+}
+
+int fp4_grouped_gemm(const uint8_t* a_codes, const float* a_scales, const int32_t* offsets, int32_t num_experts,
+                     int32_t total_rows, const uint64_t* w_ptrs, const uint64_t* s_ptrs, const int32_t* kinds,
+                     const float* scale2, float* out, int32_t n, int32_t k, void* workspace, size_t workspace_bytes,
                      hipStream_t stream) {
-  if (a_rows < 0 || total_rows < 0)
-    return fail(FP4MOE_EINVAL, "fp4_grouped_gemm: a_rows = %d, total_rows = %d must be >= 0",
-                (int)a_rows, (int)total_rows);
-  if (num_experts <= 0)
-    return fail(FP4MOE_EINVAL, "fp4_grouped_gemm: num_experts = %d must be positive", (int)num_experts);
-  if (n <= 0) return fail(FP4MOE_EINVAL, "fp4_grouped_gemm: n = %d must be positive", (int)n);
-  if (int rc = check_k(k, "fp4_grouped_gemm")) return rc;
-  if (!row_ids && a_rows < total_rows)
-    return fail(FP4MOE_EINVAL, "fp4_grouped_gemm: row_ids is NULL but a_rows = %d < total_rows = %d",
-                (int)a_rows, (int)total_rows);
-  if (total_rows == 0) return ok();
-  if (!a_codes || !a_scales || !offsets || !w_ptrs || !s_ptrs || !kinds || !scale2 || !out)
-    return fail(FP4MOE_EINVAL, "fp4_grouped_gemm: NULL buffer with total_rows > 0");
-  if (int rc = check_planes(a_rows, n, k, "fp4_grouped_gemm")) return rc;
-  fp4moe::GemmArgs a{};
-  a.a_codes = a_codes;
-  a.a_scales = a_scales;
-  a.row_ids = row_ids;
-  a.a_rows = a_rows;
-  a.offsets = offsets;
-  a.num_experts = num_experts;
-  a.total_rows = total_rows;
-  a.w_ptrs = w_ptrs;
-  a.s_ptrs = s_ptrs;
-  a.kinds = kinds;
-  a.scale2s = scale2;
-  a.out = out;
-  a.n = n;
-  a.k = k;
-  return launched(launch_gemm(a, total_rows, num_experts, stream), "fp4_grouped_gemm");
+  const char* what = "fp4_grouped_gemm";
+  if (!workspace && workspace_bytes > 0)
+    return fail(FP4MOE_EINVAL, "%s: workspace is NULL but workspace_bytes = %zu", what, workspace_bytes);
+  const size_t need = fp4_grouped_gemm_workspace_size(num_experts, total_rows, n, k);
+  if (workspace_bytes < need)
+    return fail(FP4MOE_EINVAL, "%s: workspace of %zu bytes, %zu needed", what, workspace_bytes, need);
+  return grouped_gemm(what, a_codes, a_scales, total_rows, nullptr, offsets, num_experts, total_rows, w_ptrs, s_ptrs,
+                      kinds, scale2, out, n, k, stream);
+}
+
+int fp4_grouped_gemm_gather(const uint8_t* a_codes, const float* a_scales, int32_t a_rows, const int32_t* row_ids,
+                            const int32_t* offsets, int32_t num_experts, int32_t total_rows, const uint64_t* w_ptrs,
+                            const uint64_t* s_ptrs, const int32_t* kinds, const float* scale2, float* out, int32_t n,
+                            int32_t k, hipStream_t stream) {
+  return grouped_gemm("fp4_grouped_gemm_gather", a_codes, a_scales, a_rows, row_ids, offsets, num_experts, total_rows,
+                      w_ptrs, s_ptrs, kinds, scale2, out, n, k, stream);
 }
 
 int fp4_grouped_gemm_swiglu_quant(const uint8_t* a_codes, const float* a_scales, int32_t a_rows,
@@ -354,6 +427,7 @@ int fp4_grouped_gemm_swiglu_quant(const uint8_t* a_codes, const float* a_scales,
   if ((reinterpret_cast<uintptr_t>(h_codes) | reinterpret_cast<uintptr_t>(h_out)) & 15)
     return fail(FP4MOE_EINVAL, "%s: h_codes and h_out must be 16-byte aligned", what);
   if (int rc = check_planes(a_rows, 2 * inter, k, what)) return rc;
+  if (int rc = debug_check_tables(what, offsets, num_experts, total_rows, row_ids, a_rows, kinds, stream)) return rc;
   fp4moe::GemmArgs a{};
   a.a_codes = a_codes;
   a.a_scales = a_scales;
@@ -406,6 +480,12 @@ int fp4moe_set_gemm_schedule(int32_t schedule) {
   if (schedule < FP4MOE_SCHEDULE_AUTO || schedule > FP4MOE_SCHEDULE_SPLITK)
     return fail(FP4MOE_EINVAL, "fp4moe_set_gemm_schedule: schedule = %d is not 0, 1, 2 or 3", (int)schedule);
   g_schedule.store(schedule, std::memory_order_relaxed);
+  return ok();
+}
+
+int fp4moe_set_debug_checks(int32_t on) {
+  if (on != 0 && on != 1) return fail(FP4MOE_EINVAL, "fp4moe_set_debug_checks: on = %d is not 0 or 1", (int)on);
+  g_debug_checks.store(on, std::memory_order_relaxed);
   return ok();
 }
 

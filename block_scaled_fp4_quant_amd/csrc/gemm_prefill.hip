@@ -91,6 +91,10 @@ struct ExpertView {
   int kind;
 };
 
+// Per (tile row, thread half): the row uses an activation scale that is not a positive normal power
+// of two (set by scan_act_scales before the main loop, read by the epilogues).
+__shared__ uint8_t s_rowbad[kThreads];
+
 __device__ __forceinline__ int act_row(const GemmArgs& p, int prow) {
   if (!p.row_ids) return prow;
   const int r = p.row_ids[prow];
@@ -357,7 +361,7 @@ __device__ __forceinline__ int tile_col(const GemmArgs& p, int n0, int wave, int
 // swiglu_quant_fp8.  A packed row whose activation row is invalid gets what the unfused route gives
 // the grouped GEMM's NaN output: the activation of NaN gate and up values, in every column.
 constexpr int kHPitch = 128 + 4;                           // floats per row of the t exchange
-template <int NMT>
+template <int NMT, bool ROWCHECK>
 __device__ __forceinline__ void swiglu_epilogue(const GemmArgs& p, int m0, int mrows, int n0, float post,
                                                 f32x16 (&acc)[kMT][kNT], Stage (&st)[2]) {
   static_assert(kNT == 2 && kWaves == 4, "a wavefront holds 32 gate and 32 up columns");
@@ -391,7 +395,7 @@ __device__ __forceinline__ void swiglu_epilogue(const GemmArgs& p, int m0, int m
   if (row < mrows) {
     const int prow = m0 + row;
     const float w = p.swiglu_row_w ? p.swiglu_row_w[prow] : 1.0f;
-    const bool bad = act_row(p, prow) < 0;
+    const bool bad = act_row(p, prow) < 0 || (ROWCHECK && (s_rowbad[2 * row] | s_rowbad[2 * row + 1]));
     const float hbad = swiglu_one(__builtin_nanf(""), __builtin_nanf(""), limit, w);
     const float tmax = fmaxf(hmax[row], hmax[kBM + row]);
     const float amax = fmaxf(bad ? fabsf(hbad) : tmax * fabsf(w), 1e-4f);
@@ -527,7 +531,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
 
   const float post = is_nv(KIND) ? ex.scale2 : 1.0f;
   if (p.swiglu_inter) {
-    swiglu_epilogue<NMT>(p, m0, mrows, n0, post, acc, st);
+    swiglu_epilogue<NMT, KIND != kW4>(p, m0, mrows, n0, post, acc, st);
   } else {
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt)
@@ -537,7 +541,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
         if (row < mrows) {
           const int prow = m0 + row;
           const int arow = act_row(p, prow);
-          const bool bad = arow < 0;
+          const bool bad = arow < 0 || (KIND != kW4 && (s_rowbad[2 * row] | s_rowbad[2 * row + 1]));
           const float rsc = (KIND == kW4 && !bad) ? p.a_row_scale[arow] : 1.0f;
 #pragma unroll
           for (int nt = 0; nt < kNT; ++nt) {
@@ -549,18 +553,24 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
   }
 }
 
-// f16 holds E4M3 x 2^t exactly for every code when 2^-15 <= 2^t <= 2^7 (the smallest code step
-// 2^-9 stays >= f16's 2^-24, and 448 x 2^7 < 65504).  A tile takes the f16 route when the scale of
-// every 128-wide activation block of its rows lies in that range (or is 0: rows not loaded).  Real
-// activations have block scales of 2^-9 .. 2^3; all-zero or tiny blocks fall back to bf16.
-__device__ __forceinline__ bool f16_operands_exact(const GemmArgs& p, int m0, int mrows) {
+// The scan of a tile's activation scales before its main loop (FP8 activations only).
+// - The activation scale is folded into the A operand by the hardware scaled conversion, which
+//   applies only the exponent of its f32 scale: that is exact for the positive normal powers of two
+//   that act_quant_fp8 writes, and wrong for anything else.  A row that uses any other value in any
+//   128-wide block gets s_rowbad[2 row] | s_rowbad[2 row + 1] set, and the epilogue writes it as NaN.
+// - f16 holds E4M3 x 2^t exactly for every code when 2^-15 <= 2^t <= 2^7 (the smallest code step
+//   2^-9 stays >= f16's 2^-24, and 448 x 2^7 < 65504).  The return value says whether the scale of
+//   every 128-wide activation block of the tile's rows lies in that range (or is 0: rows not loaded),
+//   i.e. whether the tile may take the f16 route.  Real activations have block scales of 2^-9 .. 2^3;
+//   all-zero or tiny blocks fall back to bf16.
+__device__ __forceinline__ bool scan_act_scales(const GemmArgs& p, int m0, int mrows) {
   // two threads per row (kThreads = 2 x kBM): thread half h reads blocks 8j + 4h .. +4 with 16-byte
   // loads, all issued before the first test (past the row's end the buffer reads 0, which passes)
   const int nblk = p.k >> 7, row = threadIdx.x >> 1, h = threadIdx.x & 1;
   const int ar = row < mrows ? act_row(p, m0 + row) : -1;
   const rsrc_t r = make_rsrc(p.a_scales, (uint32_t)p.a_rows * (uint32_t)nblk * 4u);
   const uint32_t base = ar >= 0 ? (uint32_t)ar * (uint32_t)nblk * 4u : kOffNone;
-  bool ok = true;
+  bool ok = true, bad = false;
   for (int b0 = 4 * h; b0 < nblk; b0 += 32) {
     f32x4 v[4];
 #pragma unroll
@@ -572,11 +582,16 @@ __device__ __forceinline__ bool f16_operands_exact(const GemmArgs& p, int m0, in
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        // blocks past the row's end read the next row's scales: harmless, the test only gets stricter
+        // blocks past the row's end read the next row's scales: harmless for the f16 test (it only
+        // gets stricter); the power-of-two test skips them
         const float x = v[j][e];
         ok &= x == 0.0f || (x >= 0x1p-15f && x <= 128.0f);
+        const uint32_t bits = f2u(x), ex = bits >> 23;
+        const bool pow2 = (bits & 0x807FFFFFu) == 0u && ex >= 1u && ex <= 254u;
+        bad |= base != kOffNone && b0 + 8 * j + e < nblk && !pow2;
       }
   }
+  s_rowbad[threadIdx.x] = bad ? 1 : 0;
   return __builtin_amdgcn_readfirstlane(__syncthreads_and(ok)) != 0;
 }
 
@@ -591,7 +606,7 @@ __device__ __forceinline__ void nan_tile(const GemmArgs& p, int m0, int mrows, i
       for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) nacc[mt][nt][v] = __builtin_nanf("");
-    swiglu_epilogue<kMT>(p, m0, mrows, n0, 1.0f, nacc, st);
+    swiglu_epilogue<kMT, false>(p, m0, mrows, n0, 1.0f, nacc, st);
     return;
   }
   for (int i = threadIdx.x; i < mrows * kBN; i += kThreads) {
@@ -696,17 +711,18 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_prefill_kernel(GemmArgs p, i
     } else {
       nan_tile(p, m0, mrows, n0, st);
     }
-  } else if (base_kind == kNV) {
-    if (f16_operands_exact(p, m0, mrows)) {
+  } else if (base_kind == kNV || base_kind == kMX) {
+    const bool f16_ok = scan_act_scales(p, m0, mrows);
+    if (base_kind == kMX) {
+      if (swz) run_tile<kMX, 4, true>(p, ex, m0, mrows, n0, st);
+      else run_tile<kMX, 4, false>(p, ex, m0, mrows, n0, st);
+    } else if (f16_ok) {
       if (swz) run_tile_nv16<true>(p, ex, m0, mrows, nmt, n0, st);
       else run_tile_nv16<false>(p, ex, m0, mrows, nmt, n0, st);
     } else {
       if (swz) run_tile<kNV, 4, true>(p, ex, m0, mrows, n0, st);
       else run_tile<kNV, 4, false>(p, ex, m0, mrows, n0, st);
     }
-  } else if (base_kind == kMX) {
-    if (swz) run_tile<kMX, 4, true>(p, ex, m0, mrows, n0, st);
-    else run_tile<kMX, 4, false>(p, ex, m0, mrows, n0, st);
   } else {
     nan_tile(p, m0, mrows, n0, st);
   }

@@ -111,4 +111,12 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);
 // Tiled matrix-core kernel for many rows per expert (prefill): 128 x 256 output tiles.
 hipError_t launch_gemm_prefill(const GemmArgs& a, hipStream_t stream);
 
+// Validation of a grouped call's tables (table_check.hip), one workgroup: status[i] (int32,
+// kTableCheckWords of them) receives the smallest index violating condition i, or -1:
+// 0 offsets[0] != 0; 1 offsets[e+1] < offsets[e]; 2 offsets[E] != total_rows; 3 row_ids[p] outside
+// [0, a_rows) (row_ids may be null); 4 kinds[e] outside 0..3.
+constexpr int kTableCheckWords = 5;
+hipError_t launch_table_check(const int32_t* offsets, int32_t num_experts, int32_t total_rows, const int32_t* row_ids,
+                              int32_t a_rows, const int32_t* kinds, int32_t* status, hipStream_t stream);
+
 }  // namespace fp4moe

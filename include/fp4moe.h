@@ -25,8 +25,10 @@
  *     synchronizes.  Each call only enqueues kernels on `stream` (0 = the null stream) and returns.
  *   - Sizes are int32.  Arguments are validated on the host before anything is enqueued.
  *   - Return value: FP4MOE_OK (0) on success; FP4MOE_EINVAL for an invalid argument (nothing was
- *     enqueued); FP4MOE_ELAUNCH when the HIP runtime reports a launch error.  fp4moe_last_error()
- *     then holds a message (per thread).
+ *     enqueued); FP4MOE_ELAUNCH when the HIP runtime reports a launch error; FP4MOE_EDEVICE when
+ *     the optional device-side table check (fp4moe_set_debug_checks) finds a grouped call's
+ *     tables invalid (nothing but the check was enqueued).  fp4moe_last_error() then holds a
+ *     message (per thread).
  *   - Calls that write the same output buffer, or whose inputs another call writes, race unless
  *     the caller orders them (same stream or events).
  */
@@ -50,7 +52,7 @@ extern "C" {
 /* Weight formats (the pages' kind codes), plus a layout flag OR'ed into them: kinds 2 and 3 are
  * NVFP4 and MXFP4 planes in the swizzled layout written by fp4_weight_swizzle. */
 enum { FP4MOE_NVFP4 = 0, FP4MOE_MXFP4 = 1, FP4MOE_SWIZZLED = 2 };
-enum { FP4MOE_OK = 0, FP4MOE_EINVAL = 1, FP4MOE_ELAUNCH = 2 };
+enum { FP4MOE_OK = 0, FP4MOE_EINVAL = 1, FP4MOE_ELAUNCH = 2, FP4MOE_EDEVICE = 3 };
 
 /*
  * act_quant_fp8 -- [GATE: quant_rows].  For every row r and every group q of 128 columns:
@@ -73,7 +75,9 @@ FP4MOE_API int act_quant_fp8(const float* x, uint8_t* codes, float* scales, int3
  *                 E4M3(a_codes[r, k]) * E2M1(nibble(w_packed, c, k)) ) * ws[c, j] * a_scales[r, k/128]
  * with gs = 16 and ws = E4M3(w_scales[c, j]) * scale2 for NVFP4 (kind 0), gs = 32 and
  * ws = 2^(w_scales[c, j] - 127) for MXFP4 (kind 1; scale2 ignored), accumulated in f32.
- * a_codes:  u8  [g, k] E4M3 bytes;  a_scales: f32 [g, k/128].
+ * a_codes:  u8  [g, k] E4M3 bytes;  a_scales: f32 [g, k/128], positive normal powers of two as
+ *           act_quant_fp8 writes them (a call with more than 16 rows may run the tiled kernel,
+ *           which writes NaN for a row using any other value; see fp4_grouped_gemm_gather).
  * w_packed: u8  [n, k/2]: element (c, k) is the low nibble of byte (c, k/2) for even k, the high
  *           nibble for odd k.
  * w_scales: u8  [n, k/16] E4M3 (NVFP4) or [n, k/32] E8M0 (MXFP4).
@@ -92,31 +96,60 @@ FP4MOE_API int fp4_expert_gemm(const uint8_t* a_codes, const float* a_scales, co
                     int32_t n, int32_t k, hipStream_t stream);
 
 /*
- * fp4_grouped_gemm -- [CHECK: f16g grouped GEMM, CSR offsets; GATE: f64_ref per expert].
+ * fp4_grouped_gemm -- [CHECK: f16g grouped GEMM, CSR offsets; GATE: f64_ref per expert, and the
+ * FFI calls in `main` (a workspace passed explicitly, rc 0 = success)].
  * Routed rows packed per expert: packed row p belongs to expert e when
- * offsets[e] <= p < offsets[e+1], and its activation is row row_ids[p] of a_codes/a_scales (row p
- * itself when row_ids is NULL).  out[p, :] is fp4_expert_gemm of that activation row with expert
+ * offsets[e] <= p < offsets[e+1], and out[p, :] is fp4_expert_gemm of activation row p with expert
  * e's planes, format and scale2.  Experts with no rows cost nothing; both formats may be mixed.
- * a_codes:  u8  [a_rows, k];  a_scales: f32 [a_rows, k/128]  (e.g. one row per token).
- * row_ids:  int32 [total_rows] indices into [0, a_rows), or NULL (then a_rows >= total_rows).
+ * a_codes:  u8  [total_rows, k];  a_scales: f32 [total_rows, k/128], packed in the same row order.
  * offsets:  int32 [num_experts + 1], offsets[0] = 0, non-decreasing, offsets[E] = total_rows.
+ * total_rows: [host] the packed row count (== offsets[E]; the host never reads offsets).
  * w_ptrs, s_ptrs: u64 [num_experts] device addresses of expert e's w_packed [n, k/2] and
  *           w_scales [n, k/gs] planes.
  * kinds:    int32 [num_experts] (0 NVFP4, 1 MXFP4; 2 and 3 the same formats with swizzled
  *           planes, see fp4_weight_swizzle);  scale2: f32 [num_experts] (NVFP4 only).
  * out:      f32 [total_rows, n], every row overwritten.
+ * workspace, workspace_bytes: device scratch of at least fp4_grouped_gemm_workspace_size(...) bytes
+ *           (currently 0: NULL with 0 bytes is valid).  Owned by the caller.
  * All tables are read on the device only.  Out-of-range table entries never cause an
- * out-of-bounds access: offsets are clamped to [0, total_rows]; a row whose row_ids entry is
- * outside [0, a_rows), or whose expert has a kind outside 0..3, is written as NaN.
+ * out-of-bounds access: offsets are clamped to [0, total_rows]; a row whose expert has a kind
+ * outside 0..3 is written as NaN.  With fp4moe_set_debug_checks(1) the tables are first validated
+ * on the device (offsets[0] = 0, non-decreasing, offsets[E] = total_rows, kinds in 0..3): the call
+ * then synchronizes `stream` and returns FP4MOE_EDEVICE, without launching the GEMM, when they fail.
+ * a_scales are powers of two, as act_quant_fp8 writes them (see fp4_grouped_gemm_gather).
+ * Errors: EINVAL if total_rows < 0, num_experts <= 0, n <= 0, k <= 0, k % 128 != 0, a pointer is
+ * NULL while total_rows > 0, workspace is NULL with workspace_bytes > 0, workspace_bytes is below
+ * the required size, or total_rows*k or ceil(n/16)*16*k/2 is 2^31 or more.  total_rows == 0 is a
+ * no-op.
+ */
+FP4MOE_API size_t fp4_grouped_gemm_workspace_size(int32_t num_experts, int32_t total_rows, int32_t n, int32_t k);
+FP4MOE_API int fp4_grouped_gemm(const uint8_t* a_codes, const float* a_scales, const int32_t* offsets,
+                                int32_t num_experts, int32_t total_rows, const uint64_t* w_ptrs,
+                                const uint64_t* s_ptrs, const int32_t* kinds, const float* scale2, float* out,
+                                int32_t n, int32_t k, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/*
+ * fp4_grouped_gemm_gather -- fp4_grouped_gemm with the activation rows read through a gather table,
+ * so that act_quant_fp8 runs once per token instead of once per routed (token, expert) pair:
+ * packed row p's activation is row row_ids[p] of a_codes/a_scales (row p itself when row_ids is
+ * NULL).  Same definition, tables, output and debug check as fp4_grouped_gemm; no workspace.
+ * a_codes:  u8  [a_rows, k];  a_scales: f32 [a_rows, k/128]  (e.g. one row per token).
+ * row_ids:  int32 [total_rows] indices into [0, a_rows), or NULL (then a_rows >= total_rows).
+ * A row whose row_ids entry is outside [0, a_rows) is written as NaN (the debug check reports it).
+ * a_scales must be positive normal powers of two (act_quant_fp8 writes nothing else): the tiled
+ * kernel that runs rows of experts holding many rows folds each scale into the activation operand
+ * by its exponent and writes NaN for a row that uses any other value in a group it reads; the
+ * other kernels apply any f32 value.
  * Errors: EINVAL if a_rows < 0, total_rows < 0, num_experts <= 0, n <= 0, k <= 0, k % 128 != 0,
  * row_ids is NULL while a_rows < total_rows, a pointer is NULL while total_rows > 0, or a_rows*k
  * or ceil(n/16)*16*k/2 is 2^31 or more.  total_rows == 0 is a no-op.
  */
-FP4MOE_API int fp4_grouped_gemm(const uint8_t* a_codes, const float* a_scales, int32_t a_rows,
-                     const int32_t* row_ids, const int32_t* offsets, int32_t num_experts,
-                     int32_t total_rows, const uint64_t* w_ptrs, const uint64_t* s_ptrs,
-                     const int32_t* kinds, const float* scale2, float* out, int32_t n, int32_t k,
-                     hipStream_t stream);
+FP4MOE_API int fp4_grouped_gemm_gather(const uint8_t* a_codes, const float* a_scales, int32_t a_rows,
+                                       const int32_t* row_ids, const int32_t* offsets, int32_t num_experts,
+                                       int32_t total_rows, const uint64_t* w_ptrs, const uint64_t* s_ptrs,
+                                       const int32_t* kinds, const float* scale2, float* out, int32_t n,
+                                       int32_t k, hipStream_t stream);
 
 /*
  * fp4_weight_swizzle -- a load-time reordering of one expert's planes ([GATE: ExpertRaw] values,
@@ -168,18 +201,18 @@ FP4MOE_API int swiglu_quant_fp8(const float* gu, const float* row_weights, float
  * fp4_grouped_gemm_swiglu_quant -- [CHECK: f16g grouped GEMM; GATE: the swiglu_limit saturation cell,
  * then quant_rows].  The gate/up projection of the routed rows with the expert activation and its
  * FP8 quantization applied before anything is written: the result is bit-identical to
- *   gu = fp4_grouped_gemm(..., n = 2*inter, ...)   (the tiled schedule)
+ *   gu = fp4_grouped_gemm_gather(..., n = 2*inter, ...)   (the tiled schedule)
  *   swiglu_quant_fp8(gu, row_weights, limit, h_codes, h_scales, h_out, total_rows, inter)
  * without the f32 [total_rows, 2*inter] intermediate.  Expert planes are [2*inter, k/2] (gate columns
- * first, then up), as for fp4_grouped_gemm with n = 2*inter.  A packed row whose row_ids entry is
+ * first, then up), as for fp4_grouped_gemm_gather with n = 2*inter.  A packed row whose row_ids entry is
  * out of range, or whose expert has a kind outside 0..3, enters the activation as NaN gate and up
  * values, exactly as the unfused route's NaN GEMM output would.
- * Arguments as for fp4_grouped_gemm and swiglu_quant_fp8:
+ * Arguments as for fp4_grouped_gemm_gather (debug check included) and swiglu_quant_fp8:
  * row_weights: f32 [total_rows] or NULL (per packed row);  limit: [host] f32 > 0 (+Inf: no clamp).
  * h_codes:     u8  [total_rows, inter], 16-byte aligned, written.
  * h_scales:    f32 [total_rows, inter/128], written.
  * h_out:       f32 [total_rows, inter], 16-byte aligned, or NULL: receives h when given.
- * Errors: EINVAL on the conditions of fp4_grouped_gemm (with n = 2*inter), inter not a positive
+ * Errors: EINVAL on the conditions of fp4_grouped_gemm_gather (with n = 2*inter), inter not a positive
  * multiple of 128 up to 2^29, limit not > 0, or a misaligned h_codes/h_out.  total_rows == 0 is a
  * no-op.
  */
@@ -223,7 +256,7 @@ FP4MOE_API int64_t route_pack_workspace_size(int32_t tokens, int32_t experts);
  * pairs p = t * top_k + j of a routing table are packed per expert: expert e owns the packed rows
  * offsets[e] .. offsets[e+1]-1, experts in ascending id, and inside one expert the pairs in
  * ascending (t, j) order, i.e. ascending token order.  Pairs whose id lies outside [0, experts) are
- * dropped.  The outputs feed fp4_grouped_gemm (row_ids gathers the activation rows, offsets delimits
+ * dropped.  The outputs feed fp4_grouped_gemm_gather (row_ids gathers the activation rows, offsets delimits
  * the experts) and moe_combine (pair_rows).
  * topk_ids:     int32 [tokens, top_k], read only (ids of one token may repeat; each pair is a row).
  * topk_weights: f32 [tokens, top_k] or NULL, read only.
@@ -246,7 +279,7 @@ FP4MOE_API int route_pack(const int32_t* topk_ids, const float* topk_weights, in
  * gather_quant_rows -- [CHECK: f16g grouped GEMM section; the packed activation rows].  Copies the
  * act-quant rows row_ids[p] into packed row p: out_codes[p, :] = codes[row_ids[p], :] and
  * out_scales[p, :] = scales[row_ids[p], :].  A row id outside [0, a_rows) gives zero code bytes and
- * NaN scales.  fp4_grouped_gemm reads through row_ids itself; this call builds a contiguous copy
+ * NaN scales.  fp4_grouped_gemm_gather reads through row_ids itself; this call builds a contiguous copy
  * (e.g. a send buffer of routed rows).
  * codes:  u8 [a_rows, k], scales: f32 [a_rows, k/128], read only.  row_ids: int32 [rows].
  * out_codes: u8 [rows, k], out_scales: f32 [rows, k/128], written.
@@ -263,7 +296,7 @@ FP4MOE_API int gather_quant_rows(const uint8_t* codes, const float* scales, int3
  * added in j order, one f32 fused multiply-add per term (a plain f32 add when pair_weights is NULL,
  * i.e. w = 1).  Pairs with pair_rows < 0 are skipped; a row at or past y_rows makes the token's whole
  * output row NaN.  Deterministic: no atomics.
- * y:            f32 [y_rows, n], read only (e.g. fp4_grouped_gemm's packed output).
+ * y:            f32 [y_rows, n], read only (e.g. the grouped GEMM's packed output).
  * pair_rows:    int32 [tokens, top_k], read only (route_pack's output).
  * pair_weights: f32 [tokens, top_k] or NULL.
  * out:          f32 [tokens, n], written.
@@ -365,6 +398,19 @@ FP4MOE_API int w4a4_gemm(const uint8_t* a_codes, const uint8_t* a_micro, const f
 enum { FP4MOE_SCHEDULE_AUTO = 0, FP4MOE_SCHEDULE_ROWSTREAM = 1, FP4MOE_SCHEDULE_TILED = 2,
        FP4MOE_SCHEDULE_SPLITK = 3 };
 FP4MOE_API int fp4moe_set_gemm_schedule(int32_t schedule);
+
+/*
+ * fp4moe_set_debug_checks -- a debugging aid (not part of the method).  With on = 1, every grouped
+ * call (fp4_grouped_gemm, fp4_grouped_gemm_gather, fp4_grouped_gemm_swiglu_quant) first runs a
+ * one-workgroup kernel that validates its tables on the device -- offsets[0] = 0, offsets
+ * non-decreasing, offsets[E] = total_rows, every row_ids entry in [0, a_rows), every kind in 0..3 --
+ * then synchronizes `stream` and returns FP4MOE_EDEVICE, with the first violation in
+ * fp4moe_last_error(), instead of launching the GEMM.  The check's status words are library-owned
+ * device memory (one small array per device, shared by all calls on it; calls from several host
+ * threads are serialized by a lock).  on = 0 (the default) removes the check and the
+ * synchronization.  Process-wide.  Errors: EINVAL for any other value.
+ */
+FP4MOE_API int fp4moe_set_debug_checks(int32_t on);
 
 /* Message for the last nonzero return code of a call made by this thread ("" if none). */
 FP4MOE_API const char* fp4moe_last_error(void);

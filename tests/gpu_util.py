@@ -41,7 +41,7 @@ class GroupedDevice:
     def step(self, out=None, codes=None, scales=None):
         """act_quant of the token rows, then the grouped GEMM over the packed rows."""
         codes, scales = fp4.act_quant_fp8(self.x, codes, scales)
-        out = fp4.fp4_grouped_gemm(codes, scales, self.row_ids, self.offsets, self.w_ptrs,
+        out = fp4.fp4_grouped_gemm_gather(codes, scales, self.row_ids, self.offsets, self.w_ptrs,
                                    self.s_ptrs, self.kinds, self.scale2, self.n, out=out)
         return codes, scales, out
 

@@ -43,3 +43,60 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+@pytest.fixture(scope="module")
+def config4_wl():
+    return workloads.config4()
+
+
+def test_prefill_step_algorithmic_bytes_and_flops(config4_wl):
+    wl = config4_wl
+    alg = bench.algorithmic_bytes(wl)
+    # 255 NVFP4 experts of [4096, 7168/2] nibbles + [4096, 7168/16] E4M3 scales + scale2, and one
+    # MXFP4 expert with [4096, 7168/32] E8M0 scales
+    assert alg["weights"] == 255 * (4096 * 3584 + 4096 * 448 + 4) + (4096 * 3584 + 4096 * 224) == 4_226_941_948
+    assert wl.R == 65536 and 2.0 * wl.R * wl.k * wl.n == pytest.approx(3.848e12, rel=1e-3)
+
+
+def _fake_measure(gemm_ms, step_ms):
+    return {"step_ms": step_ms, "wall_ms": step_ms, "aq_ms": 0.01, "gemm_ms": gemm_ms, "gemm_ms_min": gemm_ms,
+            "gemm_pct": {"p10": gemm_ms * 1e3, "p50": gemm_ms * 1e3, "p90": gemm_ms * 1e3}}
+
+
+class _Args:
+    tokens = 0
+    layout = "swizzled"
+    steps = 20
+
+
+def test_half_results(config4_wl):
+    """Each half's roofline: achieved = algorithmic bytes (decode) or flops (prefill) over the GEMM's
+    mean event time, frac = achieved / the published peak; the prefill half also against 5 PFLOP/s."""
+    wl3 = workloads.config3()
+    d = bench.half_result("config3", wl3, _fake_measure(0.35, 0.36), _Args, {"x": "0"})
+    assert d["unit"] == "TB/s" and d["roofline"]["bound"] == "hbm"
+    assert d["roofline"]["achieved"] == pytest.approx(2_151_292_932 / 0.35e-3 / 1e9, abs=0.1)
+    assert d["roofline"]["frac"] == pytest.approx(d["roofline"]["achieved"] / 8000.0, abs=1e-4)
+    assert d["value"] == pytest.approx(2_113_930_240 / 0.36e-3 / 1e12, abs=1e-4)
+    p = bench.half_result("config4", config4_wl, _fake_measure(3.8, 3.9), _Args, {"x": "0"})
+    tf = 2.0 * 65536 * 7168 * 4096 / 3.8e-3 / 1e12
+    assert p["unit"] == "TFLOP/s" and p["roofline"]["bound"] == "mfma"
+    assert p["roofline"]["achieved"] == pytest.approx(tf, abs=0.1)
+    assert p["roofline"]["frac"] == pytest.approx(tf / 2500.0, abs=1e-4)
+    assert p["roofline_fp8"]["frac"] == pytest.approx(tf / 5000.0, abs=1e-4)
+
+
+def test_input_hashes_are_stable():
+    a, b = workloads.config0(), workloads.config0()
+    wl = workloads.grouped_random(3, 20, 4, 2, 32, 128)
+    h1 = bench.input_hashes(wl)
+    h2 = bench.input_hashes(workloads.grouped_random(3, 20, 4, 2, 32, 128))
+    assert h1 == h2 and set(h1) >= {"x", "row_ids", "offsets", "w_bank", "s_bank"}
+    assert all(len(v) == 64 for v in h1.values())
+    assert a.x.tobytes() == b.x.tobytes()
+
+
+def test_cpu_model_names_the_host():
+    m = bench.cpu_model()
+    assert "logical CPUs available" in m and "family" in m

@@ -156,7 +156,7 @@ def test_grouped_without_row_ids(orc, schedule):
     gd = GroupedDevice(wl)
     codes, scales = fp4.act_quant_fp8(gd.x)
     pc, ps = codes[gd.row_ids.long()].contiguous(), scales[gd.row_ids.long()].contiguous()
-    out = fp4.fp4_grouped_gemm(pc, ps, None, gd.offsets, gd.w_ptrs, gd.s_ptrs, gd.kinds,
+    out = fp4.fp4_grouped_gemm_gather(pc, ps, None, gd.offsets, gd.w_ptrs, gd.s_ptrs, gd.kinds,
                                gd.scale2, wl.n, out=torch.empty((wl.R, wl.n), device=pc.device))
     _, _, ref_out = gd.step()
     assert torch.equal(out, ref_out)
@@ -171,7 +171,7 @@ def test_grouped_invalid_entries_give_nan(orc, schedule):
     bad_ids[5] = -1
     bad_kinds = gd.kinds.clone()
     bad_kinds[2] = 7
-    out = fp4.fp4_grouped_gemm(codes, scales, bad_ids, gd.offsets, gd.w_ptrs, gd.s_ptrs, bad_kinds,
+    out = fp4.fp4_grouped_gemm_gather(codes, scales, bad_ids, gd.offsets, gd.w_ptrs, gd.s_ptrs, bad_kinds,
                                gd.scale2, wl.n)
     torch.cuda.synchronize()
     nan_rows = {3, 5} | set(range(int(wl.offsets[2]), int(wl.offsets[3])))
@@ -191,7 +191,7 @@ def test_grouped_offsets_are_clamped(orc, schedule):
     offs[2] = offs[2] + 10 ** 6                # expert 1 now claims rows past the end
     sentinel = torch.full((wl.R + 8, wl.n), 123.0, device=codes.device)
     out = sentinel[:wl.R]
-    fp4.fp4_grouped_gemm(codes, scales, gd.row_ids, offs, gd.w_ptrs, gd.s_ptrs, gd.kinds, gd.scale2,
+    fp4.fp4_grouped_gemm_gather(codes, scales, gd.row_ids, offs, gd.w_ptrs, gd.s_ptrs, gd.kinds, gd.scale2,
                          wl.n, out=out)
     torch.cuda.synchronize()
     assert bool((sentinel[wl.R:] == 123.0).all())
@@ -229,6 +229,33 @@ def test_config3_sampled(orc, config3_dev):
     print(f"config3 worst err / (2^-24 sum|p|) over {rows.size} samples = {worst:.2f}")
 
 
+@pytest.fixture(scope="module")
+def config3_full(orc, config3_dev):
+    """The decode step as the benchmark runs it (swizzled planes, the automatic schedule), and the
+    oracle's act-quant of its tokens."""
+    gd = config3_dev
+    w_ptrs, s_ptrs, kinds, _ = _swizzled_planes(gd)
+    codes, scales = fp4.act_quant_fp8(gd.x)
+    out = fp4.fp4_grouped_gemm_gather(codes, scales, gd.row_ids, gd.offsets, w_ptrs, s_ptrs, kinds, gd.scale2, gd.n)
+    rc, rs = orc.act_quant(gd.wl.x)
+    assert np.array_equal(codes.cpu().numpy(), rc) and np.array_equal(scales.cpu().numpy(), rs)
+    return out.cpu().numpy(), rc[gd.wl.row_ids], rs[gd.wl.row_ids]
+
+
+@pytest.mark.parametrize("quarter", [0, 1, 2, 3])
+def test_config3_every_output(orc, config3_dev, config3_full, quarter):
+    """Every one of the 4096 x 2048 outputs of the decode step against the oracle, a quarter of the
+    256 experts per case (each case streams its experts' packed rows through the f64 oracle)."""
+    gd, (got, pc, ps) = config3_dev, config3_full
+    wl = gd.wl
+    e0, e1 = 64 * quarter, 64 * quarter + 64
+    r0, r1 = int(wl.offsets[e0]), int(wl.offsets[e1])
+    ref, absp = orc.grouped_gemm(pc, ps, wl.offsets, [wl.w_of(e) for e in range(wl.E)],
+                                 [wl.s_of(e) for e in range(wl.E)], wl.kinds, wl.scale2, wl.n, row0=r0, row1=r1)
+    worst = check_bound(got[r0:r1], ref, absp, wl.k, f"config3 experts {e0}..{e1 - 1}")   # ref: rows r0..r1
+    print(f"config3 experts {e0}..{e1 - 1}: {r1 - r0} rows x {wl.n}, worst err / (2^-24 sum|p|) = {worst:.2f}")
+
+
 def test_schedules_agree_within_bound(orc):
     """The two kernels on the same large-row grouped input: both within the bound of the oracle,
     each bit-reproducible run to run."""
@@ -247,18 +274,39 @@ def test_schedules_agree_within_bound(orc):
         outs.append(o1)
 
 
+def _config4_tile_points(wl, seed):
+    """Output coordinates that touch every (expert, 128-row slice, 256-column slice) tile of the tiled
+    kernel once, plus every row of each expert's last, partial row slice (one column each)."""
+    rng = np.random.default_rng(seed)
+    rows, cols = [], []
+    for e in range(wl.E):
+        lo, hi = int(wl.offsets[e]), int(wl.offsets[e + 1])
+        for m0 in range(lo, hi, 128):
+            m1 = min(m0 + 128, hi)
+            for c0 in range(0, wl.n, 256):
+                rows.append(int(rng.integers(m0, m1)))
+                cols.append(int(rng.integers(c0, min(c0 + 256, wl.n))))
+            if m1 - m0 < 128:
+                rows.extend(range(m0, m1))
+                cols.extend(rng.integers(0, wl.n, m1 - m0).tolist())
+    return np.array(rows, np.int64), np.array(cols, np.int64)
+
+
 def test_config4_sampled(orc, config4_dev):
+    """The prefill step at full size: every tile of every expert (the MXFP4 expert included) and every
+    row of each expert's last partial row slice, against the oracle point by point; plus random
+    outputs."""
     gd = config4_dev
     _, _, out = gd.step()
     assert not bool(torch.isnan(out).any())
-    rows, cols = _sample(gd.R, gd.n, 16384, 4)
-    # include rows of the MXFP4 expert (the last one)
+    tr, tc = _config4_tile_points(gd.wl, 40)
+    rr, rcol = _sample(gd.R, gd.n, 4096, 4)
+    rows, cols = np.concatenate([tr, rr]), np.concatenate([tc, rcol])
     lo, hi = int(gd.wl.offsets[-2]), int(gd.wl.offsets[-1])
-    if hi > lo:
-        rows = np.concatenate([rows, np.arange(lo, hi)[:64]])
-        cols = np.concatenate([cols, (np.arange(lo, hi)[:64] * 37) % gd.n])
+    assert hi > lo and np.any((rows >= lo) & (rows < hi))        # the MXFP4 expert is covered
     worst = grouped_check(gd, orc, out, (rows, cols))
-    print(f"config4 worst err / (2^-24 sum|p|) over {rows.size} samples = {worst:.2f}")
+    print(f"config4 worst err / (2^-24 sum|p|) over {rows.size} points "
+          f"({tr.size} covering every tile and partial-slice row) = {worst:.2f}")
 
 
 @pytest.mark.parametrize("factor", [1.0, 1e-5, 3e5])
@@ -377,7 +425,7 @@ def test_grouped_splitk_tile_groups_unknown_kind(seed, T, E, n):
         codes, scales, good = gd.step()
         bad_kinds = gd.kinds.clone()
         bad_kinds[bad] = 6
-        out = fp4.fp4_grouped_gemm(codes, scales, gd.row_ids, gd.offsets, gd.w_ptrs, gd.s_ptrs, bad_kinds,
+        out = fp4.fp4_grouped_gemm_gather(codes, scales, gd.row_ids, gd.offsets, gd.w_ptrs, gd.s_ptrs, bad_kinds,
                                    gd.scale2, wl.n)
         torch.cuda.synchronize()
     finally:
@@ -398,8 +446,8 @@ def _few_tokens_case(orc, gd, T, swz):
         w_ptrs, s_ptrs, kinds, keep = _swizzled_planes(gd)
     else:
         w_ptrs, s_ptrs, kinds, keep = gd.w_ptrs, gd.s_ptrs, gd.kinds, None
-    o1 = fp4.fp4_grouped_gemm(codes, scales, rid, offs, w_ptrs, s_ptrs, kinds, gd.scale2, wl.n)
-    o2 = fp4.fp4_grouped_gemm(codes, scales, rid, offs, w_ptrs, s_ptrs, kinds, gd.scale2, wl.n)
+    o1 = fp4.fp4_grouped_gemm_gather(codes, scales, rid, offs, w_ptrs, s_ptrs, kinds, gd.scale2, wl.n)
+    o2 = fp4.fp4_grouped_gemm_gather(codes, scales, rid, offs, w_ptrs, s_ptrs, kinds, gd.scale2, wl.n)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
     rc, rs = orc.act_quant(x)
@@ -433,11 +481,12 @@ def _swizzled_planes(gd):
     return _SWZ_CACHE[key]
 
 
-@pytest.mark.parametrize("schedule_id", [fp4.SCHEDULE_AUTO, fp4.SCHEDULE_ROWSTREAM])
+@pytest.mark.parametrize("schedule_id", [fp4.SCHEDULE_SPLITK, fp4.SCHEDULE_ROWSTREAM], ids=["splitk", "rowstream"])
 def test_grouped_multipass_few_experts(orc, schedule_id):
     """40 tokens over 2 experts at top-1 (about 20 rows per expert, over the split-k kernel's
-    16-row pass) and ragged n, k: within the bound under the automatic (split-k) and the
-    row-streaming schedule; invalid row ids and kinds give NaN rows."""
+    16-row pass, so forced split-k runs two passes per expert; the automatic schedule would pick the
+    row-streaming kernel for 40 packed rows) and ragged n, k: within the bound under forced split-k
+    and under the row-streaming schedule; invalid row ids and kinds give NaN rows."""
     wl = workloads.grouped_random(24, 40, 2, 1, 200, 640, kinds=[NV, MX])
     gd = GroupedDevice(wl)
     fp4.set_gemm_schedule(schedule_id)
@@ -447,7 +496,7 @@ def test_grouped_multipass_few_experts(orc, schedule_id):
         bad_ids[3] = -5
         bad_kinds = gd.kinds.clone()
         bad_kinds[1] = 9
-        bad = fp4.fp4_grouped_gemm(codes, scales, bad_ids, gd.offsets, gd.w_ptrs, gd.s_ptrs, bad_kinds,
+        bad = fp4.fp4_grouped_gemm_gather(codes, scales, bad_ids, gd.offsets, gd.w_ptrs, gd.s_ptrs, bad_kinds,
                                    gd.scale2, wl.n)
         torch.cuda.synchronize()
     finally:

@@ -251,10 +251,10 @@ def test_expert_layer_from_logits(orc, schedule, seed, T, E, top, hidden, inter,
     offsets, row_ids, pair_rows, row_w = fp4.route_pack(ids, E, w)
     codes_x, scales_x = fp4.act_quant_fp8(dev(ch.x, d))
     R = T * top
-    gu = fp4.fp4_grouped_gemm(codes_x, scales_x, row_ids, offsets, up[2], up[3], kinds_d, up[4], 2 * inter)
+    gu = fp4.fp4_grouped_gemm_gather(codes_x, scales_x, row_ids, offsets, up[2], up[3], kinds_d, up[4], 2 * inter)
     h = torch.empty((R, inter), dtype=torch.float32, device=d)
     codes_h, scales_h = fp4.swiglu_quant_fp8(gu, ch.limit, row_weights=row_w, h_out=h)
-    y = fp4.fp4_grouped_gemm(codes_h, scales_h, None, offsets, dn[2], dn[3], kinds_d, dn[4], hidden,
+    y = fp4.fp4_grouped_gemm_gather(codes_h, scales_h, None, offsets, dn[2], dn[3], kinds_d, dn[4], hidden,
                              out=torch.empty((R, hidden), dtype=torch.float32, device=d))
     out = fp4.moe_combine(y, pair_rows)
     torch.cuda.synchronize()

@@ -122,10 +122,10 @@ def run_chain(ch, orc, what):
     dn = _upload_bank(ch.down, d)
     R, I, Hd = ch.R, ch.inter, ch.hidden
     codes_x, scales_x = fp4.act_quant_fp8(x)
-    gu = fp4.fp4_grouped_gemm(codes_x, scales_x, row_ids, offsets, up[2], up[3], kinds, up[4], 2 * I)
+    gu = fp4.fp4_grouped_gemm_gather(codes_x, scales_x, row_ids, offsets, up[2], up[3], kinds, up[4], 2 * I)
     h = torch.empty((R, I), dtype=torch.float32, device=d)
     codes_h, scales_h = fp4.swiglu_quant_fp8(gu, ch.limit, row_weights=rw, h_out=h)
-    y = fp4.fp4_grouped_gemm(codes_h, scales_h, None, offsets, dn[2], dn[3], kinds, dn[4], Hd,
+    y = fp4.fp4_grouped_gemm_gather(codes_h, scales_h, None, offsets, dn[2], dn[3], kinds, dn[4], Hd,
                              out=torch.empty((R, Hd), dtype=torch.float32, device=d))
     torch.cuda.synchronize()
 
@@ -191,7 +191,7 @@ def run_fused_vs_unfused(ch, limit=None, row_ids=None, kinds=None, weighted=True
     codes_x, scales_x = fp4.act_quant_fp8(xd)
     fp4.set_gemm_schedule(fp4.SCHEDULE_TILED)
     try:
-        gu = fp4.fp4_grouped_gemm(codes_x, scales_x, rid, offsets, up[2], up[3], kd, up[4], 2 * I)
+        gu = fp4.fp4_grouped_gemm_gather(codes_x, scales_x, rid, offsets, up[2], up[3], kd, up[4], 2 * I)
     finally:
         fp4.set_gemm_schedule(fp4.SCHEDULE_AUTO)
     h_ref = torch.empty((R, I), dtype=torch.float32, device=d)

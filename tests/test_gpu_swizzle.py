@@ -77,7 +77,7 @@ def test_grouped_mixed_layouts_bits_equal_plain(orc, schedule, seed, T, E, top, 
     gd = GroupedDevice(wl)
     codes, scales, plain = gd.step()
     w_ptrs, s_ptrs, kinds_t, keep = _swizzled_tables(gd, lambda e: e % 2 == 0)
-    got = fp4.fp4_grouped_gemm(codes, scales, gd.row_ids, gd.offsets, w_ptrs, s_ptrs, kinds_t, gd.scale2, wl.n)
+    got = fp4.fp4_grouped_gemm_gather(codes, scales, gd.row_ids, gd.offsets, w_ptrs, s_ptrs, kinds_t, gd.scale2, wl.n)
     torch.cuda.synchronize()
     assert torch.equal(got, plain)
     del keep
@@ -89,7 +89,7 @@ def test_grouped_kind_outside_range_gives_nan(orc, schedule):
     codes, scales, good = gd.step()
     bad_kinds = gd.kinds.clone()
     bad_kinds[2] = 4                           # not 0..3
-    out = fp4.fp4_grouped_gemm(codes, scales, gd.row_ids, gd.offsets, gd.w_ptrs, gd.s_ptrs, bad_kinds,
+    out = fp4.fp4_grouped_gemm_gather(codes, scales, gd.row_ids, gd.offsets, gd.w_ptrs, gd.s_ptrs, bad_kinds,
                                gd.scale2, wl.n)
     torch.cuda.synchronize()
     lo, hi = int(wl.offsets[2]), int(wl.offsets[3])
@@ -103,7 +103,7 @@ def test_config3_swizzled_bits_equal_plain():
     gd = GroupedDevice(workloads.config3())
     codes, scales, plain = gd.step()
     w_ptrs, s_ptrs, kinds_t, keep = _swizzled_tables(gd, lambda e: True)
-    got = fp4.fp4_grouped_gemm(codes, scales, gd.row_ids, gd.offsets, w_ptrs, s_ptrs, kinds_t, gd.scale2, gd.n)
+    got = fp4.fp4_grouped_gemm_gather(codes, scales, gd.row_ids, gd.offsets, w_ptrs, s_ptrs, kinds_t, gd.scale2, gd.n)
     torch.cuda.synchronize()
     assert torch.equal(got, plain)
     del keep
@@ -116,7 +116,7 @@ def test_config4_swizzled_bits_equal_plain():
     gd = GroupedDevice(workloads.config4())
     codes, scales, plain = gd.step()
     w_ptrs, s_ptrs, kinds_t, keep = _swizzled_tables(gd, lambda e: True)
-    got = fp4.fp4_grouped_gemm(codes, scales, gd.row_ids, gd.offsets, w_ptrs, s_ptrs, kinds_t, gd.scale2, gd.n)
+    got = fp4.fp4_grouped_gemm_gather(codes, scales, gd.row_ids, gd.offsets, w_ptrs, s_ptrs, kinds_t, gd.scale2, gd.n)
     torch.cuda.synchronize()
     assert not bool(torch.isnan(got).any())
     assert torch.equal(got, plain)

@@ -31,8 +31,18 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for fn in ("act_quant_fp8", "swiglu_quant_fp8", "fp4_expert_gemm", "fp4_grouped_gemm",
-               "fp4_grouped_gemm_swiglu_quant", "fp4moe_last_error", "fp4moe_version"):
+               "fp4_grouped_gemm_workspace_size", "fp4_grouped_gemm_gather", "fp4_grouped_gemm_swiglu_quant",
+               "fp4moe_set_debug_checks", "fp4moe_last_error", "fp4moe_version"):
         assert fn in names
+
+
+def test_header_return_codes():
+    text = open(os.path.join(ROOT, "include", "fp4moe.h")).read()
+    m = re.search(r"enum\s*\{\s*FP4MOE_OK\s*=\s*0\s*,\s*FP4MOE_EINVAL\s*=\s*1\s*,\s*FP4MOE_ELAUNCH\s*=\s*2\s*,"
+                  r"\s*FP4MOE_EDEVICE\s*=\s*3\s*\}", text)
+    assert m, "return codes OK=0, EINVAL=1, ELAUNCH=2, EDEVICE=3"
+    import block_scaled_fp4_quant_amd as fp4
+    assert (fp4.OK, fp4.EINVAL, fp4.ELAUNCH, fp4.EDEVICE) == (0, 1, 2, 3)
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -91,16 +101,52 @@ def test_expert_gemm_null_and_noop(lib):
 @pytest.mark.parametrize("a_rows,row_ids,E,R,n,k", [(-1, BAD, 4, 8, 16, 128), (8, BAD, 4, -1, 16, 128),
                                                     (8, BAD, 0, 8, 16, 128), (8, BAD, 4, 8, 0, 128),
                                                     (8, BAD, 4, 8, 16, 200), (4, NULL, 4, 8, 16, 128)])
-def test_grouped_gemm_rejects(lib, a_rows, row_ids, E, R, n, k):
-    assert lib.fp4_grouped_gemm(BAD, BAD, a_rows, row_ids, BAD, E, R, BAD, BAD, BAD, BAD, BAD,
-                                n, k, NULL) == 1
-    assert "fp4_grouped_gemm" in lib.fp4moe_last_error().decode()
+def test_grouped_gemm_gather_rejects(lib, a_rows, row_ids, E, R, n, k):
+    assert lib.fp4_grouped_gemm_gather(BAD, BAD, a_rows, row_ids, BAD, E, R, BAD, BAD, BAD, BAD, BAD,
+                                       n, k, NULL) == 1
+    assert "fp4_grouped_gemm_gather" in lib.fp4moe_last_error().decode()
 
 
-def test_grouped_gemm_null_and_noop(lib):
-    assert lib.fp4_grouped_gemm(BAD, BAD, 8, BAD, NULL, 4, 8, BAD, BAD, BAD, BAD, BAD, 16, 128, NULL) == 1
-    assert lib.fp4_grouped_gemm(NULL, NULL, 0, NULL, NULL, 4, 0, NULL, NULL, NULL, NULL, NULL,
-                                16, 128, NULL) == 0
+def test_grouped_gemm_gather_null_and_noop(lib):
+    assert lib.fp4_grouped_gemm_gather(BAD, BAD, 8, BAD, NULL, 4, 8, BAD, BAD, BAD, BAD, BAD, 16, 128, NULL) == 1
+    assert lib.fp4_grouped_gemm_gather(NULL, NULL, 0, NULL, NULL, 4, 0, NULL, NULL, NULL, NULL, NULL,
+                                       16, 128, NULL) == 0
+
+
+def test_grouped_gemm_workspace_size(lib):
+    # the packed-rows grouped GEMM needs no scratch: every kernel finds its tiles from the offsets
+    for E, R, n, k in [(1, 1, 16, 128), (256, 4096, 2048, 7168), (256, 65536, 4096, 7168), (4, 0, 16, 128)]:
+        assert lib.fp4_grouped_gemm_workspace_size(E, R, n, k) == 0
+
+
+@pytest.mark.parametrize("E,R,n,k", [(4, -1, 16, 128), (0, 8, 16, 128), (4, 8, 0, 128), (4, 8, 16, 200),
+                                     (4, 8, 16, 0), (4, 1 << 24, 16, 256)])
+def test_grouped_gemm_rejects(lib, E, R, n, k):
+    assert lib.fp4_grouped_gemm(BAD, BAD, BAD, E, R, BAD, BAD, BAD, BAD, BAD, n, k, NULL, 0, NULL) == 1
+    assert lib.fp4moe_last_error().decode().startswith("fp4_grouped_gemm:")
+
+
+def test_grouped_gemm_workspace_and_null_checks(lib):
+    f = lib.fp4_grouped_gemm
+    # a NULL workspace with a nonzero size
+    assert f(BAD, BAD, BAD, 4, 8, BAD, BAD, BAD, BAD, BAD, 16, 128, NULL, 64, NULL) == 1
+    assert "workspace" in lib.fp4moe_last_error().decode()
+    # a NULL operand with rows to compute
+    assert f(BAD, NULL, BAD, 4, 8, BAD, BAD, BAD, BAD, BAD, 16, 128, NULL, 0, NULL) == 1
+    assert "NULL" in lib.fp4moe_last_error().decode()
+    # total_rows == 0 is a no-op, with or without a (never touched) workspace
+    assert f(NULL, NULL, NULL, 4, 0, NULL, NULL, NULL, NULL, NULL, 16, 128, NULL, 0, NULL) == 0
+    assert f(NULL, NULL, NULL, 4, 0, NULL, NULL, NULL, NULL, NULL, 16, 128, BAD, 256, NULL) == 0
+    assert lib.fp4moe_last_error().decode() == ""
+
+
+def test_debug_checks_switch(lib):
+    assert lib.fp4moe_set_debug_checks(2) == 1
+    assert "fp4moe_set_debug_checks" in lib.fp4moe_last_error().decode()
+    assert lib.fp4moe_set_debug_checks(1) == 0
+    # argument validation still comes first: nothing reaches the device check
+    assert lib.fp4_grouped_gemm(BAD, BAD, BAD, 0, 8, BAD, BAD, BAD, BAD, BAD, 16, 128, NULL, 0, NULL) == 1
+    assert lib.fp4moe_set_debug_checks(0) == 0
 
 
 @pytest.mark.parametrize("a_rows,E,R,inter,k,limit", [
