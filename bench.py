@@ -188,6 +188,8 @@ def main():
                          "[n, k/gs] planes")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 disables it)")
+    ap.add_argument("--per-step", action="store_true",
+                    help="grouped workloads: list every timed step's GEMM time (HIP events) on stderr")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after timing, run 3 plain device copies of MIB MiB (a known-size kernel "
                          "for scaling the HBM byte counters of a profiler run)")
@@ -292,6 +294,7 @@ class GroupedRun:
         wall = time.perf_counter() - wall0
         gemm_all = np.array([e[1].elapsed_time(e[2]) for e in ev])
         return {"step_ms": ev[0][0].elapsed_time(ev[steps - 1][2]) / steps, "wall_ms": wall * 1e3 / steps,
+                "gemm_us_each": [round(float(v) * 1e3, 1) for v in gemm_all],
                 "aq_ms": float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
                 "gemm_ms": float(np.mean(gemm_all)), "gemm_ms_min": float(np.min(gemm_all)),
                 "gemm_pct": {f"p{q}": round(float(np.percentile(gemm_all, q)) * 1e3, 2) for q in (10, 50, 90)}}
@@ -357,6 +360,11 @@ def run_grouped(args, torch, fp4, dev):
         # 345 us in dispatches 5-25); after the prefill half's steps the decode half's W warm-up
         # steps start at the settled clock.  `--workload config3` times the decode half alone.
         meas[name] = runs[name].time(torch, args.warmup, args.steps)
+        if args.per_step:
+            each = meas[name]["gemm_us_each"]
+            log(f"[{name}] GEMM us of each timed step:")
+            for i in range(0, len(each), 10):
+                log(f"  {i:4d}: " + " ".join(f"{v:7.1f}" for v in each[i:i + 10]))
     res = {name: half_result(name, wls[name], meas[name], args, hashes[name]) for name in halves}
     head = "config3" if "config3" in res else "config4"
     h = res[head]
