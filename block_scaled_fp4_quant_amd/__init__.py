@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
         L.route_pack_workspace_size.restype = ctypes.c_int64
         L.route_pack.argtypes = [P, P, I32, I32, I32, P, P, P, P, P, P]
         L.route_pack.restype = ctypes.c_int
+        L.route_pack_noalloc.argtypes = [P, P, I32, I32, I32, P, P, P, P, P]
+        L.route_pack_noalloc.restype = ctypes.c_int
         L.gather_quant_rows.argtypes = [P, P, I32, I32, P, I32, P, P, P]
         L.gather_quant_rows.restype = ctypes.c_int
         L.moe_combine.argtypes = [P, I32, I32, P, P, I32, I32, P, P]

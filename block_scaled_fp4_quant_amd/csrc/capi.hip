@@ -112,6 +112,50 @@ int debug_check_tables(const char* what, const int32_t* offsets, int32_t num_exp
   return FP4MOE_OK;
 }
 
+// route_pack's body, with its workspace (counts then totals, fully overwritten) given.
+int pack_routes(const char* what, const int32_t* topk_ids, const float* topk_weights, int32_t tokens, int32_t top_k,
+                int32_t experts, int32_t* offsets, int32_t* row_ids, int32_t* pair_rows, float* row_weights,
+                int32_t* workspace, hipStream_t stream) {
+  if (tokens < 0) return fail(FP4MOE_EINVAL, "%s: tokens = %d < 0", what, (int)tokens);
+  if (top_k < 1 || top_k > 64) return fail(FP4MOE_EINVAL, "%s: top_k = %d must be in [1, 64]", what, (int)top_k);
+  if (experts < 1 || experts > 1024)
+    return fail(FP4MOE_EINVAL, "%s: experts = %d must be in [1, 1024]", what, (int)experts);
+  if ((int64_t)tokens * top_k >= kMaxPlaneBytes)
+    return fail(FP4MOE_EINVAL, "%s: tokens x top_k must stay below 2^31", what);
+  if (!offsets) return fail(FP4MOE_EINVAL, "%s: offsets is NULL", what);
+  if (tokens > 0 && (!topk_ids || !row_ids || !pair_rows))
+    return fail(FP4MOE_EINVAL, "%s: NULL buffer with tokens > 0", what);
+  return launched(fp4moe::launch_route_pack(topk_ids, topk_weights, tokens, top_k, experts, offsets, row_ids,
+                                            pair_rows, topk_weights ? row_weights : nullptr, workspace, stream),
+                  what);
+}
+
+// The scratch memory of the allocation-free entry point (route_pack_noalloc): route_pack's workspace
+// in a file-scope device array of kScratchWords int32 (1 MiB), one copy per device for the life of the
+// process.  Host code never uses the array's name as an address: the first call on a device takes
+// that device's address with hipGetSymbolAddress and keeps it.  Every call on a device shares its
+// copy (each call overwrites what it uses before reading it), so calls that overlap on one device race.
+constexpr int64_t kScratchWords = (int64_t)1 << 18;
+__device__ __align__(256) int32_t scratch[kScratchWords];
+std::mutex g_scratch_mutex;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_for_current_device(const char* what, int32_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FP4MOE_ELAUNCH, "%s: hipGetDevice: %s", what, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FP4MOE_ELAUNCH, "%s: device %d out of range", what, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(FP4MOE_ELAUNCH, "%s: hipGetSymbolAddress: %s", what, hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return FP4MOE_OK;
+}
+
 // The grouped GEMM behind fp4_grouped_gemm (row_ids == nullptr, a_rows == total_rows) and
 // fp4_grouped_gemm_gather.
 int grouped_gemm(const char* what, const uint8_t* a_codes, const float* a_scales, int32_t a_rows,
@@ -203,20 +247,26 @@ int route_pack(const int32_t* topk_ids, const float* topk_weights, int32_t token
                int32_t* offsets, int32_t* row_ids, int32_t* pair_rows, float* row_weights, void* workspace,
                hipStream_t stream) {
   const char* what = "route_pack";
-  if (tokens < 0) return fail(FP4MOE_EINVAL, "%s: tokens = %d < 0", what, (int)tokens);
-  if (top_k < 1 || top_k > 64) return fail(FP4MOE_EINVAL, "%s: top_k = %d must be in [1, 64]", what, (int)top_k);
-  if (experts < 1 || experts > 1024)
-    return fail(FP4MOE_EINVAL, "%s: experts = %d must be in [1, 1024]", what, (int)experts);
-  if ((int64_t)tokens * top_k >= kMaxPlaneBytes)
-    return fail(FP4MOE_EINVAL, "%s: tokens x top_k must stay below 2^31", what);
-  if (!offsets || !workspace) return fail(FP4MOE_EINVAL, "%s: offsets or workspace is NULL", what);
-  if (tokens > 0 && (!topk_ids || !row_ids || !pair_rows))
-    return fail(FP4MOE_EINVAL, "%s: NULL buffer with tokens > 0", what);
+  if (!workspace) return fail(FP4MOE_EINVAL, "%s: workspace is NULL", what);
   if (reinterpret_cast<uintptr_t>(workspace) & 3) return fail(FP4MOE_EINVAL, "%s: workspace not 4-byte aligned", what);
-  return launched(fp4moe::launch_route_pack(topk_ids, topk_weights, tokens, top_k, experts, offsets, row_ids,
-                                            pair_rows, topk_weights ? row_weights : nullptr,
-                                            static_cast<int32_t*>(workspace), stream),
-                  what);
+  return pack_routes(what, topk_ids, topk_weights, tokens, top_k, experts, offsets, row_ids, pair_rows, row_weights,
+                     static_cast<int32_t*>(workspace), stream);
+}
+
+int route_pack_noalloc(const int32_t* topk_ids, const float* topk_weights, int32_t tokens, int32_t top_k,
+                       int32_t experts, int32_t* offsets, int32_t* row_ids, int32_t* pair_rows, float* row_weights,
+                       hipStream_t stream) {
+  const char* what = "route_pack_noalloc";
+  if (tokens >= 0 && experts >= 1 && experts <= 1024) {
+    const int64_t words = fp4moe::route_pack_workspace_elems(tokens, experts);
+    if (words > kScratchWords)
+      return fail(FP4MOE_EINVAL, "%s: %d tokens x %d experts need %lld bytes of scratch; the library's array "
+                  "holds %lld", what, (int)tokens, (int)experts, (long long)(4 * words), (long long)(4 * kScratchWords));
+  }
+  int32_t* ws = nullptr;
+  if (int rc = scratch_for_current_device(what, &ws)) return rc;
+  return pack_routes(what, topk_ids, topk_weights, tokens, top_k, experts, offsets, row_ids, pair_rows, row_weights,
+                     ws, stream);
 }
 
 int gather_quant_rows(const uint8_t* codes, const float* scales, int32_t a_rows, int32_t k, const int32_t* row_ids,

@@ -276,6 +276,22 @@ FP4MOE_API int route_pack(const int32_t* topk_ids, const float* topk_weights, in
                           int32_t* pair_rows, float* row_weights, void* workspace, hipStream_t stream);
 
 /*
+ * route_pack_noalloc -- for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): route_pack without the workspace argument.
+ * Same arguments, outputs, bits and errors as route_pack; the workspace is instead a library-owned
+ * device array of 1 MiB per device (allocated when the library is loaded, held until the process
+ * ends), so tokens and experts are limited to route_pack_workspace_size(tokens, experts) <= 1 MiB
+ * (e.g. 256 experts up to 65,472 tokens; 1024 experts up to 16,320 tokens); larger sizes return
+ * FP4MOE_EINVAL.  Allocates nothing.  Every call on one device shares that device's array: calls
+ * that overlap on one device (different streams, or host threads without ordering) race and must
+ * be serialized by the caller; successive calls on one stream are safe (each overwrites what it
+ * reads).
+ */
+FP4MOE_API int route_pack_noalloc(const int32_t* topk_ids, const float* topk_weights, int32_t tokens,
+                                  int32_t top_k, int32_t experts, int32_t* offsets, int32_t* row_ids,
+                                  int32_t* pair_rows, float* row_weights, hipStream_t stream);
+
+/*
  * gather_quant_rows -- [CHECK: f16g grouped GEMM section; the packed activation rows].  Copies the
  * act-quant rows row_ids[p] into packed row p: out_codes[p, :] = codes[row_ids[p], :] and
  * out_scales[p, :] = scales[row_ids[p], :].  A row id outside [0, a_rows) gives zero code bytes and
