@@ -163,7 +163,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="both",
-                    choices=["both", "config3", "config4", "chain4", "w4a4", "config1", "config2", "peaks"],
+                    choices=["both", "config3", "config4", "chain4", "w4a4", "config1", "config2", "peaks", "floors"],
                     help="both (default): the grouped prefill GEMM step, then the grouped decode GEMM step, "
                          "reported in one line (decode = value, prefill = the `prefill` object); "
                          "config3: grouped decode GEMM alone; config4: grouped prefill GEMM alone; chain4: the "
@@ -215,6 +215,8 @@ def main():
         return run_w4a4(args, torch, fp4, dev)
     if args.workload in ("config1", "config2"):
         return run_single_expert(args, torch, fp4, dev)
+    if args.workload == "floors":
+        return run_floors(args, torch, dev)
     if args.workload == "peaks":
         return run_peaks(args, torch, dev)
 
@@ -498,6 +500,58 @@ def run_single_expert(args, torch, fp4, dev):
         "cpu_baseline": {"value": wbytes / t_cpu / 1e12, "unit": "TB/s", "cores": 1, "kind": "oracle",
                          "cpu": cpu_model(),
                          "sample": f"oracle act-quant + f64 expert GEMM of the whole step, one thread, {t_cpu:.2f} s"},
+    }
+    print(json.dumps(result), flush=True)
+
+
+def run_floors(args, torch, dev):
+    """Practical floors of a single-expert launch: an almost empty launch (torch.cuda._sleep(0)), a
+    streaming read of one expert's plane bytes by the library's own memory-bound kernel (act_quant_fp8
+    over an f32 input of that size: one 16-byte load per lane, 1 byte written per 4 read), and a
+    device copy of the same bytes (torch copy_).  Config1 planes: 7,798,784 B; config2: 8,257,540 B
+    (8,257,536 B of f32 rows here).  Inputs rotate over >= 72 copies (>= 560 MB, more than the
+    Infinity Cache) so that every launch streams from HBM.  HIP events per launch; the kernel
+    durations come from a kernel trace of the same command."""
+    import block_scaled_fp4_quant_amd as fp4
+    K = max(args.steps, 200)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        for i in range(20):
+            fn(i)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
+            fn(i)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        d = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]) * 1e3
+        return float(np.mean(d)), float(np.median(d))
+
+    res = {}
+    res["empty_launch_us"] = timed(lambda i: torch.cuda._sleep(0), K)
+    for name, rows in (("config1", 15232), ("config2", 16128)):
+        nbytes = rows * 128 * 4
+        ncopy = max(72, -(-(560 << 20) // nbytes))
+        bufs = [torch.ones((rows, 128), dtype=torch.float32, device=dev) for _ in range(ncopy)]
+        codes = torch.empty((rows, 128), dtype=torch.uint8, device=dev)
+        scales = torch.empty((rows, 1), dtype=torch.float32, device=dev)
+        dsts = [torch.empty((rows, 128), dtype=torch.float32, device=dev) for _ in range(8)]
+        res[f"{name}_read_us"] = timed(lambda i: fp4.act_quant_fp8(bufs[i % ncopy], codes, scales, stream=stream), K)
+        res[f"{name}_copy_us"] = timed(lambda i: dsts[i % 8].copy_(bufs[i % ncopy]), K)
+        del bufs, dsts
+    for k_, (mean, p50) in res.items():
+        log(f"{k_}: mean {mean:.2f} us, p50 {p50:.2f} us (events)")
+    result = {
+        "metric": "single-expert launch floors (empty launch, plane-sized streaming read and copy)",
+        "value": round(res["config1_read_us"][1], 3), "unit": "us", "n_gpus": 1, "steps": K, "warmup": 20,
+        "ms_per_step": round(res["config1_read_us"][1] / 1e3, 6), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "floors: torch.cuda._sleep(0); act_quant_fp8 and copy_ over one expert's plane "
+                               "bytes of f32, rotated over >= 560 MB",
+                   **{k_: {"mean": round(v[0], 2), "p50": round(v[1], 2)} for k_, v in res.items()}},
+        "roofline": None, "cpu_baseline": None,
     }
     print(json.dumps(result), flush=True)
 

@@ -7,16 +7,20 @@
 //   out[r, c] = sum_j ( sum_{k in group j} E4M3(A[r,k]) * E2M1(W[c,k]) ) * ws[c,j] * as[r, k/128]
 // accumulated in f32.  A single expert of the decode shapes (n = 2048 or 7168 columns) gives the
 // row-streaming kernel only n/256 = 8..28 workgroups, far too few to stream 8 MB of weights; this
-// kernel gives each workgroup 16 columns (n/16 = 128..448 workgroups) and splits k over its 8
-// wavefronts: wavefront w takes the 128-wide blocks b = w, w+8, w+16, ..., so the 8 wavefronts of a
-// workgroup read 8 consecutive 1 KB weight runs at a time with swizzled planes.  A grouped launch
-// may give a 16-column tile fewer wavefronts (KS = 4, 2 or 1, the workgroup then owning 8 / KS
-// tiles), so that each wavefront streams a longer run of blocks.
+// kernel splits each 16-column tile's k over KS wavefronts: wavefront kw takes the 128-wide blocks
+// b = kw, kw + KS, kw + 2 KS, ..., so the KS wavefronts of a tile read KS consecutive 1 KB weight
+// runs at a time with swizzled planes.  A single-expert launch picks KS from k alone, the smallest
+// of 4, 8 and 16 that leaves each wavefront at most kRing blocks (every load of the launch is then
+// issued before anything waits); a workgroup holds 8 wavefronts (2 tiles at KS = 4, 1 at KS = 8) or
+// 16 (KS = 16).  A grouped launch keeps 8 wavefronts per workgroup and gives a tile KS = 8, 4, 2 or
+// 1 wavefronts (the workgroup then owning 8 / KS tiles), so that each wavefront streams a longer run
+// of blocks.
 //
 // Data movement: a wavefront keeps kRing blocks of loads in flight, refilling a slot as soon as it
 // has computed on it: per block the lane's 16 weight bytes, its scale bytes and its 32 bytes of
 // the activation operand (which hit L2 after the first workgroup).  Only the activation scales go
-// through LDS, loaded together at the start.
+// through LDS: they are loaded before the weight ring, so storing them waits for them alone, and
+// the barrier that publishes them does not wait for the ring.
 //
 // Arithmetic per block (lane c16 = lane%16 holds column 16t + c16 and activation row c16; lane group
 // g = lane/16 holds k = 32g .. +32 of the block), as in the row-streaming kernel: NVFP4 on exact f16
@@ -33,8 +37,9 @@
 namespace fp4moe {
 namespace {
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 512;              // grouped form: 8 wavefronts per workgroup
 constexpr int kWaves = 8;
+constexpr int kMaxWaves = 16;              // single-expert form: up to 16 wavefronts per workgroup
 constexpr int kRing = 4;                    // blocks in flight per wavefront (refilled as they are consumed)
 constexpr int kMaxRows = 16;
 constexpr int kMaxK = 8192;
@@ -52,7 +57,7 @@ constexpr int kSwizzled = 2;
 
 struct Smem {
   float as[(kMaxK / 128) * kMaxRows];        // activation scales [block][row]
-  f32x4 red[kWaves][64];                     // per-wavefront result tiles
+  f32x4 red[kMaxWaves][64];                  // per-wavefront result tiles
   int active[kMaxExperts];                   // grouped: the experts with rows, in id order
   int wave_count[kWaves];
 };
@@ -80,13 +85,14 @@ __device__ __forceinline__ int act_row(const GemmArgs& p, int prow) {
 // Packed rows [m0, m0 + mrows) (mrows <= 16) of expert `ex`, column tile group tg: KS wavefronts
 // per 16-column tile, so the group holds kWaves / KS tiles, tiles (kWaves / KS) tg + sub, and the
 // wavefront kw = wave % KS of a tile takes the blocks b = kw, kw + KS, ...
-template <int KIND, bool SWZ, int KS>
+template <int KIND, bool SWZ, int KS, int WAVES>
 __device__ void run(const GemmArgs& p, const View& ex, int tg, int m0, int mrows, Smem& sm) {
-  static_assert(KS >= 1 && kWaves % KS == 0, "wavefronts per tile");
+  static_assert(KS >= 1 && WAVES % KS == 0 && WAVES <= kMaxWaves, "wavefronts per tile");
+  constexpr int kThr = 64 * WAVES;
   const int tid = threadIdx.x, lane = tid & 63, c16 = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int sub = wave / KS, kw = wave % KS;
-  const int t = (kWaves / KS) * tg + sub;
+  const int t = (WAVES / KS) * tg + sub;
   const int k = p.k, nblk = k >> 7, nq = (nblk + 3) >> 2;
   const int col = 16 * t + c16;
   const uint32_t n16 = (uint32_t)(p.n + 15) >> 4;
@@ -133,11 +139,25 @@ __device__ void run(const GemmArgs& p, const View& ex, int tg, int m0, int mrows
   const uint32_t a0 = arow >= 0 ? (uint32_t)arow * (uint32_t)k + 32u * g : kOffNone;
   auto a_off = [&](int b) -> uint32_t { return (b < nblk && a0 != kOffNone) ? a0 + (uint32_t)b * 128u : kOffNone; };
 
-  // Ring: the wavefront's blocks b = kw + KS i, weights, scale bytes and activation operand of
-  // each, all issued before anything waits.
   const int nbw = (nblk - kw + KS - 1) / KS;
   u32x4 wq[kRing], aq[kRing][2];
   uint32_t sq[kRing];
+  // Activation scales [block][row] into LDS, loaded before the weight ring so that storing them waits
+  // for these loads only; the barrier after the ring waits for LDS, not for the ring's loads.
+  {
+    const rsrc_t rsa = make_rsrc(p.a_scales, (uint32_t)p.a_rows * (uint32_t)nblk * 4u);
+    constexpr int kPer = kMaxRows * (kMaxK / 128) / kThr;
+    float v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = tid + kThr * j, b = i / kMaxRows, r = i % kMaxRows;
+      const int ar = (b < nblk && r < mrows) ? act_row(p, m0 + r) : -1;
+      v[j] = u2f(buf_load_u32(rsa, ar >= 0 ? ((uint32_t)ar * (uint32_t)nblk + b) * 4u : kOffNone));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Ring: the wavefront's blocks b = kw + KS i, weights, scale bytes and activation operand of
+    // each, all issued before anything waits.
+
 #pragma unroll
   for (int j = 0; j < kRing; ++j) {
     const int b = j < nbw ? kw + KS * j : nblk;
@@ -148,20 +168,10 @@ __device__ void run(const GemmArgs& p, const View& ex, int tg, int m0, int mrows
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // Activation scales [block][row] in LDS (at most 4 per thread, loaded together).
-  {
-    const rsrc_t rsa = make_rsrc(p.a_scales, (uint32_t)p.a_rows * (uint32_t)nblk * 4u);
-    float v[kMaxRows * (kMaxK / 128) / kThreads];
 #pragma unroll
-    for (int j = 0; j < kMaxRows * (kMaxK / 128) / kThreads; ++j) {
-      const int i = tid + kThreads * j, b = i / kMaxRows, r = i % kMaxRows;
-      const int ar = (b < nblk && r < mrows) ? act_row(p, m0 + r) : -1;
-      v[j] = u2f(buf_load_u32(rsa, ar >= 0 ? ((uint32_t)ar * (uint32_t)nblk + b) * 4u : kOffNone));
-    }
-#pragma unroll
-    for (int j = 0; j < kMaxRows * (kMaxK / 128) / kThreads; ++j) sm.as[tid + kThreads * j] = v[j];
+    for (int j = 0; j < kPer; ++j) sm.as[tid + kThr * j] = v[j];
   }
-  __syncthreads();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int i0 = 0; i0 < nbw; i0 += kRing) {
@@ -232,22 +242,23 @@ __device__ void run(const GemmArgs& p, const View& ex, int tg, int m0, int mrows
 
 // Packed rows [lo, hi) of expert `ex` for tile group tg, in passes of 16 rows (every pass streams
 // the group's weights again; the host sends only launches with few rows per expert here).
-template <int KS>
+template <int KS, int WAVES>
 __device__ void run_rows(const GemmArgs& p, const View& ex, int kind, int tg, int lo, int hi, Smem& sm) {
-  constexpr int kTilesPerGroup = kWaves / KS;
+  constexpr int kTilesPerGroup = WAVES / KS;
+  constexpr int kThr = 64 * WAVES;
   for (int m0 = lo; m0 < hi; m0 += kMaxRows) {
     const int mrows = min(kMaxRows, hi - m0);
     if (kind == kNV) {
-      run<kNV, false, KS>(p, ex, tg, m0, mrows, sm);
+      run<kNV, false, KS, WAVES>(p, ex, tg, m0, mrows, sm);
     } else if (kind == kMX) {
-      run<kMX, false, KS>(p, ex, tg, m0, mrows, sm);
+      run<kMX, false, KS, WAVES>(p, ex, tg, m0, mrows, sm);
     } else if (kind == (kNV | kSwizzled)) {
-      run<kNV, true, KS>(p, ex, tg, m0, mrows, sm);
+      run<kNV, true, KS, WAVES>(p, ex, tg, m0, mrows, sm);
     } else if (kind == (kMX | kSwizzled)) {
-      run<kMX, true, KS>(p, ex, tg, m0, mrows, sm);
+      run<kMX, true, KS, WAVES>(p, ex, tg, m0, mrows, sm);
     } else {
       // a weight format the kernel does not take: NaN rows
-      for (int i = threadIdx.x; i < mrows * 16 * kTilesPerGroup; i += kThreads) {
+      for (int i = threadIdx.x; i < mrows * 16 * kTilesPerGroup; i += kThr) {
         const int col = 16 * kTilesPerGroup * tg + (i % (16 * kTilesPerGroup));
         if (col < p.n) p.out[(size_t)(m0 + i / (16 * kTilesPerGroup)) * p.n + col] = __builtin_nanf("");
       }
@@ -263,10 +274,9 @@ __device__ __forceinline__ int2 expert_rows(const GemmArgs& p, int e) {
   return make_int2(lo, hi);
 }
 
-// Single expert (KS = 8): workgroup t owns tile t.  Grouped (persistent): every workgroup lists the
-// experts that have rows (a block-wide scan over the offsets into LDS), then takes the (active
-// expert, tile group) items blockIdx.x, blockIdx.x + gridDim.x, ... -- no workgroup is spent on an
-// empty expert.  The host picks KS so that there are about as many items as workgroups: a wavefront
+// Grouped (persistent): every workgroup lists the experts that have rows (a block-wide scan over
+// the offsets into LDS), then takes the (active expert, tile group) items blockIdx.x,
+// blockIdx.x + gridDim.x, ... -- no workgroup is spent on an empty expert.  The host picks KS so that there are about as many items as workgroups: a wavefront
 // then streams one long run of blocks, and its load ring does not drain between short items.
 // At most 128 registers (4 wavefronts per SIMD): two workgroups share a compute unit, so one
 // computes while the other waits for its loads (one token over 256 experts, 8 wavefronts per tile:
@@ -274,10 +284,6 @@ __device__ __forceinline__ int2 expert_rows(const GemmArgs& p, int e) {
 template <int KS>
 __global__ __launch_bounds__(kThreads, 4) void gemm_skinny_kernel(GemmArgs p, int ngroups) {
   __shared__ Smem sm;
-  if (!p.offsets) {
-    run_rows<KS>(p, View{p.w, p.s, p.scale2}, p.kind, blockIdx.x, 0, p.total_rows, sm);
-    return;
-  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = p.num_experts;
   constexpr int kPer = kMaxExperts / kThreads;                 // experts per thread
@@ -315,8 +321,25 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_skinny_kernel(GemmArgs p, in
     const int2 r = expert_rows(p, e);
     const View ex{reinterpret_cast<const uint8_t*>(p.w_ptrs[e]), reinterpret_cast<const uint8_t*>(p.s_ptrs[e]),
                   p.scale2s[e]};
-    run_rows<KS>(p, ex, p.kinds[e], tg, r.x, r.y, sm);
+    run_rows<KS, kWaves>(p, ex, p.kinds[e], tg, r.x, r.y, sm);
   }
+}
+
+// Single expert: workgroup tg owns WAVES / KS column tiles of KS wavefronts each, and the host picks
+// KS from k alone (so a row gives the same bits alone or in a batch) such that each wavefront
+// holds at most kRing blocks: every load of the launch is in flight after one issue round.
+template <int KS, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 4) void gemm_skinny_single_kernel(GemmArgs p) {
+  __shared__ Smem sm;
+  run_rows<KS, WAVES>(p, View{p.w, p.s, p.scale2}, p.kind, blockIdx.x, 0, p.total_rows, sm);
+}
+
+template <int KS, int WAVES>
+hipError_t launch_single(const GemmArgs& a, int tiles, hipStream_t stream) {
+  constexpr int kTilesPerGroup = WAVES / KS;
+  const int ngroups = (tiles + kTilesPerGroup - 1) / kTilesPerGroup;
+  hipLaunchKernelGGL((gemm_skinny_single_kernel<KS, WAVES>), dim3((unsigned)ngroups), dim3(64 * WAVES), 0, stream, a);
+  return hipGetLastError();
 }
 
 template <int KS>
@@ -342,7 +365,13 @@ bool gemm_skinny_grouped_fits(int64_t total_rows, int32_t num_experts, int32_t n
 
 hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
   const int tiles = (a.n + 15) / 16;
-  if (!a.offsets) return launch_ks<kWaves>(a, tiles, stream);
+  if (!a.offsets) {
+    // Single expert: at most kRing blocks per wavefront (k <= 8192: at most 64 blocks).
+    const int nblk = a.k / 128;
+    if (nblk <= 4 * kRing) return launch_single<4, 8>(a, tiles, stream);
+    if (nblk <= 8 * kRing) return launch_single<8, 8>(a, tiles, stream);
+    return launch_single<16, 16>(a, tiles, stream);
+  }
   // Grouped: at most min(E, rows) experts hold rows.  Take the fewest wavefronts per tile that
   // still give every workgroup of the persistent grid an item (one token at top-8 over n = 2048:
   // 8 experts x 128 tiles -> 4 wavefronts per tile, 512 items).

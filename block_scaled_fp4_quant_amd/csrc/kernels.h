@@ -99,7 +99,7 @@ hipError_t launch_weight_swizzle(const uint8_t* w, const uint8_t* s, int32_t kin
 // pass of 32 rows.
 hipError_t launch_gemm_decode(const GemmArgs& a, hipStream_t stream);
 
-// Split-k kernel for very few rows: 16-column tiles whose 8 (single expert) or 8, 4, 2 or 1
+// Split-k kernel for very few rows: 16-column tiles whose 4, 8 or 16 (single expert, from k) or 8, 4, 2 or 1
 // (grouped, picked per launch) wavefronts split k.  Single expert
 // (offsets == nullptr): requires gemm_skinny_fits(g, n, k) (g <= 16, k <= 8192).  Grouped: requires
 // gemm_skinny_grouped_fits (at most 16 packed rows, 128 when the schedule is forced; k <= 8192;

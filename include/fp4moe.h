@@ -404,8 +404,8 @@ FP4MOE_API int w4a4_gemm(const uint8_t* a_codes, const uint8_t* a_micro, const f
  * kernel (128 x 256 output tiles); a single-expert call (fp4_expert_gemm) with g <= 16 and
  * k <= 8192, or a grouped call with at most 16 packed rows, k <= 8192 and at most 1024 experts,
  * uses a split-k kernel instead (16-column tiles whose wavefronts split k and sum their tiles in a
- * fixed order: 8 per tile for a single expert; 8, 4, 2 or 1 for a grouped call, from its packed rows,
- * experts and n).  All compute the same definition to the same accuracy bound; only the
+ * fixed order: 4, 8 or 16 per tile for a single expert, from k alone; 8, 4, 2 or 1 for a grouped
+ * call, from its packed rows, experts and n).  All compute the same definition to the same accuracy bound; only the
  * order of the f32 additions differs.  schedule: 0 = automatic (default), 1 = always row-streaming,
  * 2 = always tiled, 3 = split-k for the calls that fit it (grouped calls with up to 128 packed
  * rows; other calls as 0).  Process-wide; affects calls made after it returns.
