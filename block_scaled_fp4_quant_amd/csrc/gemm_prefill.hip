@@ -395,7 +395,8 @@ __device__ __forceinline__ void swiglu_epilogue(const GemmArgs& p, int m0, int m
   if (row < mrows) {
     const int prow = m0 + row;
     const float w = p.swiglu_row_w ? p.swiglu_row_w[prow] : 1.0f;
-    const bool bad = act_row(p, prow) < 0 || (ROWCHECK && (s_rowbad[2 * row] | s_rowbad[2 * row + 1]));
+    // FP8 activations: the scale scan flagged the row (bad scale or row id); otherwise look the row up
+    const bool bad = ROWCHECK ? (s_rowbad[2 * row] | s_rowbad[2 * row + 1]) != 0 : act_row(p, prow) < 0;
     const float hbad = swiglu_one(__builtin_nanf(""), __builtin_nanf(""), limit, w);
     const float tmax = fmaxf(hmax[row], hmax[kBM + row]);
     const float amax = fmaxf(bad ? fabsf(hbad) : tmax * fabsf(w), 1e-4f);
@@ -532,7 +533,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
   const float post = is_nv(KIND) ? ex.scale2 : 1.0f;
   if (p.swiglu_inter) {
     swiglu_epilogue<NMT, KIND != kW4>(p, m0, mrows, n0, post, acc, st);
-  } else {
+  } else if (KIND == kW4) {
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
@@ -540,9 +541,9 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
         const int row = 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3);
         if (row < mrows) {
           const int prow = m0 + row;
-          const int arow = act_row(p, prow);
-          const bool bad = arow < 0 || (KIND != kW4 && (s_rowbad[2 * row] | s_rowbad[2 * row + 1]));
-          const float rsc = (KIND == kW4 && !bad) ? p.a_row_scale[arow] : 1.0f;
+          const int arow = act_row(p, prow);             // W4A4 tiles skip the scale scan
+          const bool bad = arow < 0;
+          const float rsc = bad ? 1.0f : p.a_row_scale[arow];
 #pragma unroll
           for (int nt = 0; nt < kNT; ++nt) {
             const int col = tile_col(p, n0, wave, nt) + c32;
@@ -550,6 +551,59 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
           }
         }
       }
+  } else {
+    // Row-contiguous stores: the accumulators go through LDS (over the activation stages, 64 rows
+    // per pass), so that each lane then writes 16 consecutive output bytes of one row (a quarter of
+    // the store instructions of the accumulator layout, whose lanes hold columns).  Non-temporal:
+    // the output is not read again by this launch.
+    constexpr int kPitch = kBN + 4;                          // floats per LDS row
+    static_assert(sizeof(Stage) * 2 >= 64 * kPitch * sizeof(float), "transpose space");
+    float* tx = reinterpret_cast<float*>(&st[0]);
+    __syncthreads();                                         // every wavefront is done with the stages
+#pragma unroll
+    for (int pass = 0; pass < (NMT + 1) / 2; ++pass) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int mt = 2 * pass + q;
+        if (mt < NMT) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int rl = 32 * q + 8 * (v >> 2) + 4 * h + (v & 3), row = 64 * pass + rl;
+            const bool bad = (s_rowbad[2 * row] | s_rowbad[2 * row + 1]) != 0;
+#pragma unroll
+            for (int nt = 0; nt < kNT; ++nt)
+              tx[rl * kPitch + kWaveCols * wave + 32 * nt + c32] = bad ? __builtin_nanf("") : acc[mt][nt][v] * post;
+          }
+        }
+      }
+      __syncthreads();
+      {
+        // thread t stores columns 4 (t % 64) .. +3 of rows t / 64, t / 64 + 4, ... of the pass
+        constexpr int kRowsPerStep = kThreads / (kBN / 4);
+        const int c4 = threadIdx.x % (kBN / 4), r0 = threadIdx.x / (kBN / 4), col = n0 + 4 * c4;
+        float* dst = p.out + (size_t)(m0 + 64 * pass + r0) * p.n + col;
+        const size_t step = (size_t)kRowsPerStep * p.n;
+        const float* src = tx + r0 * kPitch + 4 * c4;
+        // 16-byte stores need 16-byte aligned rows: n % 4 == 0 and an aligned output base
+        const bool vec = ((p.n & 3) | (int)(reinterpret_cast<uintptr_t>(p.out) & 15)) == 0;
+#pragma unroll 4
+        for (int rl = r0; rl < 64; rl += kRowsPerStep) {
+          if (64 * pass + rl < mrows && col < p.n) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(src);
+            if (vec) {
+              __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (col + e < p.n) __builtin_nontemporal_store(v[e], dst + e);
+            }
+          }
+          dst += step;
+          src += kRowsPerStep * kPitch;
+        }
+      }
+      __syncthreads();
+    }
   }
 }
 
@@ -591,6 +645,7 @@ __device__ __forceinline__ bool scan_act_scales(const GemmArgs& p, int m0, int m
         bad |= base != kOffNone && b0 + 8 * j + e < nblk && !pow2;
       }
   }
+  bad |= row < mrows && ar < 0;               // an out-of-range row_ids entry: the row is NaN too
   s_rowbad[threadIdx.x] = bad ? 1 : 0;
   return __builtin_amdgcn_readfirstlane(__syncthreads_and(ok)) != 0;
 }

@@ -61,6 +61,31 @@ def test_random_shapes(orc, schedule, kind, g, n, k):
     check_bound(got, ref, absp, k, f"g={g} n={n} k={k} kind={kind}")
 
 
+@pytest.mark.parametrize("shift", [1, 2, 3])
+def test_tiled_output_any_float_alignment(orc, shift):
+    # the tiled kernel writes whole 16-byte row pieces only when n % 4 == 0 and the output base is
+    # 16-byte aligned; any other float-aligned base takes per-element stores of the same values, and
+    # nothing outside the output is written
+    g, n, k = 150, 256, 1024
+    wl = workloads.single_random(600 + shift, g, n, k, NV)
+    ex = wl.expert
+    fp4.set_gemm_schedule(fp4.SCHEDULE_TILED)
+    try:
+        codes, scales = fp4.act_quant_fp8(dev(wl.x))
+        aligned = fp4.fp4_expert_gemm(codes, scales, dev(ex.w), dev(ex.s), ex.scale2, ex.kind)
+        buf = torch.full((g * n + 8,), 7.0, dtype=torch.float32, device="cuda")
+        out = buf[shift:shift + g * n].view(g, n)
+        fp4.fp4_expert_gemm(codes, scales, dev(ex.w), dev(ex.s), ex.scale2, ex.kind, out=out)
+        torch.cuda.synchronize()
+    finally:
+        fp4.set_gemm_schedule(fp4.SCHEDULE_AUTO)
+    assert torch.equal(out, aligned)
+    assert bool((buf[:shift] == 7.0).all()) and bool((buf[shift + g * n:] == 7.0).all())
+    rc, rs = orc.act_quant(wl.x)
+    ref, absp = orc.expert_gemm(rc, rs, ex.w, ex.s, ex.scale2, ex.kind)
+    check_bound(out.cpu().numpy(), ref, absp, k, f"output base + {4 * shift} bytes")
+
+
 @pytest.mark.parametrize("kind", [NV, MX])
 def test_wide_dynamic_range_within_blocks(orc, schedule, kind):
     # activation magnitudes log-uniform over 6 decades: inside one 128-wide block the products span
