@@ -287,10 +287,12 @@ struct Frags {
   typename OpT<KIND>::T b[kNT];
 };
 
-// One 128-wide k block.  Step s issues its MFMAs while the operands of step s+1 are prepared
-// (LDS reads, 2 weight dequantizations); steps 0-3 also convert and store the next block's
-// activations, step 4 issues the loads of the block after, and before step 7 the workgroup meets
-// at the barrier that publishes the next stage.  Step 7 prepares step 0 of the next block.
+// One 128-wide k block.  Step s issues its MFMAs while the operands of step s+1 are prepared: 2
+// weight dequantizations, and each row tile's A fragment, read from LDS into the same registers
+// right after that row tile's MFMAs (no second set of A registers).  Steps 0-3 also convert and
+// store the next block's activations, step 4 issues the loads of the block after, and before step 7
+// the workgroup meets at the barrier that publishes the next stage.  Step 7 prepares step 0 of the
+// next block.
 template <int KIND, int NMT, bool SWZ>
 __device__ __forceinline__ void run_block(const Stage& cur, Stage& nxt, const WRegs& w, const WRegs& wn,
                                           StageRegs& store_src, StageRegs& load_dst, const Rsrc& r,
@@ -306,8 +308,6 @@ __device__ __forceinline__ void run_block(const Stage& cur, Stage& nxt, const WR
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) g.a[mt] = (s + 1 < kSteps) ? lds_a<KIND>(cur, mt, s + 1) : lds_a<KIND>(nxt, mt, 0);
-#pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
       switch (s) {
         case 0: g.b[nt] = dequant_step<KIND, 1>(w, nt); break;
@@ -322,9 +322,11 @@ __device__ __forceinline__ void run_block(const Stage& cur, Stage& nxt, const WR
     }
     if (s < 4) stage_store_q<KIND>(nxt, store_src, s);
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
+    for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = mfma32x32x16(f.a[mt], f.b[nt], acc[mt][nt]);
+      f.a[mt] = (s + 1 < kSteps) ? lds_a<KIND>(cur, mt, s + 1) : lds_a<KIND>(nxt, mt, 0);
+    }
     if (s == 4) {
       __builtin_amdgcn_sched_barrier(0);
       stage_load<KIND>(r, ao, b + 1 + kADepth, nblk, load_dst);
@@ -335,8 +337,6 @@ __device__ __forceinline__ void run_block(const Stage& cur, Stage& nxt, const WR
       w_load<KIND, SWZ>(r, wo, so, b + kWDepth, nblk, wload);
       __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) f.a[mt] = g.a[mt];
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) f.b[nt] = g.b[nt];
   }
