@@ -556,10 +556,47 @@ def run_floors(args, torch, dev):
     print(json.dumps(result), flush=True)
 
 
+def mfma_loop_rates(torch, dev, timed):
+    """Sustained dense f16 MFMA rate and core clock from the register-only loop in
+    libfp4moe_probe.so (two workgroups of four wavefronts per compute unit, 32x32x16 MFMAs), with
+    operands that change every round and with constant operands.  The clock is each workgroup's
+    s_memtime cycles over its s_memrealtime (100 MHz) ticks; reported as the median over workgroups."""
+    import ctypes
+    path = os.path.join(ROOT, "block_scaled_fp4_quant_amd", "libfp4moe_probe.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is missing: build it with python -m block_scaled_fp4_quant_amd.build")
+    L = ctypes.CDLL(path)
+    fn = L.fp4moe_probe_mfma_loop
+    fn.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    nblocks, iters = 2 * cus, 20000
+    sink = torch.empty(nblocks * 256, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(nblocks * 4, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream()
+    flops = nblocks * 4 * iters * 4 * 2 * 32 * 32 * 16
+    out = {"workgroups": nblocks, "waves_per_simd": 2, "iters": iters}
+    for name, toggle in (("changing_operands", 1), ("constant_operands", 0)):
+        def launch():
+            rc = fn(iters, toggle, nblocks, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(clocks.data_ptr()),
+                    ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"fp4moe_probe_mfma_loop returned {rc}")
+        timed(launch, 20)                                 # about 60 ms of load before the timed launches
+        t = timed(launch, 20)
+        c = clocks.cpu().numpy().view(np.uint64).reshape(nblocks, 4).astype(np.float64)
+        mhz = float(np.median((c[:, 1] - c[:, 0]) / (c[:, 3] - c[:, 2]) * 100.0))
+        tf = flops / t / 1e12
+        out[name] = {"tflops": round(tf, 1), "clock_mhz": round(mhz, 0),
+                     "flops_per_clock_per_cu": round(tf * 1e12 / (mhz * 1e6) / cus, 1)}
+        log(f"f16 MFMA loop, {name.replace('_', ' ')}: {tf:.0f} TFLOP/s at {mhz:.0f} MHz")
+    return out
+
+
 def run_peaks(args, torch, dev):
-    """The roofline denominators re-measured on this GPU with library-independent torch kernels: a
-    device-to-device copy of 4 GiB (HBM read + write), a read-only reduction of 4 GiB, and a dense
-    bf16 matrix product 8192^3 (hipBLASLt).  Not part of the method: context for the fractions of
+    """The roofline denominators re-measured on this GPU: a device-to-device copy of 4 GiB (HBM read
+    + write), a read-only reduction of 4 GiB and a dense bf16 matrix product 8192^3 (hipBLASLt), all
+    torch kernels, and the register-only f16 MFMA loop of libfp4moe_probe.so.  Not part of the method: context for the fractions of
     the published figures (8 TB/s, 2.5 PFLOP/s) that the other workloads report."""
     nbytes = 4 << 30
     src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).uniform_()
@@ -586,14 +623,16 @@ def run_peaks(args, torch, dev):
     read_gbs = nbytes / t_read / 1e9
     mm_tf = 2 * 8192 ** 3 / t_mm / 1e12
     log(f"copy {copy_gbs:.0f} GB/s (read+write), read {read_gbs:.0f} GB/s, bf16 mm {mm_tf:.0f} TFLOP/s")
+    del src, dst
+    mfma = mfma_loop_rates(torch, dev, timed)
     result = {
-        "metric": "roofline denominators re-measured (copy GB/s, read GB/s, bf16 GEMM TFLOP/s)",
+        "metric": "roofline denominators re-measured (copy GB/s, read GB/s, bf16 GEMM TFLOP/s, f16 MFMA loop)",
         "value": round(read_gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": 20, "warmup": 5,
         "ms_per_step": round(t_read * 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32 / bf16", "data": "synthetic",
         "config": {"workload": "peaks: 4 GiB f32 copy and sum, bf16 mm 8192^3",
                    "copy_gbs": round(copy_gbs, 1), "read_gbs": round(read_gbs, 1),
-                   "bf16_mm_tflops": round(mm_tf, 1), "published_hbm_gbs": HBM_PEAK_GBS,
+                   "bf16_mm_tflops": round(mm_tf, 1), "f16_mfma_loop": mfma, "published_hbm_gbs": HBM_PEAK_GBS,
                    "published_bf16_tflops": MFMA_PEAK_TFLOPS["f16"]},
         "roofline": None, "cpu_baseline": None,
     }

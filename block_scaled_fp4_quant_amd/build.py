@@ -1,4 +1,5 @@
-"""Build libfp4moe.so (the HIP kernels and the C ABI) in-tree for gfx950 with hipcc.
+"""Build libfp4moe.so (the HIP kernels and the C ABI) in-tree for gfx950 with hipcc, and beside it
+libfp4moe_probe.so (the benchmark's matrix-core rate probe, not part of the method).
 
 Usage: python -m block_scaled_fp4_quant_amd.build  (or call build()).  Always recompiles.
 """
@@ -15,6 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfp4moe.so")
+PROBE_LIB = os.path.join(PKG, "libfp4moe_probe.so")
+PROBE_SOURCES = ["probe_mfma.hip"]
 SOURCES = ["act_quant.hip", "swiglu_quant.hip", "route.hip", "rung.hip", "w4a4.hip", "swizzle.hip", "gemm_decode.hip", "gemm_skinny.hip", "gemm_prefill.hip", "table_check.hip", "capi.hip"]
 
 HIPCC_FLAGS = [
@@ -33,10 +36,15 @@ def _hipcc() -> str:
 
 
 def build(verbose: bool = False, jobs: int = 4) -> str:
+    _build_lib(PROBE_SOURCES, PROBE_LIB, verbose, jobs)
+    return _build_lib(SOURCES, LIB, verbose, jobs)
+
+
+def _build_lib(sources, lib_path: str, verbose: bool, jobs: int) -> str:
     hipcc = _hipcc()
     with tempfile.TemporaryDirectory(prefix="fp4moe_build_") as tmp:
         objs, procs = [], []
-        for src in SOURCES:
+        for src in sources:
             obj = os.path.join(tmp, src + ".o")
             cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
@@ -47,13 +55,13 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
                 _wait(procs.pop(0))
         while procs:
             _wait(procs.pop(0))
-        tmp_lib = LIB + ".tmp%d" % os.getpid()
+        tmp_lib = lib_path + ".tmp%d" % os.getpid()
         cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp_lib]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
-        os.replace(tmp_lib, LIB)
-    return LIB
+        os.replace(tmp_lib, lib_path)
+    return lib_path
 
 
 def _wait(item):
