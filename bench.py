@@ -385,6 +385,23 @@ def run_grouped(args, torch, fp4, dev):
                              "ms_per_step": p["ms_per_step"], "steps": args.steps, "warmup": args.warmup,
                              "config": p["config"], "roofline": p["roofline"], "roofline_fp8": p["roofline_fp8"],
                              "cpu_baseline": None}
+    if "config4" in halves:
+        # Context for the prefill fraction: the matrix cores' sustained rate on this GPU in this run
+        # (after the timed halves, so it cannot affect them).  Full matrix-core load is power-limited,
+        # so this is well below the published 2.5 PFLOP/s that `roofline` keeps as its peak.
+        target = result["prefill"] if len(halves) == 2 else result
+        try:
+            loop = mfma_loop_rates(torch, dev, lambda fn, reps: event_timed(torch, fn, reps),
+                                   which=("changing_operands",))["changing_operands"]
+            ach = res["config4"]["roofline"]["achieved"]
+            target["roofline_sustained"] = {
+                "bound": "mfma", "achieved": ach, "peak": loop["tflops"], "unit": "TFLOP/s",
+                "frac": round(ach / loop["tflops"], 4), "clock_mhz": loop["clock_mhz"],
+                "peak_is": "register-only f16 32x32x16 MFMA loop on this GPU in the same run (operands "
+                           "changing every round, 2 wavefronts per SIMD), at the clock it measures"}
+        except (OSError, SystemExit, RuntimeError) as exc:
+            log(f"sustained MFMA rate not measured: {exc}")
+            target["roofline_sustained"] = None
     if args.calibrate_copy > 0:
         nbytes = args.calibrate_copy << 20
         src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -556,10 +573,25 @@ def run_floors(args, torch, dev):
     print(json.dumps(result), flush=True)
 
 
-def mfma_loop_rates(torch, dev, timed):
+def event_timed(torch, fn, reps):
+    """Average seconds per call of fn over reps calls (HIP events on the current stream), after a
+    few untimed calls."""
+    for _ in range(max(3, reps // 4)):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / reps
+
+
+def mfma_loop_rates(torch, dev, timed, which=("changing_operands", "constant_operands")):
     """Sustained dense f16 MFMA rate and core clock from the register-only loop in
     libfp4moe_probe.so (two workgroups of four wavefronts per compute unit, 32x32x16 MFMAs), with
-    operands that change every round and with constant operands.  The clock is each workgroup's
+    operands that change every round and/or with constant operands.  The clock is each workgroup's
     s_memtime cycles over its s_memrealtime (100 MHz) ticks; reported as the median over workgroups."""
     import ctypes
     path = os.path.join(ROOT, "block_scaled_fp4_quant_amd", "libfp4moe_probe.so")
@@ -577,6 +609,9 @@ def mfma_loop_rates(torch, dev, timed):
     flops = nblocks * 4 * iters * 4 * 2 * 32 * 32 * 16
     out = {"workgroups": nblocks, "waves_per_simd": 2, "iters": iters}
     for name, toggle in (("changing_operands", 1), ("constant_operands", 0)):
+        if name not in which:
+            continue
+
         def launch():
             rc = fn(iters, toggle, nblocks, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(clocks.data_ptr()),
                     ctypes.c_void_p(stream.cuda_stream))
@@ -605,16 +640,7 @@ def run_peaks(args, torch, dev):
     b = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
 
     def timed(fn, reps):
-        for _ in range(max(3, reps // 4)):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e-3 / reps
+        return event_timed(torch, fn, reps)
 
     t_copy = timed(lambda: dst.copy_(src), 20)
     t_read = timed(lambda: src.sum(), 20)
