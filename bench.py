@@ -48,11 +48,47 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def code_text(src: str) -> str:
+    """C/C++ source without its comments, whitespace runs collapsed to one space: what the compiler
+    sees, so that an edit to comments or layout keeps a recorded measurement valid and any other
+    edit does not.  String and character literals are kept as they are."""
+    out, i, n = [], 0, len(src)
+
+    def space():
+        if out and out[-1] != " ":
+            out.append(" ")
+
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            space()
+            i = n if j < 0 else j + 2
+        elif c.isspace():
+            space()
+            i += 1
+        else:
+            out.append(c)
+            i += 1
+    return "".join(out).strip()
+
+
 def sources_sha(workload: str) -> str:
+    """Hash of the code (comments and layout aside) of the kernel sources a traffic record belongs to."""
     h = hashlib.sha256()
     for rel in GEMM_SOURCES[workload]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

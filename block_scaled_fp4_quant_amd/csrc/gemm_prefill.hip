@@ -31,14 +31,20 @@
 // dequantizes its own weights in registers (a 2-block ring of 32 nibble bytes + scale bytes per
 // column tile per lane), while the bf16 activation tile sits in a two-stage LDS ring shared by the
 // 4 wavefronts.  Inside a block the steps are software-pipelined: the MFMAs of step s run while
-// the LDS reads and weight dequantization of step s+1 are issued, and the conversion of the next
-// block's activations into the other LDS stage is spread over the first four steps.  One barrier
+// the weight dequantization of step s+1 is issued and each row tile's A fragment for step s+1 is
+// read from LDS right after that row tile's MFMAs, and the conversion of the next block's
+// activations into the other LDS stage is spread over the first four steps.  One barrier
 // per block.  Two workgroups share a compute unit (256 registers per lane, 139 KB of LDS), so each
 // SIMD interleaves two independent wavefronts.  On the f16 route an expert's last row slice
 // computes only its occupied 32-row MFMA tiles (32, 64 or 96 rows), which keeps the padding of the
 // skewed per-expert row counts small; the bf16 route computes whole slices.
 // Activations are staged with 8 lanes per row, so each 16-byte load instruction touches 8 cache
 // lines.
+//
+// Epilogue.  The accumulators go through LDS (over the activation stages), 64 rows at a time, so that
+// each thread writes 16 consecutive bytes of one output row with a non-temporal store; rows whose
+// activation scale or row id is invalid were flagged by the scale scan before the main loop and are
+// written as NaN.  The fused activation epilogue (swiglu_inter > 0) has its own exchange through LDS.
 //
 // Work list.  Tiles are (expert, 128-row slice, 256-column slice).  Each workgroup finds its tile by
 // a prefix scan of ceil(rows_e / 128) over the device-side offsets (no workspace, no host read of

@@ -148,3 +148,15 @@ def test_mfma_probe_runs_and_stamps_clocks():
         mhz = (c[:, 1] - c[:, 0]).astype(np.float64) / (c[:, 3] - c[:, 2]).astype(np.float64) * 100.0
         assert 100.0 < float(np.median(mhz)) < 5000.0     # a core clock, in MHz
         assert bool(torch.isfinite(sink).all())           # operands in [0.5, 1): sums stay finite
+
+
+def test_source_hash_ignores_comments_and_layout_only():
+    # a recorded traffic figure stays valid across comment and whitespace edits, not code edits
+    base = 'int f(int x) {\n  // twice\n  return 2 * x; /* done */\n}\nconst char* s = "// not a comment";\n'
+    same = 'int f(int x) {   return 2 * x;\n\n}\n// new note\nconst char* s = "// not a comment"; /* x */\n'
+    code = 'int f(int x) {\n  return 3 * x;\n}\nconst char* s = "// not a comment";\n'
+    lit = 'int f(int x) {\n  return 2 * x;\n}\nconst char* s = "//  not a comment";\n'
+    assert bench.code_text(base) == bench.code_text(same)
+    assert bench.code_text(base) != bench.code_text(code)
+    assert bench.code_text(base) != bench.code_text(lit)            # string literals are kept whole
+    assert bench.code_text("char c = '\"'; // q\nint y;") == "char c = '\"'; int y;"
