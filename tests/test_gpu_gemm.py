@@ -86,6 +86,21 @@ def test_tiled_output_any_float_alignment(orc, shift):
     check_bound(out.cpu().numpy(), ref, absp, k, f"output base + {4 * shift} bytes")
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_single_random_sweep(orc, schedule, seed):
+    # seeded random single-expert shapes: g 1..300 (split-k sizes g <= 16 in a third of the seeds),
+    # any n 1..600, k up to 2048, both formats, power-of-two and other scale2 values
+    rng = np.random.default_rng([4096, seed])
+    g = int(rng.integers(1, 17)) if seed % 3 == 0 else int(rng.integers(1, 301))
+    n = int(rng.integers(1, 601))
+    k = 128 * int(rng.integers(1, 17))
+    kind = NV if seed % 2 == 0 else MX
+    scale2 = float(2.0 ** -int(rng.integers(4, 9))) if seed % 4 else 0.3
+    wl = workloads.single_random(7000 + seed, g, n, k, kind, scale2=scale2, x_scale=float(rng.uniform(0.1, 4.0)))
+    got, ref, absp = run_single(wl, orc)
+    check_bound(got, ref, absp, k, f"sweep seed={seed} g={g} n={n} k={k} kind={kind}")
+
+
 @pytest.mark.parametrize("kind", [NV, MX])
 def test_wide_dynamic_range_within_blocks(orc, schedule, kind):
     # activation magnitudes log-uniform over 6 decades: inside one 128-wide block the products span
@@ -154,6 +169,32 @@ def grouped_check(gd: GroupedDevice, orc, out, rows=None):
 def test_grouped_small_mixed(orc, schedule, seed, T, E, top, n, k):
     kinds = [NV if e % 3 else MX for e in range(E)]
     wl = workloads.grouped_random(seed, T, E, top, n, k, kinds=kinds, empty_experts=(1, E - 2))
+    gd = GroupedDevice(wl)
+    _, _, out = gd.step()
+    grouped_check(gd, orc, out)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_grouped_random_sweep(orc, schedule, seed):
+    # seeded random grouped problems: any n (1..600, so ragged column tiles and n % 4 != 0), k up to
+    # 1024, experts of both formats with some left empty, 1..4 experts per token, normal or
+    # Student-t(3) activations, uniform or Zipf(1.1) routing; every fourth seed has 1..4 experts and
+    # up to 600 tokens, so that experts span several 128-row slices, the others 1..20 experts and up
+    # to 200 tokens (the short tail slices of every 32-row class)
+    rng = np.random.default_rng([8128, seed])
+    few = seed % 4 == 0
+    E = int(rng.integers(1, 5)) if few else int(rng.integers(1, 21))
+    n_empty = int(rng.integers(0, E // 3 + 1))
+    empties = tuple(int(e) for e in rng.choice(E, n_empty, replace=False)) if n_empty else ()
+    top = int(rng.integers(1, min(4, E - n_empty) + 1))
+    T = int(rng.integers(100, 601)) if few else int(rng.integers(1, 201))
+    n = int(rng.integers(1, 601))
+    k = 128 * int(rng.integers(1, 5 if few else 9))
+    kinds = [int(v) for v in rng.integers(0, 2, size=E)]
+    x_dist = "t3" if seed % 2 else "normal"
+    zipf = 1.1 if seed % 3 == 0 else None
+    wl = workloads.grouped_random(9000 + seed, T, E, top, n, k, kinds=kinds, empty_experts=empties, zipf=zipf,
+                                  x_dist=x_dist)
     gd = GroupedDevice(wl)
     _, _, out = gd.step()
     grouped_check(gd, orc, out)
