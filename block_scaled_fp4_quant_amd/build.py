@@ -24,6 +24,9 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # keep hipcc from forming packed-f32 instructions (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # kernels whose leading arguments are scalars get up to 16 of their dwords in SGPRs before the
+    # first instruction (the compiler keeps a loading prologue for firmware without the feature)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-fvisibility=hidden", "-Wall",
 ]
 

@@ -327,18 +327,37 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_skinny_kernel(GemmArgs p, in
 
 // Single expert: workgroup tg owns WAVES / KS column tiles of KS wavefronts each, and the host picks
 // KS from k alone (so a row gives the same bits alone or in a batch) such that each wavefront
-// holds at most kRing blocks: every load of the launch is in flight after one issue round.
+// holds at most kRing blocks: every load of the launch is in flight after one issue round.  The
+// arguments are scalars, in the order the kernel first needs them, so that all but the output
+// pointer arrive preloaded in SGPRs (no kernel-argument load before the first weight load: 7.3
+// against 7.8 us for n = 2048, k = 7168, g = 8, and 6.3 against 7.0 us for n = 7168, k = 2048).
 template <int KS, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 4) void gemm_skinny_single_kernel(GemmArgs p) {
+__global__ __launch_bounds__(64 * WAVES, 4) void gemm_skinny_single_kernel(const float* a_scales, const uint8_t* a_codes,
+                                                                          const uint8_t* w, const uint8_t* s, int k, int n,
+                                                                          int rows, int kind, float scale2, float* out) {
   __shared__ Smem sm;
-  run_rows<KS, WAVES>(p, View{p.w, p.s, p.scale2}, p.kind, blockIdx.x, 0, p.total_rows, sm);
+  GemmArgs p{};
+  p.a_codes = a_codes;
+  p.a_scales = a_scales;
+  p.a_rows = rows;
+  p.total_rows = rows;
+  p.num_experts = 1;
+  p.w = w;
+  p.s = s;
+  p.scale2 = scale2;
+  p.kind = kind;
+  p.out = out;
+  p.n = n;
+  p.k = k;
+  run_rows<KS, WAVES>(p, View{w, s, scale2}, kind, blockIdx.x, 0, rows, sm);
 }
 
 template <int KS, int WAVES>
 hipError_t launch_single(const GemmArgs& a, int tiles, hipStream_t stream) {
   constexpr int kTilesPerGroup = WAVES / KS;
   const int ngroups = (tiles + kTilesPerGroup - 1) / kTilesPerGroup;
-  hipLaunchKernelGGL((gemm_skinny_single_kernel<KS, WAVES>), dim3((unsigned)ngroups), dim3(64 * WAVES), 0, stream, a);
+  hipLaunchKernelGGL((gemm_skinny_single_kernel<KS, WAVES>), dim3((unsigned)ngroups), dim3(64 * WAVES), 0, stream,
+                     a.a_scales, a.a_codes, a.w, a.s, a.k, a.n, a.total_rows, a.kind, a.scale2, a.out);
   return hipGetLastError();
 }
 
