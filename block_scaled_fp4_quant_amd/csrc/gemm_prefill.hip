@@ -203,6 +203,44 @@ __device__ __forceinline__ void w_load(const Rsrc& r, const uint32_t (&wo)[kNT],
   }
 }
 
+// The two halves of w_load: the first 16 nibble bytes of each column tile (steps 0-3), then the
+// second 16 bytes and the scale bytes (steps 4-7 and every step).
+template <bool SWZ>
+__device__ __forceinline__ void w_load_first(const Rsrc& r, const uint32_t (&wo)[kNT], int b, int nblk, WRegs& d) {
+  const bool valid = b < nblk;
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt)
+    d.w[nt][0] = buf_load_x4(r.w, valid ? wo[nt] + (uint32_t)b * (SWZ ? 1024u : 64u) : kOffNone);
+}
+
+template <int KIND, bool SWZ>
+__device__ __forceinline__ void w_load_second(const Rsrc& r, const uint32_t (&wo)[kNT], const uint32_t (&so)[kNT],
+                                              int b, int nblk, WRegs& d) {
+  const bool valid = b < nblk;
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) {
+    const uint32_t o = valid ? wo[nt] + (uint32_t)b * (SWZ ? 1024u : 64u) : kOffNone;
+    d.w[nt][1] = buf_load_x4(r.w, o == kOffNone ? kOffNone : o + (SWZ ? 256u : 16u));
+  }
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) {
+    if constexpr (SWZ) {
+      const uint32_t ub = (uint32_t)b;
+      if constexpr (is_nv(KIND)) {
+        const uint32_t o = valid ? so[nt] + (ub >> 2) * 512u + (ub & 3u) * 2u : kOffNone;
+        d.s[nt] = buf_load_u16(r.s, o) | (buf_load_u16(r.s, o + 128u) << 16);
+      } else {
+        const uint32_t o = valid ? so[nt] + (ub >> 2) * 256u + (ub & 3u) : kOffNone;
+        d.s[nt] = buf_load_u8(r.s, o) | (buf_load_u8(r.s, o + 64u) << 8);
+      }
+    } else if constexpr (is_nv(KIND)) {
+      d.s[nt] = buf_load_u32(r.s, valid ? so[nt] + (uint32_t)b * 8u : kOffNone);
+    } else {
+      d.s[nt] = buf_load_u16(r.s, valid ? so[nt] + (uint32_t)b * 4u : kOffNone);
+    }
+  }
+}
+
 // Row i of the staged rows (16 activation bytes): converted to bf16 (f16 for kNV16) with the
 // power-of-two row scale folded in (exact: the scale only moves the exponent, and kNV16 tiles keep
 // every scaled value inside f16's exact range) and written to the LDS stage.  The two 16-byte halves
@@ -296,9 +334,10 @@ struct Frags {
 // One 128-wide k block.  Step s issues its MFMAs while the operands of step s+1 are prepared: 2
 // weight dequantizations, and each row tile's A fragment, read from LDS into the same registers
 // right after that row tile's MFMAs (no second set of A registers).  Steps 0-3 also convert and
-// store the next block's activations, step 4 issues the loads of the block after, and before step 7
-// the workgroup meets at the barrier that publishes the next stage.  Step 7 prepares step 0 of the
-// next block.
+// store the next block's activations, steps 3 and 7 refill the weight slot with the block after next
+// (its first 16 bytes per column tile, then the rest), step 4 issues the activation loads of the
+// block after, and before step 7 the workgroup meets at the barrier that publishes the next stage.
+// Step 7 prepares step 0 of the next block.
 template <int KIND, int NMT, bool SWZ>
 __device__ __forceinline__ void run_block(const Stage& cur, Stage& nxt, const WRegs& w, const WRegs& wn,
                                           StageRegs& store_src, StageRegs& load_dst, const Rsrc& r,
@@ -333,6 +372,12 @@ __device__ __forceinline__ void run_block(const Stage& cur, Stage& nxt, const WR
       for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = mfma32x32x16(f.a[mt], f.b[nt], acc[mt][nt]);
       f.a[mt] = (s + 1 < kSteps) ? lds_a<KIND>(cur, mt, s + 1) : lds_a<KIND>(nxt, mt, 0);
     }
+    if (s == 3) {
+      // the first 16 bytes of the slot were last read by step 3's dequantization (issued at s = 2)
+      __builtin_amdgcn_sched_barrier(0);
+      w_load_first<SWZ>(r, wo, b + kWDepth, nblk, wload);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (s == 4) {
       __builtin_amdgcn_sched_barrier(0);
       stage_load<KIND>(r, ao, b + 1 + kADepth, nblk, load_dst);
@@ -340,7 +385,7 @@ __device__ __forceinline__ void run_block(const Stage& cur, Stage& nxt, const WR
     }
     if (s == kSteps - 1) {
       __builtin_amdgcn_sched_barrier(0);
-      w_load<KIND, SWZ>(r, wo, so, b + kWDepth, nblk, wload);
+      w_load_second<KIND, SWZ>(r, wo, so, b + kWDepth, nblk, wload);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -511,9 +556,11 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
 #pragma unroll
   for (int q = 0; q < 4; ++q) stage_store_q<KIND>(st[0], sr[0], q);
   __builtin_amdgcn_sched_barrier(0);
+  w_load_first<SWZ>(r, wo, kWDepth - 1, nblk, wr[kWDepth - 1]);
+  __builtin_amdgcn_sched_barrier(0);
   stage_load<KIND>(r, ao, kADepth, nblk, sr[0]);
   __builtin_amdgcn_sched_barrier(0);
-  w_load<KIND, SWZ>(r, wo, so, kWDepth - 1, nblk, wr[kWDepth - 1]);
+  w_load_second<KIND, SWZ>(r, wo, so, kWDepth - 1, nblk, wr[kWDepth - 1]);
   __builtin_amdgcn_sched_barrier(0);
   lds_barrier();
   Frags<KIND> f;
@@ -524,7 +571,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
 
   // Block b reads LDS stage b&1 and weights wr[b%kWDepth]; it stores block b+1 (staged in
   // sr[(b+1)%kADepth]) into the other LDS stage, refills those staging registers with block
-  // b+1+kADepth and, at its end, refills wr[b%kWDepth] with block b+kWDepth.  A block count that is
+  // b+1+kADepth, and refills wr[b%kWDepth] with block b+kWDepth: the first 16 bytes of each column
+  // tile at step 3 (dead after step 3's dequantization), the rest at its end.  A block count that is
   // not a multiple of kUnroll runs up to kUnroll-1 all-zero blocks.
   const int nblk_r = (nblk + kUnroll - 1) / kUnroll * kUnroll;
   for (int b = 0; b < nblk_r; b += kUnroll) {
