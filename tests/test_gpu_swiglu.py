@@ -231,6 +231,24 @@ def test_fused_gate_up_matches_the_unfused_route(orc, seed, T, E, top, hidden, i
         assert np.array_equal(codes, rc) and np.array_equal(scales, rs)
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_fused_gate_up_random_sweep(seed):
+    # seeded random chains: 1..600 tokens, 1..12 experts of both formats, 1..3 per token, uniform or
+    # Zipf(1.1) routing, hidden (k) 128..1024, inter 128..1024, activation scales from 0.1 to 20,
+    # with and without row weights; the fused launch must give the unfused route's bits
+    rng = np.random.default_rng([6502, seed])
+    E = int(rng.integers(1, 13))
+    top = int(rng.integers(1, min(3, E) + 1))
+    T = int(rng.integers(1, 601))
+    hidden = 128 * int(rng.integers(1, 9))
+    inter = 128 * int(rng.integers(1, 9))
+    kinds = [int(v) for v in rng.integers(0, 2, size=E)]
+    x_scale = float(10.0 ** rng.uniform(-1.0, 1.3))
+    ch = workloads.expert_chain(7100 + seed, T, E, top, hidden, inter, kinds=kinds, x_scale=x_scale,
+                                zipf=1.1 if seed % 2 else None)
+    run_fused_vs_unfused(ch, weighted=seed % 3 != 0)
+
+
 @pytest.mark.parametrize("limit", [7.0, float("inf")])
 def test_fused_gate_up_saturation(limit):
     ch = workloads.expert_chain(58, 70, 3, 2, 512, 256, kinds=[NV, MX, NV], x_scale=50.0)
