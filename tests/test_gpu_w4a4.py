@@ -74,6 +74,27 @@ def test_gemm_parity(orc, arm, T, n, k, k_res):
     check_bound(y, ref, absp, k + k_res + 2, f"w4a4 {arm} T={T} n={n} k={k} k_res={k_res}")
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_gemm_random_sweep(orc, seed):
+    # seeded random shapes on the tiled kernel's W4A4 path: 1..300 tokens (every 32-row tail class),
+    # any n 1..400, k up to 2048, 0, 8 or 64 kept channels, all three activation arms
+    rng = np.random.default_rng([1729, seed])
+    T = int(rng.integers(1, 301))
+    n = int(rng.integers(1, 401))
+    k = 128 * int(rng.integers(1, 17))
+    k_res = (0, 8, 64)[seed % 3]
+    arm = ("uniform", "dyn", "res")[seed % 3]
+    x, ex = workloads.w4a4_case(300 + seed, T, n, k, arm)
+    codes, micro, rs, y, idx = gpu_w4a4(x, ex, seed % 4 != 3, k_res)
+    xq = x.copy()
+    if idx is not None:
+        xq[:, idx] = 0.0                                  # kept channels enter the quantizer as zeros
+    rc, rm, rr = orc.act_quant_fp4(xq, seed % 4 != 3)
+    assert np.array_equal(codes, rc) and np.array_equal(micro, rm) and np.array_equal(rs, rr)
+    ref, absp = orc.w4a4_gemm(codes, micro, rs, ex.w, ex.s, ex.scale2, x if k_res else None, idx)
+    check_bound(y, ref, absp, k + k_res + 2, f"w4a4 sweep seed={seed} T={T} n={n} k={k} k_res={k_res}")
+
+
 @pytest.mark.parametrize("T", [16, 64, 128, 512])
 def test_informational_band(orc, T):
     x, ex = workloads.w4a4_case(4, T, 256, 1024, "uniform")
