@@ -41,6 +41,15 @@
 // Activations are staged with 8 lanes per row, so each 16-byte load instruction touches 8 cache
 // lines.
 //
+// Vector instruction budget.  A block costs each wavefront 128 weight conversions and scale
+// multiplies whatever the tile's row count, so a short tile issues many vector instructions per MFMA
+// and the loop keeps the rest small: only the occupied row groups of the activations are loaded and
+// converted; a load past the last block gets its out-of-range offset from one scalar per block
+// (kBlkNone) instead of a per-lane select; one packed conversion yields two weight group scales; and
+// the LDS stage layout spreads the staging stores over the banks without data selects (stage_store_q).
+// Measured together on the prefill workload: 2.6% faster (3485 us against 3576 us; the down-projection
+// shape 1934 against 1991 us), identical bits.
+//
 // Epilogue.  The accumulators go through LDS (over the activation stages), 64 rows at a time, so that
 // each thread writes 16 consecutive bytes of one output row with a non-temporal store; rows whose
 // activation scale or row id is invalid were flagged by the scale scan before the main loop and are
@@ -70,6 +79,9 @@ constexpr int kWaveCols = 32 * kNT;          // 64
 constexpr int kBN = kWaves * kWaveCols;      // 256 columns per tile
 constexpr int kSteps = 8;                    // 16-wide k steps per 128-wide block
 constexpr int kARow = 128 * 2 + 16;          // bf16 activation row of one block, padded (272 B)
+// Block offset of a load past the last block: every plane is smaller than 2^31 bytes, so a valid
+// lane's offset plus this is out of range (the load returns zeros) without wrapping past 2^32.
+constexpr uint32_t kBlkNone = 0x80000000u;
 constexpr int kWDepth = 2;                   // register sets in the weight load ring
 constexpr int kADepth = 1;                   // register sets in the activation load ring
 constexpr int kUnroll = 2;                   // blocks per loop iteration (a multiple of both depths and of the 2 LDS stages)
@@ -149,94 +161,80 @@ struct Rsrc {
   rsrc_t w, s, a, as;
 };
 
-template <int KIND>
+// The activations of block b for the NMT occupied row groups (32 rows each) of the tile.  Past the
+// last block the offsets move out of range by kBlkNone, so the loads return zeros.  A lane whose row
+// is outside the slice or has an invalid row id (offset kOffNone) may wrap back into the plane and
+// load bytes of another row: those rows are never stored, or are stored as NaN from the scan's flags.
+template <int KIND, int NMT>
 __device__ __forceinline__ void stage_load(const Rsrc& r, const AOffs& o, int b, int nblk, StageRegs& d) {
   const bool valid = b < nblk;
   if constexpr (KIND == kW4) {
     // W4A4: 8 nibble bytes (16 elements, one micro-scale group) and that group's micro-scale byte
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NMT; ++i) {
       const uint2 v = buf_load_x2(r.a, valid && o.a[i] != kOffNone ? o.a[i] + (uint32_t)b * 64u : kOffNone);
       d.a[i] = u32x4{v.x, v.y, 0u, 0u};
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NMT; ++i)
       d.as[i] = u2f(buf_load_u8(r.as, valid && o.as[i] != kOffNone ? o.as[i] + (uint32_t)b * 8u : kOffNone));
     return;
   }
+  const uint32_t sa = valid ? (uint32_t)b * 128u : kBlkNone, ss = valid ? (uint32_t)b * 4u : kBlkNone;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) d.a[i] = buf_load_x4(r.a, valid ? o.a[i] + (uint32_t)b * 128u : kOffNone);
+  for (int i = 0; i < NMT; ++i) d.a[i] = buf_load_x4(r.a, o.a[i] + sa);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) d.as[i] = u2f(buf_load_u32(r.as, valid ? o.as[i] + (uint32_t)b * 4u : kOffNone));
+  for (int i = 0; i < NMT; ++i) d.as[i] = u2f(buf_load_u32(r.as, o.as[i] + ss));
 }
 
 // SWZ: planes in the swizzled layout (fp4_weight_swizzle).  The lane's 32 bytes are then the lane
 // pieces 2h and 2h+1 of its column (256 bytes apart), and their scale bytes sit in those pieces'
 // rows of the 4-block chunk: (b/4) * chunk bytes + (b%4) * bytes per block, the second piece 16 rows
 // further.  wo/so are the block-0 offsets of piece 2h.
+template <bool SWZ>
+__device__ __forceinline__ void w_load_first(const Rsrc& r, const uint32_t (&wo)[kNT], int b, int nblk, WRegs& d);
+template <int KIND, bool SWZ>
+__device__ __forceinline__ void w_load_second(const Rsrc& r, const uint32_t (&wo)[kNT], const uint32_t (&so)[kNT],
+                                              int b, int nblk, WRegs& d);
 template <int KIND, bool SWZ>
 __device__ __forceinline__ void w_load(const Rsrc& r, const uint32_t (&wo)[kNT], const uint32_t (&so)[kNT],
                                        int b, int nblk, WRegs& d) {
-  const bool valid = b < nblk;
-#pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) {
-    const uint32_t o = valid ? wo[nt] + (uint32_t)b * (SWZ ? 1024u : 64u) : kOffNone;
-    d.w[nt][0] = buf_load_x4(r.w, o);
-    d.w[nt][1] = buf_load_x4(r.w, o + (SWZ ? 256u : 16u));
-  }
-#pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) {
-    if constexpr (SWZ) {
-      const uint32_t ub = (uint32_t)b;
-      if constexpr (is_nv(KIND)) {
-        const uint32_t o = valid ? so[nt] + (ub >> 2) * 512u + (ub & 3u) * 2u : kOffNone;
-        d.s[nt] = buf_load_u16(r.s, o) | (buf_load_u16(r.s, o + 128u) << 16);
-      } else {
-        const uint32_t o = valid ? so[nt] + (ub >> 2) * 256u + (ub & 3u) : kOffNone;
-        d.s[nt] = buf_load_u8(r.s, o) | (buf_load_u8(r.s, o + 64u) << 8);
-      }
-    } else if constexpr (is_nv(KIND)) {
-      d.s[nt] = buf_load_u32(r.s, valid ? so[nt] + (uint32_t)b * 8u : kOffNone);
-    } else {
-      d.s[nt] = buf_load_u16(r.s, valid ? so[nt] + (uint32_t)b * 4u : kOffNone);
-    }
-  }
+  w_load_first<SWZ>(r, wo, b, nblk, d);
+  w_load_second<KIND, SWZ>(r, wo, so, b, nblk, d);
 }
 
 // The two halves of w_load: the first 16 nibble bytes of each column tile (steps 0-3), then the
-// second 16 bytes and the scale bytes (steps 4-7 and every step).
+// second 16 bytes and the scale bytes (steps 4-7 and every step).  As in stage_load, past the last
+// block the offsets move out of range by kBlkNone; a lane past the last column (offset kOffNone) may
+// wrap into the plane, and its column is never stored.
 template <bool SWZ>
 __device__ __forceinline__ void w_load_first(const Rsrc& r, const uint32_t (&wo)[kNT], int b, int nblk, WRegs& d) {
-  const bool valid = b < nblk;
+  const uint32_t sb = b < nblk ? (uint32_t)b * (SWZ ? 1024u : 64u) : kBlkNone;
 #pragma unroll
-  for (int nt = 0; nt < kNT; ++nt)
-    d.w[nt][0] = buf_load_x4(r.w, valid ? wo[nt] + (uint32_t)b * (SWZ ? 1024u : 64u) : kOffNone);
+  for (int nt = 0; nt < kNT; ++nt) d.w[nt][0] = buf_load_x4(r.w, wo[nt] + sb);
 }
 
 template <int KIND, bool SWZ>
 __device__ __forceinline__ void w_load_second(const Rsrc& r, const uint32_t (&wo)[kNT], const uint32_t (&so)[kNT],
                                               int b, int nblk, WRegs& d) {
   const bool valid = b < nblk;
+  const uint32_t sb = valid ? (uint32_t)b * (SWZ ? 1024u : 64u) : kBlkNone;
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) d.w[nt][1] = buf_load_x4(r.w, wo[nt] + sb + (SWZ ? 256u : 16u));
+  const uint32_t ub = (uint32_t)b;
+  const uint32_t ss = !valid ? kBlkNone
+                      : SWZ ? (is_nv(KIND) ? (ub >> 2) * 512u + (ub & 3u) * 2u : (ub >> 2) * 256u + (ub & 3u))
+                            : ub * (is_nv(KIND) ? 8u : 4u);
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) {
-    const uint32_t o = valid ? wo[nt] + (uint32_t)b * (SWZ ? 1024u : 64u) : kOffNone;
-    d.w[nt][1] = buf_load_x4(r.w, o == kOffNone ? kOffNone : o + (SWZ ? 256u : 16u));
-  }
-#pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) {
+    const uint32_t o = so[nt] + ss;
     if constexpr (SWZ) {
-      const uint32_t ub = (uint32_t)b;
-      if constexpr (is_nv(KIND)) {
-        const uint32_t o = valid ? so[nt] + (ub >> 2) * 512u + (ub & 3u) * 2u : kOffNone;
-        d.s[nt] = buf_load_u16(r.s, o) | (buf_load_u16(r.s, o + 128u) << 16);
-      } else {
-        const uint32_t o = valid ? so[nt] + (ub >> 2) * 256u + (ub & 3u) : kOffNone;
-        d.s[nt] = buf_load_u8(r.s, o) | (buf_load_u8(r.s, o + 64u) << 8);
-      }
+      if constexpr (is_nv(KIND)) d.s[nt] = buf_load_u16(r.s, o) | (buf_load_u16(r.s, o + 128u) << 16);
+      else d.s[nt] = buf_load_u8(r.s, o) | (buf_load_u8(r.s, o + 64u) << 8);
     } else if constexpr (is_nv(KIND)) {
-      d.s[nt] = buf_load_u32(r.s, valid ? so[nt] + (uint32_t)b * 8u : kOffNone);
+      d.s[nt] = buf_load_u32(r.s, o);
     } else {
-      d.s[nt] = buf_load_u16(r.s, valid ? so[nt] + (uint32_t)b * 4u : kOffNone);
+      d.s[nt] = buf_load_u16(r.s, o);
     }
   }
 }
@@ -251,18 +249,20 @@ __device__ __forceinline__ void stage_store_q(Stage& st, const StageRegs& d, int
   if constexpr (KIND == kW4) {
     // 16 E2M1 values times their UE4M3 micro-scale as f16 (at most 5 significant bits: exact)
     const _Float16 ms = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)f2u(d.as[i]), 0);
-    const bool swap = (c >> 2) & 1;
-    const h16x8 first = e2m1x8_scaled_f16(swap ? d.a[i][1] : d.a[i][0], ms);
-    const h16x8 second = e2m1x8_scaled_f16(swap ? d.a[i][0] : d.a[i][1], ms);
+    const bool swap = (c >> 2) & 1;                         // the layout below (pair-swapped upper half)
+    const h16x8 first = e2m1x8_scaled_f16(d.a[i][0], ms);
+    const h16x8 second = e2m1x8_scaled_f16(d.a[i][1], ms);
     uint8_t* dst = st.a + row * kARow + 32 * c;
     *reinterpret_cast<h16x8*>(dst + (swap ? 16 : 0)) = first;
     *reinterpret_cast<h16x8*>(dst + (swap ? 0 : 16)) = second;
     return;
   }
-  // lanes c >= 4 write their upper half first: the code dwords are swapped before conversion
+  // The upper half of a row (lanes c >= 4, k 64..127) holds each 32-byte piece pair with its two
+  // 16-byte halves swapped: the first store of every lane then goes to +0 (c < 4) or +16 (c >= 4),
+  // which spreads one store instruction over the banks, with no data selects; lds_a reads the upper
+  // half's pieces at the swapped positions.
   const bool swap = (c >> 2) & 1;
-  const uint32_t src[4] = {swap ? d.a[i][2] : d.a[i][0], swap ? d.a[i][3] : d.a[i][1],
-                           swap ? d.a[i][0] : d.a[i][2], swap ? d.a[i][1] : d.a[i][3]};
+  const uint32_t src[4] = {d.a[i][0], d.a[i][1], d.a[i][2], d.a[i][3]};
   u32x4 first, second;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
@@ -292,8 +292,10 @@ template <int KIND, int S>
 __device__ __forceinline__ typename OpT<KIND>::T dequant_step(const WRegs& w, int nt) {
   const uint32_t q = w.w[nt][S >> 2][S & 3];
   if constexpr (KIND == kNV16 || KIND == kW4) {
-    // E2M1 -> f16 (exact), times the E4M3 group scale as f16 (exact; at most 5 significant bits)
-    return e2m1x8_scaled_f16(q, (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)w.s[nt], S >> 1));
+    // E2M1 -> f16 (exact), times the E4M3 group scale as f16 (exact; at most 5 significant bits).
+    // One packed conversion yields the scales of two groups (bytes 0-1 for steps 0-3, 2-3 after).
+    const h16x2 sp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.s[nt], 1.0f, S >= 4);
+    return e2m1x8_scaled_f16(q, sp[(S >> 1) & 1]);
   } else if constexpr (KIND == kNV) {
     // E2M1 -> f32 (exact), times the E4M3 group scale (<= 6 significant bits: exact), -> bf16 (exact)
     const float sv = __builtin_amdgcn_cvt_f32_fp8((int)w.s[nt], S >> 1);
@@ -320,8 +322,11 @@ __device__ __forceinline__ typename OpT<KIND>::T dequant_step(const WRegs& w, in
 template <int KIND>
 __device__ __forceinline__ typename OpT<KIND>::T lds_a(const Stage& st, int mt, int s) {
   const int lane = threadIdx.x & 63;
-  return *reinterpret_cast<const typename OpT<KIND>::T*>(st.a + (32 * mt + (lane & 31)) * kARow +
-                                                         128 * (lane >> 5) + 16 * s);
+  // lane half h reads k 64h + 8s .. +8, i.e. 16-byte piece 8h + s of the row; the upper half
+  // (h = 1) stores its pieces pair-swapped (stage_store_q), so piece 8 + s sits at 8 + (s ^ 1)
+  const int h = lane >> 5;
+  const int hoff = (s & 1) ? 112 * h : 144 * h;
+  return *reinterpret_cast<const typename OpT<KIND>::T*>(st.a + (32 * mt + (lane & 31)) * kARow + hoff + 16 * s);
 }
 
 // Fragments of the step the MFMAs consume next.
@@ -365,7 +370,7 @@ __device__ __forceinline__ void run_block(const Stage& cur, Stage& nxt, const WR
         default: g.b[nt] = dequant_step<KIND, 0>(wn, nt); break;
       }
     }
-    if (s < 4) stage_store_q<KIND>(nxt, store_src, s);
+    if (s < NMT) stage_store_q<KIND>(nxt, store_src, s);
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
@@ -380,7 +385,7 @@ __device__ __forceinline__ void run_block(const Stage& cur, Stage& nxt, const WR
     }
     if (s == 4) {
       __builtin_amdgcn_sched_barrier(0);
-      stage_load<KIND>(r, ao, b + 1 + kADepth, nblk, load_dst);
+      stage_load<KIND, NMT>(r, ao, b + 1 + kADepth, nblk, load_dst);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (s == kSteps - 1) {
@@ -541,11 +546,11 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
   // then the weights of block b+kWDepth).  Loads past the last block return zeros.
   StageRegs sr[kADepth];
   WRegs wr[kWDepth];
-  stage_load<KIND>(r, ao, 0, nblk, sr[0]);
+  stage_load<KIND, NMT>(r, ao, 0, nblk, sr[0]);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 1; j < kADepth; ++j) {
-    stage_load<KIND>(r, ao, j, nblk, sr[j]);
+    stage_load<KIND, NMT>(r, ao, j, nblk, sr[j]);
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
@@ -554,11 +559,11 @@ __device__ __forceinline__ void run_tile(const GemmArgs& p, const ExpertView& ex
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) stage_store_q<KIND>(st[0], sr[0], q);
+  for (int q = 0; q < NMT; ++q) stage_store_q<KIND>(st[0], sr[0], q);
   __builtin_amdgcn_sched_barrier(0);
   w_load_first<SWZ>(r, wo, kWDepth - 1, nblk, wr[kWDepth - 1]);
   __builtin_amdgcn_sched_barrier(0);
-  stage_load<KIND>(r, ao, kADepth, nblk, sr[0]);
+  stage_load<KIND, NMT>(r, ao, kADepth, nblk, sr[0]);
   __builtin_amdgcn_sched_barrier(0);
   w_load_second<KIND, SWZ>(r, wo, so, kWDepth - 1, nblk, wr[kWDepth - 1]);
   __builtin_amdgcn_sched_barrier(0);
