@@ -200,19 +200,23 @@ def test_grouped_random_sweep(orc, schedule, seed):
     grouped_check(gd, orc, out)
 
 
+@pytest.mark.parametrize("sched", [fp4.SCHEDULE_ROWSTREAM, fp4.SCHEDULE_TILED], ids=["rowstream", "tiled"])
 @pytest.mark.parametrize("E,T,top", [(9, 90, 2), (37, 200, 4), (505, 700, 8), (512, 700, 8), (520, 700, 8)])
-def test_decode_expert_order(orc, E, T, top):
-    """The row-streaming kernel hands each XCD its experts with more than 16 rows first (up to 512
-    experts; more keep the plain order).  Every expert must be computed exactly once: a NaN-filled
-    output, expert counts whose per-XCD lists differ in length (E % 8 != 0), that fill all 64 lanes of
-    the ballot (512) or exceed it (520), with empty, short, long and multi-pass experts."""
+def test_many_experts_every_output(orc, E, T, top, sched):
+    """Every expert computed exactly once into a NaN-filled output.  The row-streaming kernel hands
+    each XCD its experts with more than 16 rows first (up to 512 experts; more keep the plain order):
+    expert counts whose per-XCD lists differ in length (E % 8 != 0), that fill all 64 lanes of the
+    ballot (512) or exceed it (520).  The tiled kernel scans the offsets of several 64-expert chunks
+    per tile, and with n = 72 and rows that leave most 32-row tiles partial, its loads of columns past
+    n and rows outside the slice run on every tile (they may read any bytes of the planes but must
+    never reach the output).  Empty, short, long and multi-pass experts."""
     kinds = [NV if e % 5 else MX for e in range(E)]
     wl = workloads.grouped_random(7100 + E, T, E, top, 72, 256, kinds=kinds, zipf=1.1)
     rows = np.diff(wl.offsets)
     assert (rows > 16).any() and ((rows > 0) & (rows <= 16)).any()
     gd = GroupedDevice(wl)
     out = torch.full((wl.R, wl.n), float("nan"), dtype=torch.float32, device=gd.x.device)
-    fp4.set_gemm_schedule(fp4.SCHEDULE_ROWSTREAM)
+    fp4.set_gemm_schedule(sched)
     try:
         _, _, out = gd.step(out=out)
     finally:
